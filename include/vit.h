@@ -1,0 +1,157 @@
+/*
+ * vit.h -- C ABI of the MI355X (gfx950) vision encoder for DeepSeek V4 / V4.1 Flash.
+ *
+ * The encoder turns images into visual rows for the language model in five stages:
+ * 14x14 RGB patchify, patch projection, a stack of pre-LayerNorm ViT blocks with 2D RoPE,
+ * a 3x3 spatial merge, and a projection to the language hidden width.
+ * Sources (web pages, cited by title and section):
+ *   [Z] "DeepSeek V4.1 Flash Engineering, Part 3: Integrating Vision" (zhuai.tech)
+ *   [G] ds4-learning "glossary/vision": V4 Flash Vision-Exp and V4.1 Flash vision rows
+ *   [L] lucebox "docs/image-input.md": DS4V section
+ *
+ * Conventions
+ *  - bf16 values travel as uint16_t bit patterns.
+ *  - Pointers named d_* are device pointers (HIP, current device); h_* are host pointers.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every call that
+ *    takes a stream only enqueues work on it and returns without synchronising; results are
+ *    valid once that stream has synchronised.  A context is not thread-safe: use one per
+ *    stream.
+ *  - All arguments of a call are validated before anything is enqueued, so a rejected call
+ *    publishes no partial output ([L] DS4V: failed multi-image encoding publishes no partial
+ *    embedding matrices).
+ *  - The caller owns every buffer it passes; the library keeps no pointer after a call
+ *    returns.  The context owns its device copy of the weights, tables and workspace.
+ */
+#ifndef VIT_H
+#define VIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    VIT_OK = 0,
+    VIT_E_ARG = 1,      /* invalid argument (null pointer, bad size, bad grid, bad row index) */
+    VIT_E_BUDGET = 2,   /* an image exceeds max_tokens_per_image merged tokens */
+    VIT_E_NOMEM = 3,    /* device or pinned-host allocation failed, or over the reserve cap */
+    VIT_E_DEVICE = 4    /* a HIP call or kernel launch failed; see vit_last_error */
+} vit_status;
+
+typedef struct vit_ctx vit_ctx;
+
+/* Patch grid of one image: the image is (patch*gh) x (patch*gw) pixels. */
+typedef struct { int32_t gh, gw; } vit_grid;
+
+/* Encoder dimensions.  [Z] "Step 1": 14x14 patches, hidden 1024, 16 heads, 32 layers, 3x3
+ * merge, 5120-wide projection (4096 for V4, [G]); token cap 1024 for V4.1, 384 for V4 ([G]).
+ * Supported by this build: hidden % 64 == 0, head_dim = hidden/heads in {16, 32, 64, 128},
+ * mlp % 64 == 0, patch 14, merge 3, out_hidden >= 1. */
+typedef struct {
+    int32_t layers, hidden, heads, mlp, patch, merge, out_hidden, max_tokens_per_image;
+    float ln_eps;        /* LayerNorm epsilon (1e-6) */
+    float rope_base;     /* 2D RoPE frequency base (10000) */
+    float pix_mean[3];   /* per-channel pixel normalisation: v = (u8/255 - mean) / std, */
+    float pix_std[3];    /* evaluated as fmaf(u8, 1/(255 std), -mean/std) in fp32 */
+} vit_config;
+
+/* Weights: one host bf16 blob, tensors back to back, every matrix [out][in] row-major:
+ *   W_pe [D][3*patch^2], b_pe [D];
+ *   per layer: ln1.g [D], ln1.b [D], W_qkv [3D][D] (rows: q | k | v, head-major inside
+ *   each), b_qkv [3D], W_o [D][D], b_o [D], ln2.g [D], ln2.b [D], W_1 [F][D], b_1 [F],
+ *   W_2 [D][F], b_2 [D];
+ *   lnf.g [D], lnf.b [D], W_proj [out_hidden][9D] (input column c*9 + k: channel-major 3x3
+ *   unfold, [Z] "Step 4"), b_proj [out_hidden].
+ * blob_elems must equal that total. */
+typedef struct {
+    vit_config cfg;
+    const uint16_t *blob;
+    size_t blob_elems;
+} vit_weights;
+
+/* Number of bf16 elements vit_create expects in the blob for `cfg` (0 if cfg is invalid). */
+size_t vit_blob_elems(const vit_config *cfg);
+
+/* Create a context on the current HIP device: validates cfg, copies the weights to the
+ * device (the host blob may be freed afterwards) and prepares the derived tables.
+ * Synchronous.  On failure *out is NULL and vit_last_error(NULL) describes why. */
+vit_status vit_create(const vit_weights *w, vit_ctx **out);
+
+/* Release everything the context owns.  Waits for the device first.  NULL is a no-op. */
+void vit_destroy(vit_ctx *ctx);
+
+/* Optional: pre-size the workspace for up to max_patches patches in one call, and cap it
+ * there (a later vit_encode needing more returns VIT_E_NOMEM).  max_patches <= 0 removes
+ * the cap.  Synchronous. */
+vit_status vit_reserve(vit_ctx *ctx, int64_t max_patches);
+
+/* Merged visual tokens of a batch: sum over images of ceil(gh/3) * ceil(gw/3)
+ * ([Z] "Step 4": right/bottom padding to multiples of 3).  -1 if an argument is invalid. */
+int64_t vit_num_tokens(const vit_ctx *ctx, const vit_grid *h_grids, int32_t n_images);
+
+/* Patches of a batch: sum of gh * gw.  -1 if an argument is invalid. */
+int64_t vit_num_patches(const vit_ctx *ctx, const vit_grid *h_grids, int32_t n_images);
+
+/* Encode a packed batch of images into visual rows.
+ *   d_pixels:  uint8 RGB, each image HWC [patch*gh][patch*gw][3], images back to back.
+ *   h_grids:   n_images patch grids (host).  Each gh, gw >= 1 and each image's merged token
+ *              count <= max_tokens_per_image (else VIT_E_BUDGET).
+ *   d_out_rows: fp32 [vit_num_tokens][out_hidden], image-major, merged tokens row-major
+ *              inside each image ([G] V4.1: plain row-major stream).
+ * Attention is bidirectional inside each image and never crosses images ([L] DS4V).
+ * Returns without synchronising the stream. */
+vit_status vit_encode(vit_ctx *ctx, const uint8_t *d_pixels, const vit_grid *h_grids,
+                      int32_t n_images, float *d_out_rows, void *stream);
+
+/* Token types of the image span layout. */
+enum { VIT_TOK_START = 1, VIT_TOK_IMAGE = 2, VIT_TOK_NEWLINE = 3, VIT_TOK_END = 4 };
+
+/* Span layout of a batch ([Z] "Connect the complete image-to-text path"; [G] V4.1: START,
+ * then per merged row width x IMAGE and one NEWLINE, then END; identity order).  Writes
+ * *n_positions = sum of 2 + mh*(mw+1); if h_types / h_src are non-NULL they must hold that
+ * many entries: h_types[p] is a VIT_TOK_* value and h_src[p] the visual row (image-major
+ * numbering, as in vit_encode's output) of an IMAGE position, -1 elsewhere.  Host only. */
+vit_status vit_layout(const vit_grid *h_grids, int32_t n_images, int32_t merge,
+                      int32_t *h_types, int32_t *h_src, int64_t *n_positions);
+
+/* Overlay visual rows onto prompt embeddings ([Z] "Multimodal basics": vision vectors
+ * replace the image-placeholder rows):  d_embeds[h_rows[t]][:] = bf16_rne(d_rows[t][:]) for
+ * t < n_rows.  d_embeds is bf16 [n_embed_rows][hidden], d_rows fp32 [n_rows][hidden].
+ * h_rows[t] < 0 skips row t (chunked prefill writes only the rows inside its chunk,
+ * [Z] "Connect the complete image-to-text path").  VIT_E_ARG if ctx is NULL, hidden !=
+ * out_hidden, a row index >= n_embed_rows, or two rows name the same destination. */
+vit_status vit_overlay(vit_ctx *ctx, uint16_t *d_embeds, int64_t n_embed_rows,
+                       const int32_t *h_rows, const float *d_rows, int64_t n_rows,
+                       int32_t hidden, void *stream);
+
+/* Debug boundaries ([Z] "Step 2": compare patches, block outputs, final norm and aligner
+ * input to find the earliest divergence).  vit_dump runs the encoder up to the boundary on
+ * the given batch and copies that tensor into d_dst (dst_bytes must equal its size):
+ *   VIT_DUMP_PATCHES     bf16 [N][3*patch^2]   patchify output (same loader as the GEMM)
+ *   VIT_DUMP_EMBED       bf16 [N][D]           patch projection output
+ *   VIT_DUMP_QKV         bf16 [N][3D]          q,k after RoPE and v of layer `arg`
+ *   VIT_DUMP_ATTN        bf16 [N][D]           attention output of layer `arg`
+ *   VIT_DUMP_LAYER       bf16 [N][D]           residual stream after layer `arg`
+ *   VIT_DUMP_FINAL_NORM  bf16 [N][D]           final LayerNorm output
+ *   VIT_DUMP_MERGED      bf16 [M][9D]          merged projector input, channel-major
+ *                                              (same gather as the projector GEMM)
+ * N = patches, M = merged tokens of the batch. */
+enum {
+    VIT_DUMP_PATCHES = 0, VIT_DUMP_EMBED = 1, VIT_DUMP_QKV = 2, VIT_DUMP_ATTN = 3,
+    VIT_DUMP_LAYER = 4, VIT_DUMP_FINAL_NORM = 5, VIT_DUMP_MERGED = 6
+};
+vit_status vit_dump(vit_ctx *ctx, int32_t boundary, int32_t arg, const uint8_t *d_pixels,
+                    const vit_grid *h_grids, int32_t n_images, void *d_dst, size_t dst_bytes,
+                    void *stream);
+
+/* Text of the last error on ctx (or of the last failed vit_create on this thread when ctx
+ * is NULL).  Never NULL; valid until the next call on the same ctx / thread. */
+const char *vit_last_error(const vit_ctx *ctx);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VIT_H */

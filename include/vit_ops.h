@@ -1,0 +1,70 @@
+/*
+ * vit_ops.h -- single-step entry points of the MI355X vision encoder.
+ *
+ * Each call launches exactly the kernel(s) that vit_encode uses for that step, with the same
+ * launch configuration, on caller-provided device buffers.  They exist so that every step can
+ * be checked and timed in isolation at the encoder's real shapes.  Conventions are those of
+ * vit.h (bf16 as uint16_t, d_* device pointers, asynchronous on `stream`, validation before
+ * any launch, VIT_E_* codes, text in vit_last_error(ctx)).  `ctx` must be non-NULL; only
+ * vit_op_rope, vit_op_attention and vit_op_merge_project read its configuration and tables.
+ */
+#ifndef VIT_OPS_H
+#define VIT_OPS_H
+
+#include "vit.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { VIT_ACT_NONE = 0, VIT_ACT_GELU_TANH = 1 };
+
+/* Linear layer on bf16 MFMA with fp32 accumulation ([Z] "Multimodal basics": patch
+ * projection and the block's linear layers; "End-to-end results": tanh GELU):
+ *   out[i][j] = act(sum_k A[i][k] W[j][k] + b[j])
+ * A bf16 [M][K] (row stride K), W bf16 [N][K], b bf16 [N] or NULL.  out is bf16 [M][N]
+ * rounded once after the activation (out_f32 == 0) or fp32 [M][N] (out_f32 != 0).
+ * Requires M >= 0, N >= 1, K >= 64 and K % 64 == 0. */
+vit_status vit_op_linear(vit_ctx *ctx, const uint16_t *d_A, int64_t M, int32_t K,
+                         const uint16_t *d_W, const uint16_t *d_b, int32_t N, int32_t act,
+                         int32_t out_f32, void *d_out, void *stream);
+
+/* Residual add + LayerNorm over rows of width D (D in {64, 128, 256, 512, 1024, 1536, 2048}):
+ *   if d_delta != NULL:  x = bf16(x + delta), written to d_xout (may alias d_x);
+ *   out = bf16((x - mean) / sqrt(var + eps) * g + b), mean/var over the row (biased).
+ * x, delta, xout, out are bf16 [M][D]; g, b bf16 [D]. */
+vit_status vit_op_layernorm(vit_ctx *ctx, const uint16_t *d_x, const uint16_t *d_delta,
+                            uint16_t *d_xout, int64_t M, int32_t D, const uint16_t *d_g,
+                            const uint16_t *d_b, float eps, uint16_t *d_out, void *stream);
+
+/* Row stride (in elements) of the transposed-V buffer for a batch: the buffer is
+ * bf16 [heads][head_dim][stride] and image i owns columns starting at a multiple of 64,
+ * stride = sum over images of ceil(gh*gw / 64) * 64.  -1 if an argument is invalid. */
+int64_t vit_vt_stride(const vit_grid *h_grids, int32_t n_images);
+
+/* 2D RoPE on q and k ([Z] "Step 3": height/width-blocked angles, half-vector rotation;
+ * [G] V4: raw patch grid) in place inside d_qkv = bf16 [N][3D] (q | k | v, head-major),
+ * and v copied transposed to d_vt = bf16 [H][hd][vit_vt_stride(grids)] for the attention
+ * (the columns of each image past its last patch are written as zeros).
+ * Patch n of an image sits at (n / gw, n % gw) of that image's grid. */
+vit_status vit_op_rope(vit_ctx *ctx, uint16_t *d_qkv, uint16_t *d_vt, const vit_grid *h_grids,
+                       int32_t n_images, void *stream);
+
+/* Bidirectional softmax attention inside each image of a packed batch (block-diagonal),
+ * scale 1/sqrt(head_dim): d_o = bf16 [N][D], head h in columns h*hd .. h*hd+hd-1.
+ * Inputs as produced by vit_op_rope. */
+vit_status vit_op_attention(vit_ctx *ctx, const uint16_t *d_qkv, const uint16_t *d_vt,
+                            const vit_grid *h_grids, int32_t n_images, uint16_t *d_o,
+                            void *stream);
+
+/* 3x3 merge + projector ([Z] "Step 4": right/bottom zero padding on the 2D grid,
+ * channel-major unfold; then the aligner projection): d_y = bf16 [N][D] final-norm rows,
+ * d_out = fp32 [M][out_hidden] using the context's projector weights. */
+vit_status vit_op_merge_project(vit_ctx *ctx, const uint16_t *d_y, const vit_grid *h_grids,
+                                int32_t n_images, float *d_out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VIT_OPS_H */

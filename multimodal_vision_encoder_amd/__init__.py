@@ -1,0 +1,259 @@
+"""Python binding of the MI355X (gfx950) vision encoder for DeepSeek V4 / V4.1 Flash.
+
+Argument marshalling only: every step of the encoder runs in the HIP kernels of
+``libvit.so`` behind the C ABI declared in ``include/vit.h`` and ``include/vit_ops.h``.
+PyTorch supplies device memory and the current stream and nothing else.  There is no CPU
+fallback: if the library is missing or the GPU call fails, these functions raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libvit.so")
+
+VIT_OK, VIT_E_ARG, VIT_E_BUDGET, VIT_E_NOMEM, VIT_E_DEVICE = 0, 1, 2, 3, 4
+TOK_START, TOK_IMAGE, TOK_NEWLINE, TOK_END = 1, 2, 3, 4
+DUMP_PATCHES, DUMP_EMBED, DUMP_QKV, DUMP_ATTN, DUMP_LAYER, DUMP_FINAL_NORM, DUMP_MERGED = range(7)
+ACT_NONE, ACT_GELU_TANH = 0, 1
+
+# every entry point declared in include/vit.h and include/vit_ops.h
+EXPORTS = ("vit_blob_elems", "vit_create", "vit_destroy", "vit_reserve", "vit_num_tokens",
+           "vit_num_patches", "vit_encode", "vit_layout", "vit_overlay", "vit_dump",
+           "vit_last_error", "vit_op_linear", "vit_op_layernorm", "vit_vt_stride", "vit_op_rope",
+           "vit_op_attention", "vit_op_merge_project")
+
+
+class VitError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"vit status {status}: {msg}")
+        self.status = status
+
+
+class Grid(ctypes.Structure):
+    _fields_ = [("gh", ctypes.c_int32), ("gw", ctypes.c_int32)]
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("layers", ctypes.c_int32), ("hidden", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("mlp", ctypes.c_int32), ("patch", ctypes.c_int32), ("merge", ctypes.c_int32),
+                ("out_hidden", ctypes.c_int32), ("max_tokens_per_image", ctypes.c_int32),
+                ("ln_eps", ctypes.c_float), ("rope_base", ctypes.c_float),
+                ("pix_mean", ctypes.c_float * 3), ("pix_std", ctypes.c_float * 3)]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [("cfg", Config), ("blob", ctypes.c_void_p), ("blob_elems", ctypes.c_size_t)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libvit.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python multimodal_vision_encoder_amd/build.py`")
+        L = ctypes.CDLL(LIB_PATH)
+        i32, i64, vp, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+        P = ctypes.POINTER
+        sig = {
+            "vit_blob_elems": (sz, [P(Config)]),
+            "vit_create": (i32, [P(Weights), P(vp)]),
+            "vit_destroy": (None, [vp]),
+            "vit_reserve": (i32, [vp, i64]),
+            "vit_num_tokens": (i64, [vp, P(Grid), i32]),
+            "vit_num_patches": (i64, [vp, P(Grid), i32]),
+            "vit_encode": (i32, [vp, vp, P(Grid), i32, vp, vp]),
+            "vit_layout": (i32, [P(Grid), i32, i32, vp, vp, P(i64)]),
+            "vit_overlay": (i32, [vp, vp, i64, vp, vp, i64, i32, vp]),
+            "vit_dump": (i32, [vp, i32, i32, vp, P(Grid), i32, vp, sz, vp]),
+            "vit_last_error": (ctypes.c_char_p, [vp]),
+            "vit_op_linear": (i32, [vp, vp, i64, i32, vp, vp, i32, i32, i32, vp, vp]),
+            "vit_op_layernorm": (i32, [vp, vp, vp, vp, i64, i32, vp, vp, ctypes.c_float, vp, vp]),
+            "vit_vt_stride": (i64, [P(Grid), i32]),
+            "vit_op_rope": (i32, [vp, vp, vp, P(Grid), i32, vp]),
+            "vit_op_attention": (i32, [vp, vp, vp, P(Grid), i32, vp, vp]),
+            "vit_op_merge_project": (i32, [vp, vp, P(Grid), i32, vp, vp]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def make_config(cfg) -> Config:
+    """vit_config from any object with the encoder's dimension attributes."""
+    c = Config()
+    for f in ("layers", "hidden", "heads", "mlp", "patch", "merge", "out_hidden",
+              "max_tokens_per_image"):
+        setattr(c, f, int(getattr(cfg, f)))
+    c.ln_eps = float(cfg.ln_eps)
+    c.rope_base = float(cfg.rope_base)
+    for i in range(3):
+        c.pix_mean[i] = float(cfg.pix_mean[i])
+        c.pix_std[i] = float(cfg.pix_std[i])
+    return c
+
+
+def grid_array(grids):
+    arr = (Grid * max(1, len(grids)))()
+    for i, (gh, gw) in enumerate(grids):
+        arr[i].gh, arr[i].gw = int(gh), int(gw)
+    return arr
+
+
+def layout(grids, merge: int = 3):
+    """Span layout (types, src) of a batch, as int32 numpy arrays."""
+    L = lib()
+    g = grid_array(grids)
+    n = ctypes.c_int64(0)
+    st = L.vit_layout(g, len(grids), merge, None, None, ctypes.byref(n))
+    if st != VIT_OK:
+        raise VitError(st, L.vit_last_error(None).decode())
+    types = np.zeros(n.value, np.int32)
+    src = np.zeros(n.value, np.int32)
+    st = L.vit_layout(g, len(grids), merge, types.ctypes.data, src.ctypes.data, ctypes.byref(n))
+    if st != VIT_OK:
+        raise VitError(st, L.vit_last_error(None).decode())
+    return types, src
+
+
+def vt_stride(grids) -> int:
+    return int(lib().vit_vt_stride(grid_array(grids), len(grids)))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+class Encoder:
+    """A vision-encoder context on the current GPU (weights uploaded once)."""
+
+    def __init__(self, cfg, blob: np.ndarray):
+        L = lib()
+        self.cfg = cfg
+        self.out_hidden = int(cfg.out_hidden)
+        blob = np.ascontiguousarray(blob, dtype=np.uint16)
+        w = Weights()
+        w.cfg = make_config(cfg)
+        w.blob = blob.ctypes.data
+        w.blob_elems = blob.size
+        ctx = ctypes.c_void_p()
+        st = L.vit_create(ctypes.byref(w), ctypes.byref(ctx))
+        if st != VIT_OK:
+            raise VitError(st, L.vit_last_error(None).decode())
+        self._ctx = ctx
+
+    def close(self):
+        if getattr(self, "_ctx", None):
+            lib().vit_destroy(self._ctx)
+            self._ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _check(self, st):
+        if st != VIT_OK:
+            raise VitError(st, lib().vit_last_error(self._ctx).decode())
+
+    # ---- queries ---------------------------------------------------------------------
+    def num_tokens(self, grids) -> int:
+        return int(lib().vit_num_tokens(self._ctx, grid_array(grids), len(grids)))
+
+    def num_patches(self, grids) -> int:
+        return int(lib().vit_num_patches(self._ctx, grid_array(grids), len(grids)))
+
+    def reserve(self, max_patches: int):
+        self._check(lib().vit_reserve(self._ctx, int(max_patches)))
+
+    # ---- the encoder -----------------------------------------------------------------
+    def encode(self, pixels, grids, out=None, stream=None):
+        """pixels: uint8 CUDA tensor (packed HWC images); returns fp32 [tokens][out_hidden]."""
+        import torch
+        M = self.num_tokens(grids)
+        if out is None:
+            out = torch.empty((max(M, 0), self.out_hidden), dtype=torch.float32, device=pixels.device)
+        self._check(lib().vit_encode(self._ctx, _ptr(pixels), grid_array(grids), len(grids),
+                                     _ptr(out), _stream(stream)))
+        return out
+
+    def dump(self, boundary: int, pixels, grids, arg: int = 0, stream=None):
+        import torch
+        N, M = self.num_patches(grids), self.num_tokens(grids)
+        D, ps = int(self.cfg.hidden), int(self.cfg.patch)
+        shape = {DUMP_PATCHES: (N, 3 * ps * ps), DUMP_EMBED: (N, D), DUMP_QKV: (N, 3 * D),
+                 DUMP_ATTN: (N, D), DUMP_LAYER: (N, D), DUMP_FINAL_NORM: (N, D),
+                 DUMP_MERGED: (M, 9 * D)}[boundary]
+        dst = torch.empty(shape, dtype=torch.bfloat16, device=pixels.device)
+        self._check(lib().vit_dump(self._ctx, boundary, arg, _ptr(pixels), grid_array(grids),
+                                   len(grids), _ptr(dst), dst.numel() * 2, _stream(stream)))
+        return dst
+
+    def overlay(self, embeds, rows, visual_rows, stream=None):
+        """embeds: bf16 CUDA tensor [R][out_hidden] (modified in place); rows: host ints
+        (negative = skip); visual_rows: fp32 CUDA tensor [len(rows)][out_hidden]."""
+        r = np.ascontiguousarray(np.asarray(rows, dtype=np.int32))
+        self._check(lib().vit_overlay(self._ctx, _ptr(embeds), embeds.shape[0], r.ctypes.data,
+                                      _ptr(visual_rows), r.size, int(embeds.shape[1]),
+                                      _stream(stream)))
+        return embeds
+
+    # ---- single steps (include/vit_ops.h) ---------------------------------------------
+    def op_linear(self, A, W, b, act=ACT_NONE, out_f32=False, stream=None):
+        import torch
+        M, K = A.shape
+        N = W.shape[0]
+        out = torch.empty((M, N), dtype=torch.float32 if out_f32 else torch.bfloat16, device=A.device)
+        self._check(lib().vit_op_linear(self._ctx, _ptr(A), M, K, _ptr(W), _ptr(b), N, act,
+                                        1 if out_f32 else 0, _ptr(out), _stream(stream)))
+        return out
+
+    def op_layernorm(self, x, g, b, eps, delta=None, xout=None, stream=None):
+        import torch
+        M, D = x.shape
+        out = torch.empty_like(x)
+        self._check(lib().vit_op_layernorm(self._ctx, _ptr(x), _ptr(delta), _ptr(xout), M, D,
+                                           _ptr(g), _ptr(b), float(eps), _ptr(out),
+                                           _stream(stream)))
+        return out
+
+    def op_rope(self, qkv, grids, stream=None):
+        """In place on qkv; returns the transposed-V buffer."""
+        import torch
+        H, D = int(self.cfg.heads), int(self.cfg.hidden)
+        vt = torch.empty((H, D // H, vt_stride(grids)), dtype=torch.bfloat16, device=qkv.device)
+        self._check(lib().vit_op_rope(self._ctx, _ptr(qkv), _ptr(vt), grid_array(grids),
+                                      len(grids), _stream(stream)))
+        return vt
+
+    def op_attention(self, qkv, vt, grids, stream=None):
+        import torch
+        o = torch.empty((qkv.shape[0], int(self.cfg.hidden)), dtype=torch.bfloat16, device=qkv.device)
+        self._check(lib().vit_op_attention(self._ctx, _ptr(qkv), _ptr(vt), grid_array(grids),
+                                           len(grids), _ptr(o), _stream(stream)))
+        return o
+
+    def op_merge_project(self, y, grids, stream=None):
+        import torch
+        out = torch.empty((self.num_tokens(grids), self.out_hidden), dtype=torch.float32,
+                          device=y.device)
+        self._check(lib().vit_op_merge_project(self._ctx, _ptr(y), grid_array(grids), len(grids),
+                                               _ptr(out), _stream(stream)))
+        return out

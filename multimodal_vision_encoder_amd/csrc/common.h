@@ -1,0 +1,87 @@
+// Shared device-side definitions of the gfx950 vision encoder kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef uint16_t bf16_t;  // bf16 bit pattern
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+
+constexpr int kWave = 64;
+
+// Per-image geometry of a packed batch (device copy built by the host planner).
+struct ImgDesc {
+    int32_t gh, gw;       // patch grid
+    int32_t patch_off;    // first patch row of the image in the packed activations
+    int32_t n;            // gh * gw
+    int32_t tok_off;      // first merged-token row of the image in the output
+    int32_t mh, mw;       // merged grid: ceil(gh/3), ceil(gw/3)
+    int32_t vt_off;       // first column of the image in the transposed-V buffer (multiple of 64)
+    int64_t pix_off;      // byte offset of the image in the pixel buffer
+};
+
+// One tile of rows of one image (attention query tiles, RoPE row tiles).
+struct RowTile {
+    int32_t img;
+    int32_t r0;           // first row, local to the image
+};
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// fp32 -> bf16, round to nearest even (inputs are finite).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (bf16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// Index of the image containing `row` given ascending offsets off(0) = 0 <= ... (n entries).
+template <class OffFn>
+__device__ __forceinline__ int find_segment(int n, int64_t row, OffFn off)
+{
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if ((int64_t)off(mid) <= row) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+__device__ __forceinline__ int image_of_patch(const ImgDesc *imgs, int n, int64_t row)
+{
+    return find_segment(n, row, [&](int i) { return imgs[i].patch_off; });
+}
+
+__device__ __forceinline__ int image_of_token(const ImgDesc *imgs, int n, int64_t row)
+{
+    return find_segment(n, row, [&](int i) { return imgs[i].tok_off; });
+}
+
+// Source patch (local row inside the image) of position `pos` (dy*3 + dx) of merged token
+// (my, mx), or -1 when it falls in the right/bottom zero padding.
+__device__ __forceinline__ int merge_source(const ImgDesc &d, int my, int mx, int pos)
+{
+    int sy = 3 * my + pos / 3, sx = 3 * mx + pos % 3;
+    return (sy < d.gh && sx < d.gw) ? sy * d.gw + sx : -1;
+}
+
+// MFMA 32x32x16 bf16 -> fp32 (gfx950).  A: lane l holds row l%32, k = 8*(l/32)..+7;
+// B: lane l holds column l%32, same k; D: lane l holds column l%32, rows
+// 8*(r/4) + 4*(l/32) + r%4 for register r.
+__device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

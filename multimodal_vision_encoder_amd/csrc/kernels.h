@@ -1,0 +1,52 @@
+// Host-side launchers of the gfx950 encoder kernels (one per hot-path step).
+#pragma once
+
+#include "common.h"
+
+// Activation of the linear epilogue.
+enum { ACT_NONE = 0, ACT_GELU_TANH = 1 };
+
+// out = act(A W^T + b) on bf16 MFMA, fp32 accumulation; out bf16 (rounded once) or fp32.
+// A bf16 [M][K], W bf16 [N][K]; K % 64 == 0.
+hipError_t launch_linear(const bf16_t *A, int64_t M, int K, const bf16_t *W, const bf16_t *bias,
+                         int N, int act, bool out_f32, void *out, hipStream_t s);
+
+// Patchify + patch projection: x0 = bf16(P W_pe^T + b), W_pe zero-padded to Kp columns.
+hipError_t launch_patch_embed(const uint8_t *px, const ImgDesc *imgs, int n_img, int64_t M,
+                              const float *s3, const float *t3, int ps, const bf16_t *Wpe,
+                              int Kp, const bf16_t *bias, int D, bf16_t *out, hipStream_t s);
+
+// 3x3 merge gather + projector: out fp32 [Mtok][Dl]; Wp position-major [Dl][9D].
+hipError_t launch_merge_project(const bf16_t *y, const ImgDesc *imgs, int n_img, int64_t Mtok,
+                                int D, const bf16_t *Wp, const bf16_t *bias, int Dl, float *out,
+                                hipStream_t s);
+
+// Optional residual add + LayerNorm (rows of width D).
+hipError_t launch_layernorm(const bf16_t *x, const bf16_t *delta, bf16_t *xout, int64_t M, int D,
+                            const bf16_t *g, const bf16_t *b, float eps, bf16_t *out,
+                            hipStream_t s);
+
+// 2D RoPE on q,k in place + transposed copy of v; one block per (64-row tile, head).
+hipError_t launch_rope(bf16_t *qkv, bf16_t *vt, int64_t ldv, const RowTile *tiles, int n_tiles,
+                       const ImgDesc *imgs, int D, int H, const float *cos_t,
+                       const float *sin_t, hipStream_t s);
+
+// Block-diagonal flash attention; one block per (128-query tile, head).
+hipError_t launch_attention(const bf16_t *qkv, const bf16_t *vt, int64_t ldv, bf16_t *o,
+                            const RowTile *work, int n_work, const ImgDesc *imgs, int D, int H,
+                            hipStream_t s);
+
+// embeds[rows[t]] = bf16(src[t]) for rows[t] >= 0.
+hipError_t launch_overlay(uint16_t *embeds, const float *src, const int32_t *rows, int64_t n_rows,
+                          int hidden, hipStream_t s);
+
+// Debug materialisation of fused-only tensors through the GEMM loaders.
+hipError_t launch_dump_patches(const uint8_t *px, const ImgDesc *imgs, int n_img, int64_t M,
+                               const float *s3, const float *t3, int ps, bf16_t *out,
+                               hipStream_t s);
+hipError_t launch_dump_merged(const bf16_t *y, const ImgDesc *imgs, int n_img, int64_t Mtok,
+                              int D, bf16_t *out, hipStream_t s);
+
+// Rows of a query tile / RoPE tile.
+constexpr int kAttnQTile = 128;
+constexpr int kRopeTile = 64;

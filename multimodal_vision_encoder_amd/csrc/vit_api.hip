@@ -1,0 +1,692 @@
+// Host side of the C ABI: validation, batch planning, weight preparation, workspace and the
+// launch sequence of one encoder pass.  Every argument of a call is checked before anything
+// is enqueued ([L] DS4V: failed multi-image encoding publishes no partial embeddings).
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "vit.h"
+#include "vit_ops.h"
+
+namespace {
+
+constexpr int kMaxSide = 4096;       // largest patch-grid side (rows of the RoPE tables)
+constexpr int kMaxImages = 4096;     // images per call
+constexpr int kVtAlign = 64;         // per-image column alignment of the transposed-V buffer
+
+thread_local std::string g_err;
+
+struct Layer {
+    const bf16_t *ln1g, *ln1b, *wqkv, *bqkv, *wo, *bo, *ln2g, *ln2b, *w1, *b1, *w2, *b2;
+};
+
+struct Plan {
+    std::vector<ImgDesc> imgs;
+    std::vector<RowTile> attn, rope;
+    int64_t N = 0, M = 0, vt_cols = 0;
+};
+
+}  // namespace
+
+struct vit_ctx {
+    vit_config cfg{};
+    int device = 0;
+    int D = 0, H = 0, hd = 0, F = 0, Dl = 0, L = 0, ps = 0, Kp = 0;
+    float s3[3] = {0, 0, 0}, t3[3] = {0, 0, 0};
+
+    bf16_t *d_blob = nullptr, *d_wpe = nullptr, *d_wproj = nullptr;
+    const bf16_t *pe_b = nullptr, *lnf_g = nullptr, *lnf_b = nullptr, *proj_b = nullptr;
+    std::vector<Layer> layers;
+    float *d_cos = nullptr, *d_sin = nullptr;
+
+    // workspace
+    int64_t cap_patches = 0, cap_vt_cols = 0, reserve_cap = 0;
+    bf16_t *x = nullptr, *ln = nullptr, *qkv = nullptr, *vt = nullptr, *o = nullptr,
+           *delta = nullptr, *h1 = nullptr;
+
+    // per-call metadata: pinned staging -> device
+    char *h_stage = nullptr, *d_meta = nullptr;
+    size_t meta_cap = 0;
+    hipEvent_t stage_ev = nullptr;
+    bool stage_pending = false;
+
+    std::string err;
+};
+
+namespace {
+
+vit_status fail(vit_ctx *ctx, vit_status st, const std::string &msg)
+{
+    (ctx ? ctx->err : g_err) = msg;
+    return st;
+}
+
+#define HIP_TRY(ctx, expr)                                                                    \
+    do {                                                                                      \
+        hipError_t e_ = (expr);                                                               \
+        if (e_ != hipSuccess)                                                                 \
+            return fail(ctx, VIT_E_DEVICE, std::string(#expr) + ": " + hipGetErrorString(e_)); \
+    } while (0)
+
+bool supported_hidden(int D)
+{
+    return D == 64 || D == 128 || D == 256 || D == 512 || D == 1024 || D == 1536 || D == 2048;
+}
+
+std::string check_config(const vit_config &c)
+{
+    if (c.layers < 0) return "layers < 0";
+    if (!supported_hidden(c.hidden)) return "hidden must be one of 64,128,256,512,1024,1536,2048";
+    if (c.heads < 1 || c.hidden % c.heads) return "heads must divide hidden";
+    const int hd = c.hidden / c.heads;
+    if (hd != 16 && hd != 32 && hd != 64 && hd != 128) return "head_dim must be 16, 32, 64 or 128";
+    if (c.mlp < 64 || c.mlp % 64) return "mlp must be a positive multiple of 64";
+    if (c.patch < 1 || c.patch > 64) return "patch must be in [1, 64]";
+    if (c.merge != 3) return "merge must be 3";
+    if (c.out_hidden < 1) return "out_hidden must be >= 1";
+    if (c.max_tokens_per_image < 1) return "max_tokens_per_image must be >= 1";
+    if (!(c.ln_eps > 0.f) || !(c.rope_base > 0.f)) return "ln_eps and rope_base must be > 0";
+    for (int i = 0; i < 3; ++i)
+        if (!(c.pix_std[i] != 0.f) || !std::isfinite(c.pix_std[i]) || !std::isfinite(c.pix_mean[i]))
+            return "pixel std must be non-zero and finite";
+    return "";
+}
+
+size_t blob_elems_of(const vit_config &c)
+{
+    const size_t D = c.hidden, F = c.mlp, P = 3 * (size_t)c.patch * c.patch, Dl = c.out_hidden;
+    size_t n = D * P + D;
+    n += (size_t)c.layers * (2 * D + 3 * D * D + 3 * D + D * D + D + 2 * D + F * D + F + D * F + D);
+    n += 2 * D + Dl * 9 * D + Dl;
+    return n;
+}
+
+int64_t tokens_of(int gh, int gw) { return (int64_t)((gh + 2) / 3) * ((gw + 2) / 3); }
+
+vit_status make_plan(vit_ctx *ctx, const vit_grid *grids, int n, Plan &p)
+{
+    if (n < 0 || n > kMaxImages) return fail(ctx, VIT_E_ARG, "n_images out of range");
+    if (n > 0 && !grids) return fail(ctx, VIT_E_ARG, "h_grids is NULL");
+    p = Plan();
+    int64_t pix = 0;
+    for (int i = 0; i < n; ++i) {
+        const int gh = grids[i].gh, gw = grids[i].gw;
+        if (gh < 1 || gw < 1 || gh > kMaxSide || gw > kMaxSide)
+            return fail(ctx, VIT_E_ARG, "image " + std::to_string(i) + ": grid " +
+                                            std::to_string(gh) + "x" + std::to_string(gw) +
+                                            " out of range [1, " + std::to_string(kMaxSide) + "]");
+        const int64_t tok = tokens_of(gh, gw);
+        if (tok > ctx->cfg.max_tokens_per_image)
+            return fail(ctx, VIT_E_BUDGET, "image " + std::to_string(i) + ": " + std::to_string(tok) +
+                                               " merged tokens exceed the budget of " +
+                                               std::to_string(ctx->cfg.max_tokens_per_image));
+        ImgDesc d{};
+        d.gh = gh;
+        d.gw = gw;
+        d.n = gh * gw;
+        d.patch_off = (int32_t)p.N;
+        d.tok_off = (int32_t)p.M;
+        d.mh = (gh + 2) / 3;
+        d.mw = (gw + 2) / 3;
+        d.vt_off = (int32_t)p.vt_cols;
+        d.pix_off = pix;
+        p.imgs.push_back(d);
+        p.N += d.n;
+        p.M += tok;
+        p.vt_cols += ceil_div(d.n, kVtAlign) * kVtAlign;
+        pix += (int64_t)ctx->ps * gh * ctx->ps * gw * 3;
+        if (p.vt_cols > INT32_MAX / 2) return fail(ctx, VIT_E_ARG, "batch too large");
+    }
+    // attention query tiles, largest images first (longest-processing-time order)
+    std::vector<int> order(n);
+    for (int i = 0; i < n; ++i) order[i] = i;
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int a, int b) { return p.imgs[a].n > p.imgs[b].n; });
+    for (int i : order)
+        for (int r = 0; r < p.imgs[i].n; r += kAttnQTile) p.attn.push_back(RowTile{i, r});
+    for (int i = 0; i < n; ++i)
+        for (int r = 0; r < p.imgs[i].n; r += kRopeTile) p.rope.push_back(RowTile{i, r});
+    return VIT_OK;
+}
+
+void free_workspace(vit_ctx *c)
+{
+    bf16_t **bufs[] = {&c->x, &c->ln, &c->qkv, &c->vt, &c->o, &c->delta, &c->h1};
+    for (auto b : bufs) {
+        if (*b) (void)hipFree(*b);
+        *b = nullptr;
+    }
+    c->cap_patches = c->cap_vt_cols = 0;
+}
+
+vit_status ensure_workspace(vit_ctx *c, int64_t N, int64_t vt_cols)
+{
+    if (N <= c->cap_patches && vt_cols <= c->cap_vt_cols) return VIT_OK;
+    if (c->reserve_cap > 0 && N > c->reserve_cap)
+        return fail(c, VIT_E_NOMEM, "batch of " + std::to_string(N) +
+                                        " patches exceeds the reserved workspace of " +
+                                        std::to_string(c->reserve_cap));
+    HIP_TRY(c, hipDeviceSynchronize());
+    free_workspace(c);
+    const int64_t Np = std::max<int64_t>(N, 64);
+    const int64_t Vc = std::max<int64_t>(vt_cols, kVtAlign);
+    const size_t D = c->D;
+    struct { bf16_t **p; size_t n; } req[] = {
+        {&c->x, Np * D}, {&c->ln, Np * D}, {&c->qkv, Np * 3 * D}, {&c->o, Np * D},
+        {&c->delta, Np * D}, {&c->h1, Np * (size_t)c->F}, {&c->vt, (size_t)c->H * c->hd * Vc}};
+    for (auto &r : req) {
+        if (hipMalloc((void **)r.p, r.n * sizeof(bf16_t)) != hipSuccess) {
+            (void)hipGetLastError();
+            free_workspace(c);
+            return fail(c, VIT_E_NOMEM, "workspace allocation failed");
+        }
+    }
+    HIP_TRY(c, hipMemset(c->vt, 0, (size_t)c->H * c->hd * Vc * sizeof(bf16_t)));
+    c->cap_patches = Np;
+    c->cap_vt_cols = Vc;
+    return VIT_OK;
+}
+
+// Copy `bytes` of host metadata to the context's device metadata buffer on `s`.
+vit_status upload_meta(vit_ctx *c, const std::vector<std::pair<const void *, size_t>> &parts,
+                       hipStream_t s, std::vector<size_t> &offsets)
+{
+    size_t total = 0;
+    offsets.clear();
+    for (auto &p : parts) {
+        offsets.push_back(total);
+        total += (p.second + 255) & ~(size_t)255;
+    }
+    if (total == 0) return VIT_OK;
+    if (c->stage_pending) {
+        HIP_TRY(c, hipEventSynchronize(c->stage_ev));
+        c->stage_pending = false;
+    }
+    if (total > c->meta_cap) {
+        HIP_TRY(c, hipDeviceSynchronize());
+        if (c->h_stage) (void)hipHostFree(c->h_stage);
+        if (c->d_meta) (void)hipFree(c->d_meta);
+        c->h_stage = c->d_meta = nullptr;
+        c->meta_cap = 0;
+        const size_t cap = std::max<size_t>(total, 1 << 16);
+        if (hipHostMalloc((void **)&c->h_stage, cap, hipHostMallocDefault) != hipSuccess ||
+            hipMalloc((void **)&c->d_meta, cap) != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(c, VIT_E_NOMEM, "metadata staging allocation failed");
+        }
+        c->meta_cap = cap;
+    }
+    for (size_t i = 0; i < parts.size(); ++i)
+        if (parts[i].second) std::memcpy(c->h_stage + offsets[i], parts[i].first, parts[i].second);
+    HIP_TRY(c, hipMemcpyAsync(c->d_meta, c->h_stage, total, hipMemcpyHostToDevice, s));
+    HIP_TRY(c, hipEventRecord(c->stage_ev, s));
+    c->stage_pending = true;
+    return VIT_OK;
+}
+
+struct DevPlan {
+    const ImgDesc *imgs;
+    const RowTile *attn, *rope;
+};
+
+vit_status stage_plan(vit_ctx *c, const Plan &p, hipStream_t s, DevPlan &dp)
+{
+    std::vector<size_t> off;
+    vit_status st = upload_meta(c,
+                                {{p.imgs.data(), p.imgs.size() * sizeof(ImgDesc)},
+                                 {p.attn.data(), p.attn.size() * sizeof(RowTile)},
+                                 {p.rope.data(), p.rope.size() * sizeof(RowTile)}},
+                                s, off);
+    if (st != VIT_OK) return st;
+    dp.imgs = (const ImgDesc *)(c->d_meta + off[0]);
+    dp.attn = (const RowTile *)(c->d_meta + off[1]);
+    dp.rope = (const RowTile *)(c->d_meta + off[2]);
+    return VIT_OK;
+}
+
+#define LAUNCH(ctx, expr)                                                                     \
+    do {                                                                                      \
+        hipError_t e_ = (expr);                                                               \
+        if (e_ != hipSuccess)                                                                 \
+            return fail(ctx, VIT_E_DEVICE, std::string("launch failed: ") + #expr + ": " +    \
+                                               hipGetErrorString(e_));                        \
+    } while (0)
+
+constexpr int kStopNone = -1;
+
+// One encoder pass; with stop >= 0 it ends at that debug boundary and copies the tensor.
+vit_status encode_impl(vit_ctx *c, const uint8_t *px, const vit_grid *grids, int n, float *out,
+                       hipStream_t s, int stop, int arg, void *dst, size_t dst_bytes)
+{
+    Plan p;
+    vit_status st = make_plan(c, grids, n, p);
+    if (st != VIT_OK) return st;
+    const int D = c->D, H = c->H, L = c->L;
+    const size_t b2 = sizeof(bf16_t);
+    if (stop == kStopNone) {
+        if (p.N > 0 && (!px || !out)) return fail(c, VIT_E_ARG, "d_pixels or d_out_rows is NULL");
+    } else {
+        size_t want = 0;
+        switch (stop) {
+        case VIT_DUMP_PATCHES: want = (size_t)p.N * 3 * c->ps * c->ps * b2; break;
+        case VIT_DUMP_EMBED: case VIT_DUMP_ATTN: case VIT_DUMP_LAYER: case VIT_DUMP_FINAL_NORM:
+            want = (size_t)p.N * D * b2; break;
+        case VIT_DUMP_QKV: want = (size_t)p.N * 3 * D * b2; break;
+        case VIT_DUMP_MERGED: want = (size_t)p.M * 9 * D * b2; break;
+        default: return fail(c, VIT_E_ARG, "unknown dump boundary");
+        }
+        if ((stop == VIT_DUMP_QKV || stop == VIT_DUMP_ATTN || stop == VIT_DUMP_LAYER) &&
+            (arg < 0 || arg >= L))
+            return fail(c, VIT_E_ARG, "layer index out of range");
+        if (dst_bytes != want) return fail(c, VIT_E_ARG, "dst_bytes does not match the boundary size");
+        if (p.N > 0 && (!px || !dst)) return fail(c, VIT_E_ARG, "d_pixels or d_dst is NULL");
+    }
+    if (p.N == 0) return VIT_OK;
+    st = ensure_workspace(c, p.N, p.vt_cols);
+    if (st != VIT_OK) return st;
+    DevPlan dp{};
+    st = stage_plan(c, p, s, dp);
+    if (st != VIT_OK) return st;
+    const int ni = (int)p.imgs.size();
+    auto copy_out = [&](const void *src) -> vit_status {
+        HIP_TRY(c, hipMemcpyAsync(dst, src, dst_bytes, hipMemcpyDeviceToDevice, s));
+        return VIT_OK;
+    };
+
+    if (stop == VIT_DUMP_PATCHES) {
+        LAUNCH(c, launch_dump_patches(px, dp.imgs, ni, p.N, c->s3, c->t3, c->ps, (bf16_t *)dst, s));
+        return VIT_OK;
+    }
+    LAUNCH(c, launch_patch_embed(px, dp.imgs, ni, p.N, c->s3, c->t3, c->ps, c->d_wpe, c->Kp,
+                                 c->pe_b, D, c->x, s));
+    if (stop == VIT_DUMP_EMBED) return copy_out(c->x);
+
+    for (int l = 0; l < L; ++l) {
+        const Layer &w = c->layers[l];
+        LAUNCH(c, launch_layernorm(c->x, l ? c->delta : nullptr, c->x, p.N, D, w.ln1g, w.ln1b,
+                                   c->cfg.ln_eps, c->ln, s));
+        LAUNCH(c, launch_linear(c->ln, p.N, D, w.wqkv, w.bqkv, 3 * D, ACT_NONE, false, c->qkv, s));
+        LAUNCH(c, launch_rope(c->qkv, c->vt, p.vt_cols, dp.rope, (int)p.rope.size(), dp.imgs, D, H,
+                              c->d_cos, c->d_sin, s));
+        if (stop == VIT_DUMP_QKV && arg == l) return copy_out(c->qkv);
+        LAUNCH(c, launch_attention(c->qkv, c->vt, p.vt_cols, c->o, dp.attn, (int)p.attn.size(),
+                                   dp.imgs, D, H, s));
+        if (stop == VIT_DUMP_ATTN && arg == l) return copy_out(c->o);
+        LAUNCH(c, launch_linear(c->o, p.N, D, w.wo, w.bo, D, ACT_NONE, false, c->delta, s));
+        LAUNCH(c, launch_layernorm(c->x, c->delta, c->x, p.N, D, w.ln2g, w.ln2b, c->cfg.ln_eps,
+                                   c->ln, s));
+        LAUNCH(c, launch_linear(c->ln, p.N, D, w.w1, w.b1, c->F, ACT_GELU_TANH, false, c->h1, s));
+        LAUNCH(c, launch_linear(c->h1, p.N, c->F, w.w2, w.b2, D, ACT_NONE, false, c->delta, s));
+        if (stop == VIT_DUMP_LAYER && arg == l) {
+            // the residual add is fused into the next LayerNorm; run it to materialise x
+            LAUNCH(c, launch_layernorm(c->x, c->delta, c->x, p.N, D, c->lnf_g, c->lnf_b,
+                                       c->cfg.ln_eps, c->ln, s));
+            return copy_out(c->x);
+        }
+    }
+    LAUNCH(c, launch_layernorm(c->x, L ? c->delta : nullptr, c->x, p.N, D, c->lnf_g, c->lnf_b,
+                               c->cfg.ln_eps, c->ln, s));
+    if (stop == VIT_DUMP_FINAL_NORM) return copy_out(c->ln);
+    if (stop == VIT_DUMP_MERGED) {
+        LAUNCH(c, launch_dump_merged(c->ln, dp.imgs, ni, p.M, D, (bf16_t *)dst, s));
+        return VIT_OK;
+    }
+    LAUNCH(c, launch_merge_project(c->ln, dp.imgs, ni, p.M, D, c->d_wproj, c->proj_b, c->Dl, out, s));
+    return VIT_OK;
+}
+
+void destroy(vit_ctx *c)
+{
+    if (!c) return;
+    (void)hipDeviceSynchronize();
+    free_workspace(c);
+    void *bufs[] = {c->d_blob, c->d_wpe, c->d_wproj, c->d_cos, c->d_sin, c->d_meta};
+    for (void *b : bufs)
+        if (b) (void)hipFree(b);
+    if (c->h_stage) (void)hipHostFree(c->h_stage);
+    if (c->stage_ev) (void)hipEventDestroy(c->stage_ev);
+    delete c;
+}
+
+}  // namespace
+
+// =========================================================================================
+// C ABI
+// =========================================================================================
+extern "C" {
+
+size_t vit_blob_elems(const vit_config *cfg)
+{
+    if (!cfg || !check_config(*cfg).empty()) return 0;
+    return blob_elems_of(*cfg);
+}
+
+vit_status vit_create(const vit_weights *w, vit_ctx **out)
+{
+    if (!out) return fail(nullptr, VIT_E_ARG, "out is NULL");
+    *out = nullptr;
+    if (!w || !w->blob) return fail(nullptr, VIT_E_ARG, "weights or blob is NULL");
+    const std::string why = check_config(w->cfg);
+    if (!why.empty()) return fail(nullptr, VIT_E_ARG, "invalid config: " + why);
+    const size_t want = blob_elems_of(w->cfg);
+    if (w->blob_elems != want)
+        return fail(nullptr, VIT_E_ARG, "blob has " + std::to_string(w->blob_elems) +
+                                            " elements, config needs " + std::to_string(want));
+
+    vit_ctx *c = new vit_ctx();
+    c->cfg = w->cfg;
+    c->D = w->cfg.hidden;
+    c->H = w->cfg.heads;
+    c->hd = c->D / c->H;
+    c->F = w->cfg.mlp;
+    c->Dl = w->cfg.out_hidden;
+    c->L = w->cfg.layers;
+    c->ps = w->cfg.patch;
+    const int P = 3 * c->ps * c->ps;
+    c->Kp = (int)ceil_div(P, 64) * 64;
+    for (int i = 0; i < 3; ++i) {
+        const double sd = (double)w->cfg.pix_std[i], mu = (double)w->cfg.pix_mean[i];
+        c->s3[i] = (float)(1.0 / (255.0 * sd));
+        c->t3[i] = (float)(-mu / sd);
+    }
+    auto bad = [&](vit_status st, const std::string &m) {
+        g_err = m;
+        destroy(c);
+        return st;
+    };
+#define CREATE_HIP(expr)                                                                      \
+    do {                                                                                      \
+        hipError_t e_ = (expr);                                                               \
+        if (e_ != hipSuccess) {                                                               \
+            (void)hipGetLastError();                                                          \
+            return bad(e_ == hipErrorOutOfMemory ? VIT_E_NOMEM : VIT_E_DEVICE,                \
+                       std::string(#expr) + ": " + hipGetErrorString(e_));                    \
+        }                                                                                     \
+    } while (0)
+
+    CREATE_HIP(hipGetDevice(&c->device));
+    CREATE_HIP(hipEventCreateWithFlags(&c->stage_ev, hipEventDisableTiming));
+    CREATE_HIP(hipMalloc((void **)&c->d_blob, want * sizeof(bf16_t)));
+    CREATE_HIP(hipMemcpy(c->d_blob, w->blob, want * sizeof(bf16_t), hipMemcpyHostToDevice));
+
+    const size_t D = c->D, F = c->F, Dl = c->Dl;
+    const uint16_t *hb = w->blob;
+    size_t off = 0;
+    auto take = [&](size_t n) { const size_t o = off; off += n; return o; };
+    const size_t o_wpe = take(D * P), o_bpe = take(D);
+    c->pe_b = c->d_blob + o_bpe;
+    c->layers.resize(c->L);
+    for (int l = 0; l < c->L; ++l) {
+        Layer &y = c->layers[l];
+        y.ln1g = c->d_blob + take(D);
+        y.ln1b = c->d_blob + take(D);
+        y.wqkv = c->d_blob + take(3 * D * D);
+        y.bqkv = c->d_blob + take(3 * D);
+        y.wo = c->d_blob + take(D * D);
+        y.bo = c->d_blob + take(D);
+        y.ln2g = c->d_blob + take(D);
+        y.ln2b = c->d_blob + take(D);
+        y.w1 = c->d_blob + take(F * D);
+        y.b1 = c->d_blob + take(F);
+        y.w2 = c->d_blob + take(D * F);
+        y.b2 = c->d_blob + take(D);
+    }
+    c->lnf_g = c->d_blob + take(D);
+    c->lnf_b = c->d_blob + take(D);
+    const size_t o_wproj = take(Dl * 9 * D);
+    c->proj_b = c->d_blob + take(Dl);
+
+    // patch projection weight zero-padded to Kp columns ([Z] "Step 5")
+    {
+        std::vector<uint16_t> pad(D * c->Kp, 0);
+        for (size_t r = 0; r < D; ++r)
+            std::memcpy(&pad[r * c->Kp], hb + o_wpe + r * P, P * sizeof(uint16_t));
+        CREATE_HIP(hipMalloc((void **)&c->d_wpe, pad.size() * sizeof(bf16_t)));
+        CREATE_HIP(hipMemcpy(c->d_wpe, pad.data(), pad.size() * sizeof(bf16_t), hipMemcpyHostToDevice));
+    }
+    // projector weight permuted from channel-major (c*9 + pos) to position-major (pos*D + c)
+    {
+        std::vector<uint16_t> perm(Dl * 9 * D);
+        for (size_t j = 0; j < Dl; ++j) {
+            const uint16_t *src = hb + o_wproj + j * 9 * D;
+            uint16_t *dstp = &perm[j * 9 * D];
+            for (size_t ch = 0; ch < D; ++ch)
+                for (int pos = 0; pos < 9; ++pos) dstp[pos * D + ch] = src[ch * 9 + pos];
+        }
+        CREATE_HIP(hipMalloc((void **)&c->d_wproj, perm.size() * sizeof(bf16_t)));
+        CREATE_HIP(hipMemcpy(c->d_wproj, perm.data(), perm.size() * sizeof(bf16_t), hipMemcpyHostToDevice));
+    }
+    // RoPE tables: cos/sin of p * f_j, f_j = base^(-2j/(hd/2)), j < hd/4 ([Z] "Step 3")
+    {
+        const int Q4 = c->hd / 4, half = c->hd / 2;
+        std::vector<float> cs((size_t)kMaxSide * Q4), sn((size_t)kMaxSide * Q4);
+        for (int pos = 0; pos < kMaxSide; ++pos)
+            for (int j = 0; j < Q4; ++j) {
+                const double f = std::pow((double)w->cfg.rope_base, -2.0 * j / (double)half);
+                const double ang = (double)pos * f;
+                cs[(size_t)pos * Q4 + j] = (float)std::cos(ang);
+                sn[(size_t)pos * Q4 + j] = (float)std::sin(ang);
+            }
+        CREATE_HIP(hipMalloc((void **)&c->d_cos, cs.size() * sizeof(float)));
+        CREATE_HIP(hipMalloc((void **)&c->d_sin, sn.size() * sizeof(float)));
+        CREATE_HIP(hipMemcpy(c->d_cos, cs.data(), cs.size() * sizeof(float), hipMemcpyHostToDevice));
+        CREATE_HIP(hipMemcpy(c->d_sin, sn.data(), sn.size() * sizeof(float), hipMemcpyHostToDevice));
+    }
+#undef CREATE_HIP
+    *out = c;
+    return VIT_OK;
+}
+
+void vit_destroy(vit_ctx *ctx) { destroy(ctx); }
+
+vit_status vit_reserve(vit_ctx *ctx, int64_t max_patches)
+{
+    if (!ctx) return fail(nullptr, VIT_E_ARG, "ctx is NULL");
+    if (max_patches <= 0) {
+        ctx->reserve_cap = 0;
+        return VIT_OK;
+    }
+    ctx->reserve_cap = 0;
+    // the transposed-V buffer also holds per-image padding (up to 63 columns per image); it
+    // is sized here for 64 images and may still grow for batches with more images
+    vit_status st = ensure_workspace(ctx, max_patches, max_patches + (int64_t)kVtAlign * 64);
+    if (st != VIT_OK) return st;
+    ctx->reserve_cap = max_patches;
+    return VIT_OK;
+}
+
+int64_t vit_num_tokens(const vit_ctx *ctx, const vit_grid *h_grids, int32_t n_images)
+{
+    if (!ctx || n_images < 0 || (n_images > 0 && !h_grids)) return -1;
+    int64_t m = 0;
+    for (int i = 0; i < n_images; ++i) {
+        if (h_grids[i].gh < 1 || h_grids[i].gw < 1) return -1;
+        m += tokens_of(h_grids[i].gh, h_grids[i].gw);
+    }
+    return m;
+}
+
+int64_t vit_num_patches(const vit_ctx *ctx, const vit_grid *h_grids, int32_t n_images)
+{
+    if (!ctx || n_images < 0 || (n_images > 0 && !h_grids)) return -1;
+    int64_t m = 0;
+    for (int i = 0; i < n_images; ++i) {
+        if (h_grids[i].gh < 1 || h_grids[i].gw < 1) return -1;
+        m += (int64_t)h_grids[i].gh * h_grids[i].gw;
+    }
+    return m;
+}
+
+vit_status vit_encode(vit_ctx *ctx, const uint8_t *d_pixels, const vit_grid *h_grids,
+                      int32_t n_images, float *d_out_rows, void *stream)
+{
+    if (!ctx) return fail(nullptr, VIT_E_ARG, "ctx is NULL");
+    return encode_impl(ctx, d_pixels, h_grids, n_images, d_out_rows, (hipStream_t)stream,
+                       kStopNone, 0, nullptr, 0);
+}
+
+vit_status vit_dump(vit_ctx *ctx, int32_t boundary, int32_t arg, const uint8_t *d_pixels,
+                    const vit_grid *h_grids, int32_t n_images, void *d_dst, size_t dst_bytes,
+                    void *stream)
+{
+    if (!ctx) return fail(nullptr, VIT_E_ARG, "ctx is NULL");
+    if (boundary < 0) return fail(ctx, VIT_E_ARG, "unknown dump boundary");
+    return encode_impl(ctx, d_pixels, h_grids, n_images, nullptr, (hipStream_t)stream, boundary,
+                       arg, d_dst, dst_bytes);
+}
+
+vit_status vit_layout(const vit_grid *h_grids, int32_t n_images, int32_t merge, int32_t *h_types,
+                      int32_t *h_src, int64_t *n_positions)
+{
+    if (!n_positions) return fail(nullptr, VIT_E_ARG, "n_positions is NULL");
+    if (n_images < 0 || (n_images > 0 && !h_grids) || merge < 1)
+        return fail(nullptr, VIT_E_ARG, "bad grids or merge");
+    int64_t total = 0;
+    for (int i = 0; i < n_images; ++i) {
+        if (h_grids[i].gh < 1 || h_grids[i].gw < 1) return fail(nullptr, VIT_E_ARG, "bad grid");
+        const int64_t mh = (h_grids[i].gh + merge - 1) / merge, mw = (h_grids[i].gw + merge - 1) / merge;
+        total += 2 + mh * (mw + 1);
+    }
+    *n_positions = total;
+    if (!h_types && !h_src) return VIT_OK;
+    int64_t p = 0, row = 0;
+    auto put = [&](int32_t t, int32_t s) {
+        if (h_types) h_types[p] = t;
+        if (h_src) h_src[p] = s;
+        ++p;
+    };
+    for (int i = 0; i < n_images; ++i) {
+        const int64_t mh = (h_grids[i].gh + merge - 1) / merge, mw = (h_grids[i].gw + merge - 1) / merge;
+        put(VIT_TOK_START, -1);
+        for (int64_t r = 0; r < mh; ++r) {
+            for (int64_t cc = 0; cc < mw; ++cc) put(VIT_TOK_IMAGE, (int32_t)row++);
+            put(VIT_TOK_NEWLINE, -1);
+        }
+        put(VIT_TOK_END, -1);
+    }
+    return VIT_OK;
+}
+
+vit_status vit_overlay(vit_ctx *ctx, uint16_t *d_embeds, int64_t n_embed_rows,
+                       const int32_t *h_rows, const float *d_rows, int64_t n_rows, int32_t hidden,
+                       void *stream)
+{
+    if (!ctx) return fail(nullptr, VIT_E_ARG, "ctx is NULL");
+    if (n_rows < 0 || n_embed_rows < 0 || hidden < 1)
+        return fail(ctx, VIT_E_ARG, "negative size or hidden < 1");
+    if (hidden != ctx->Dl) return fail(ctx, VIT_E_ARG, "hidden does not match out_hidden");
+    if (n_rows == 0) return VIT_OK;
+    if (!d_embeds || !h_rows || !d_rows) return fail(ctx, VIT_E_ARG, "NULL pointer");
+    std::vector<int32_t> dsts;
+    dsts.reserve(n_rows);
+    for (int64_t t = 0; t < n_rows; ++t) {
+        const int32_t r = h_rows[t];
+        if (r >= n_embed_rows) return fail(ctx, VIT_E_ARG, "placeholder row out of range");
+        if (r >= 0) dsts.push_back(r);
+    }
+    std::sort(dsts.begin(), dsts.end());
+    if (std::adjacent_find(dsts.begin(), dsts.end()) != dsts.end())
+        return fail(ctx, VIT_E_ARG, "two visual rows target the same placeholder row");
+    std::vector<size_t> off;
+    vit_status st = upload_meta(ctx, {{h_rows, (size_t)n_rows * sizeof(int32_t)}},
+                                (hipStream_t)stream, off);
+    if (st != VIT_OK) return st;
+    LAUNCH(ctx, launch_overlay(d_embeds, d_rows, (const int32_t *)(ctx->d_meta + off[0]), n_rows,
+                               hidden, (hipStream_t)stream));
+    return VIT_OK;
+}
+
+const char *vit_last_error(const vit_ctx *ctx) { return ctx ? ctx->err.c_str() : g_err.c_str(); }
+
+// ---------------------------------------------------------------------------------------
+// single-step entry points (vit_ops.h)
+// ---------------------------------------------------------------------------------------
+vit_status vit_op_linear(vit_ctx *ctx, const uint16_t *d_A, int64_t M, int32_t K,
+                         const uint16_t *d_W, const uint16_t *d_b, int32_t N, int32_t act,
+                         int32_t out_f32, void *d_out, void *stream)
+{
+    if (!ctx) return fail(nullptr, VIT_E_ARG, "ctx is NULL");
+    if (M < 0 || N < 1 || K < 64 || K % 64) return fail(ctx, VIT_E_ARG, "bad M, N or K");
+    if (act != VIT_ACT_NONE && act != VIT_ACT_GELU_TANH) return fail(ctx, VIT_E_ARG, "bad act");
+    if (M == 0) return VIT_OK;
+    if (!d_A || !d_W || !d_out) return fail(ctx, VIT_E_ARG, "NULL pointer");
+    LAUNCH(ctx, launch_linear(d_A, M, K, d_W, d_b, N, act, out_f32 != 0, d_out, (hipStream_t)stream));
+    return VIT_OK;
+}
+
+vit_status vit_op_layernorm(vit_ctx *ctx, const uint16_t *d_x, const uint16_t *d_delta,
+                            uint16_t *d_xout, int64_t M, int32_t D, const uint16_t *d_g,
+                            const uint16_t *d_b, float eps, uint16_t *d_out, void *stream)
+{
+    if (!ctx) return fail(nullptr, VIT_E_ARG, "ctx is NULL");
+    if (M < 0 || !supported_hidden(D)) return fail(ctx, VIT_E_ARG, "bad M or D");
+    if (M == 0) return VIT_OK;
+    if (!d_x || !d_g || !d_b || !d_out || (d_delta && !d_xout)) return fail(ctx, VIT_E_ARG, "NULL pointer");
+    LAUNCH(ctx, launch_layernorm(d_x, d_delta, d_xout, M, D, d_g, d_b, eps, d_out, (hipStream_t)stream));
+    return VIT_OK;
+}
+
+int64_t vit_vt_stride(const vit_grid *h_grids, int32_t n_images)
+{
+    if (n_images < 0 || (n_images > 0 && !h_grids)) return -1;
+    int64_t cols = 0;
+    for (int i = 0; i < n_images; ++i) {
+        if (h_grids[i].gh < 1 || h_grids[i].gw < 1) return -1;
+        cols += ceil_div((int64_t)h_grids[i].gh * h_grids[i].gw, kVtAlign) * kVtAlign;
+    }
+    return cols;
+}
+
+vit_status vit_op_rope(vit_ctx *ctx, uint16_t *d_qkv, uint16_t *d_vt, const vit_grid *h_grids,
+                       int32_t n_images, void *stream)
+{
+    if (!ctx) return fail(nullptr, VIT_E_ARG, "ctx is NULL");
+    Plan p;
+    vit_status st = make_plan(ctx, h_grids, n_images, p);
+    if (st != VIT_OK) return st;
+    if (p.N == 0) return VIT_OK;
+    if (!d_qkv || !d_vt) return fail(ctx, VIT_E_ARG, "NULL pointer");
+    DevPlan dp{};
+    if ((st = stage_plan(ctx, p, (hipStream_t)stream, dp)) != VIT_OK) return st;
+    LAUNCH(ctx, launch_rope(d_qkv, d_vt, p.vt_cols, dp.rope, (int)p.rope.size(), dp.imgs, ctx->D,
+                            ctx->H, ctx->d_cos, ctx->d_sin, (hipStream_t)stream));
+    return VIT_OK;
+}
+
+vit_status vit_op_attention(vit_ctx *ctx, const uint16_t *d_qkv, const uint16_t *d_vt,
+                            const vit_grid *h_grids, int32_t n_images, uint16_t *d_o, void *stream)
+{
+    if (!ctx) return fail(nullptr, VIT_E_ARG, "ctx is NULL");
+    Plan p;
+    vit_status st = make_plan(ctx, h_grids, n_images, p);
+    if (st != VIT_OK) return st;
+    if (p.N == 0) return VIT_OK;
+    if (!d_qkv || !d_vt || !d_o) return fail(ctx, VIT_E_ARG, "NULL pointer");
+    DevPlan dp{};
+    if ((st = stage_plan(ctx, p, (hipStream_t)stream, dp)) != VIT_OK) return st;
+    LAUNCH(ctx, launch_attention(d_qkv, d_vt, p.vt_cols, d_o, dp.attn, (int)p.attn.size(), dp.imgs,
+                                 ctx->D, ctx->H, (hipStream_t)stream));
+    return VIT_OK;
+}
+
+vit_status vit_op_merge_project(vit_ctx *ctx, const uint16_t *d_y, const vit_grid *h_grids,
+                                int32_t n_images, float *d_out, void *stream)
+{
+    if (!ctx) return fail(nullptr, VIT_E_ARG, "ctx is NULL");
+    Plan p;
+    vit_status st = make_plan(ctx, h_grids, n_images, p);
+    if (st != VIT_OK) return st;
+    if (p.N == 0) return VIT_OK;
+    if (!d_y || !d_out) return fail(ctx, VIT_E_ARG, "NULL pointer");
+    DevPlan dp{};
+    if ((st = stage_plan(ctx, p, (hipStream_t)stream, dp)) != VIT_OK) return st;
+    LAUNCH(ctx, launch_merge_project(d_y, dp.imgs, (int)p.imgs.size(), p.M, ctx->D, ctx->d_wproj,
+                                     ctx->proj_b, ctx->Dl, d_out, (hipStream_t)stream));
+    return VIT_OK;
+}
+
+}  // extern "C"

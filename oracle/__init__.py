@@ -118,9 +118,12 @@ def float_to_bf16_bits(x: np.ndarray) -> np.ndarray:
 
 
 def pixel_affine(mean, std):
-    """Per-channel (s_c, t_c) in fp32: s_c = 1/(255 std_c), t_c = -mean_c/std_c, in double."""
-    s = np.array([1.0 / (255.0 * sd) for sd in std], dtype=np.float32)
-    t = np.array([-m / sd for m, sd in zip(mean, std)], dtype=np.float32)
+    """Per-channel (s_c, t_c) in fp32: s_c = 1/(255 std_c), t_c = -mean_c/std_c, evaluated in
+    double from the fp32 values of mean and std (the configuration carries them in fp32)."""
+    m32 = [float(np.float32(m)) for m in mean]
+    s32 = [float(np.float32(sd)) for sd in std]
+    s = np.array([1.0 / (255.0 * sd) for sd in s32], dtype=np.float32)
+    t = np.array([-m / sd for m, sd in zip(m32, s32)], dtype=np.float32)
     return s, t
 
 

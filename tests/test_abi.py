@@ -1,0 +1,84 @@
+"""The C ABI library loads and exports every function the public headers declare; its
+host-only logic (layout, sizes, argument validation) is checked without a GPU."""
+import ctypes
+import os
+import re
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+import multimodal_vision_encoder_amd as vit
+import oracle
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for h in ("vit.h", "vit_ops.h"):
+        text = open(os.path.join(ROOT, "include", h)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(vit_\w+)\s*\(", text))
+    return names
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 17
+    L = ctypes.CDLL(vit.LIB_PATH)
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+    assert names == set(vit.EXPORTS)
+
+
+def test_blob_size_agrees_with_generator():
+    for cfg in (synth.TINY, synth.V41, synth.V4, synth.V41_ONE_LAYER):
+        assert vit.lib().vit_blob_elems(vit.make_config(cfg)) == cfg.blob_elems()
+    assert vit.lib().vit_blob_elems(vit.make_config(replace(synth.TINY, hidden=100))) == 0
+
+
+@pytest.mark.parametrize("grids", [[(96, 96)], [(54, 63)], [(6, 6), (5, 7), (1, 1), (10, 4)],
+                                   synth.packed_grids_batch()])
+def test_layout_matches_oracle(grids):
+    t, s = vit.layout(grids)
+    ot, os_ = oracle.layout(grids)
+    assert np.array_equal(t, ot) and np.array_equal(s, os_)
+
+
+def test_layout_v41_closed_form():
+    t, s = vit.layout([(96, 96)])
+    assert t.size == 1058 and (t == vit.TOK_IMAGE).sum() == 1024 and (t == vit.TOK_NEWLINE).sum() == 32
+
+
+def test_vt_stride():
+    assert vit.vt_stride([(96, 96)]) == 9216
+    assert vit.vt_stride([(5, 7), (1, 1)]) == 64 + 64
+    assert vit.vt_stride([(9, 15)]) == 192
+
+
+def test_create_rejects_bad_weights_without_touching_the_device():
+    L = vit.lib()
+    cfg = synth.TINY
+    blob = synth.make_weights(cfg)
+    ctx = ctypes.c_void_p()
+    for bad_cfg, n in [(replace(cfg, heads=3), blob.size), (replace(cfg, merge=2), blob.size),
+                       (cfg, blob.size - 1), (replace(cfg, mlp=100), blob.size),
+                       (replace(cfg, pix_std=(0.5, 0.0, 0.5)), blob.size)]:
+        w = vit.Weights()
+        w.cfg = vit.make_config(bad_cfg)
+        w.blob = blob.ctypes.data
+        w.blob_elems = n
+        assert L.vit_create(ctypes.byref(w), ctypes.byref(ctx)) == vit.VIT_E_ARG
+        assert not ctx.value
+        assert L.vit_last_error(None)
+    assert L.vit_create(None, ctypes.byref(ctx)) == vit.VIT_E_ARG
+
+
+def test_null_context_is_rejected():
+    L = vit.lib()
+    g = vit.grid_array([(6, 6)])
+    assert L.vit_encode(None, None, g, 1, None, None) == vit.VIT_E_ARG
+    assert L.vit_num_tokens(None, g, 1) == -1
+    assert L.vit_overlay(None, None, 0, None, None, 0, 128, None) == vit.VIT_E_ARG

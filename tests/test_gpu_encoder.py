@@ -1,0 +1,223 @@
+"""End-to-end parity of vit_encode / vit_dump / vit_overlay against the CPU oracle, plus the
+boundary's error behaviour, determinism and image isolation."""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+import multimodal_vision_encoder_amd as vit
+import oracle
+import synth
+from tests.gpu_util import (assert_bf16_close, assert_projector_gate, from_dev_bf16, rel_l2,
+                            require_gpu)
+
+pytestmark = pytest.mark.gpu
+
+
+def run(cfg, blob, grids, pixels=None):
+    torch = require_gpu()
+    px = synth.make_pixels(cfg, grids) if pixels is None else pixels
+    enc = vit.Encoder(cfg, blob)
+    out = enc.encode(torch.from_numpy(px).cuda(), grids)
+    torch.cuda.synchronize()
+    return enc, px, out.cpu().numpy()
+
+
+# ------------------------------------------------------------------------------------------
+# bit-exact parts: patchify, the K padding of the patch projection, merge gather, overlay
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg,grids", [(synth.TINY, [(6, 6)]), (synth.V41, [(5, 7), (2, 9), (1, 1)]),
+                                       (synth.V41, [(24, 24)])], ids=["tiny", "ragged", "one_layer"])
+def test_patchify_bit_exact(cfg, grids):
+    torch = require_gpu()
+    c1 = replace(cfg, layers=0, out_hidden=16)
+    enc = vit.Encoder(c1, synth.make_weights(c1))
+    px = synth.make_pixels(c1, grids)
+    got = from_dev_bf16(enc.dump(vit.DUMP_PATCHES, torch.from_numpy(px).cuda(), grids))
+    torch.cuda.synchronize()
+    off, pix = 0, 0
+    for gh, gw in grids:
+        n, npx = gh * gw, 14 * gh * 14 * gw * 3
+        assert np.array_equal(got[off:off + n], oracle.patchify(px[pix:pix + npx], gh, gw, c1))
+        off += n
+        pix += npx
+
+
+def test_identity_patch_projection_bit_exact():
+    """W_pe = identity (D = 1024 >= 588 columns), b = 0: x0[:, :588] = patches and 0 after;
+    exact because each output has one non-zero product, so the zero K padding (588 -> 640)
+    and the patchify gather are checked together."""
+    torch = require_gpu()
+    cfg = replace(synth.V41, layers=0, out_hidden=16)
+    blob = synth.make_weights(cfg)
+    W = synth.split_weights(cfg, blob)
+    W["pe.w"][:] = 0
+    W["pe.w"][np.arange(588), np.arange(588)] = 0x3F80
+    grids = [(7, 5), (3, 3)]
+    enc = vit.Encoder(cfg, blob)
+    px = synth.make_pixels(cfg, grids)
+    x0 = from_dev_bf16(enc.dump(vit.DUMP_EMBED, torch.from_numpy(px).cuda(), grids))
+    torch.cuda.synchronize()
+    P = np.concatenate([oracle.patchify(px[:14 * 7 * 14 * 5 * 3], 7, 5, cfg),
+                        oracle.patchify(px[14 * 7 * 14 * 5 * 3:], 3, 3, cfg)])
+    assert np.array_equal(x0[:, :588], P)
+    assert not x0[:, 588:].any()
+
+
+def test_merge_gather_one_hot_projector_bit_exact():
+    """W_proj row j = e_sigma(j) over all 9D columns (out_hidden = 9D), b = 0: the projector
+    output is the merged input permuted by sigma, exactly; the merged input comes from the
+    oracle's merge of the same seeded rows.  A 5x7 grid exercises the right/bottom padding."""
+    torch = require_gpu()
+    cfg = replace(synth.TINY, out_hidden=9 * synth.TINY.hidden)
+    blob = synth.make_weights(cfg)
+    W = synth.split_weights(cfg, blob)
+    sigma = np.random.default_rng(7).permutation(9 * cfg.hidden)
+    W["proj.w"][:] = 0
+    W["proj.w"][np.arange(9 * cfg.hidden), sigma] = 0x3F80
+    enc = vit.Encoder(cfg, blob)
+    grids = [(5, 7), (6, 6), (1, 2)]
+    N = sum(a * b for a, b in grids)
+    y = synth.normal_bf16(201, 0, N * cfg.hidden).reshape(N, cfg.hidden)
+    from tests.gpu_util import to_dev_bf16
+    got = enc.op_merge_project(to_dev_bf16(y), grids).cpu().numpy()
+    torch.cuda.synchronize()
+    yf = synth.bf16_bits_to_f32(y)
+    off, want = 0, []
+    for gh, gw in grids:
+        want.append(oracle.merge(yf[off:off + gh * gw], gh, gw)[:, sigma])
+        off += gh * gw
+    assert np.array_equal(got, np.concatenate(want))
+
+
+def test_merged_dump_is_the_channel_major_unfold_of_the_final_norm():
+    """vit_dump(MERGED) (the projector's own gather) equals the unfold of vit_dump(FINAL_NORM)
+    with right/bottom zero padding, element for element."""
+    torch = require_gpu()
+    cfg = synth.TINY
+    enc = vit.Encoder(cfg, synth.make_weights(cfg))
+    grids = [(5, 7), (6, 9)]
+    px = torch.from_numpy(synth.make_pixels(cfg, grids)).cuda()
+    y = enc.dump(vit.DUMP_FINAL_NORM, px, grids).float()
+    A = from_dev_bf16(enc.dump(vit.DUMP_MERGED, px, grids))
+    torch.cuda.synchronize()
+    off, t0 = 0, 0
+    for gh, gw in grids:
+        img = y[off:off + gh * gw].reshape(gh, gw, -1).permute(2, 0, 1)[None].cpu()
+        img = torch.nn.functional.pad(img, (0, (-gw) % 3, 0, (-gh) % 3))
+        want = torch.nn.functional.unfold(img, 3, stride=3)[0].T.numpy()
+        assert np.array_equal(A[t0:t0 + want.shape[0]], want)
+        off += gh * gw
+        t0 += want.shape[0]
+
+
+# ------------------------------------------------------------------------------------------
+# end to end
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("perturbed", [False, True])
+def test_tiny_end_to_end(perturbed):
+    wl = synth.workload("tiny")
+    blob = synth.make_weights(wl.cfg, perturbed=perturbed)
+    enc, px, got = run(wl.cfg, blob, wl.grids)
+    want = oracle.encode(wl.cfg, blob, px, wl.grids)
+    assert got.shape == (4, 128)
+    assert_projector_gate(got, want, "tiny")
+
+
+def test_tiny_ragged_multi_image():
+    cfg = synth.TINY
+    grids = [(5, 7), (6, 6), (1, 1), (10, 4)]
+    blob = synth.make_weights(cfg, perturbed=True)
+    enc, px, got = run(cfg, blob, grids)
+    want = oracle.encode(cfg, blob, px, grids)
+    assert got.shape[0] == 6 + 4 + 1 + 8
+    assert_projector_gate(got, want, "tiny ragged")
+
+
+@pytest.mark.parametrize("perturbed", [False, True])
+def test_one_layer_end_to_end(perturbed):
+    """One full-width layer (336x336 image, 576 patches, 9216 -> 5120 projector), with the
+    boundary tensors compared on the way to locate the first divergence."""
+    torch = require_gpu()
+    wl = synth.workload("one_layer")
+    blob = synth.make_weights(wl.cfg, perturbed=perturbed)
+    enc, px, got = run(wl.cfg, blob, wl.grids)
+    W = oracle.Weights(wl.cfg, blob)
+    dumps = {}
+    want = oracle.encode_image(wl.cfg, W, px, 24, 24, workers=8, dumps=dumps)
+    d_px = torch.from_numpy(px).cuda()
+    assert np.array_equal(from_dev_bf16(enc.dump(vit.DUMP_PATCHES, d_px, wl.grids)), dumps["patches"])
+    assert_bf16_close(from_dev_bf16(enc.dump(vit.DUMP_EMBED, d_px, wl.grids)), dumps["embed"],
+                      atol=1e-6, what="embed")
+    for name, b, arg in (("qkv0", vit.DUMP_QKV, 0), ("attn0", vit.DUMP_ATTN, 0),
+                         ("layer0", vit.DUMP_LAYER, 0), ("final_norm", vit.DUMP_FINAL_NORM, 0)):
+        g = from_dev_bf16(enc.dump(b, d_px, wl.grids, arg=arg))
+        assert rel_l2(g, dumps[name]) < 1e-2, name
+    assert_projector_gate(got, want, "one layer")
+
+
+def test_uniform_gray_image_rows_agree():
+    """A flat RGB-127 canvas: all patches equal, v equal at every position, so every visual
+    row is the same vector up to rounding (positions enter only through q and k)."""
+    cfg = synth.V41_ONE_LAYER
+    grids = [(12, 12)]
+    px = np.full(14 * 12 * 14 * 12 * 3, 127, np.uint8)
+    blob = synth.make_weights(cfg)
+    enc, _, got = run(cfg, blob, grids, pixels=px)
+    want = oracle.encode(cfg, blob, px, grids, workers=8)
+    assert_projector_gate(got, want, "uniform")
+    assert rel_l2(got, np.repeat(got[:1], got.shape[0], 0)) < 1e-2
+
+
+# ------------------------------------------------------------------------------------------
+# boundary behaviour
+# ------------------------------------------------------------------------------------------
+def test_errors_publish_nothing():
+    torch = require_gpu()
+    cfg = synth.TINY
+    enc = vit.Encoder(cfg, synth.make_weights(cfg))
+    grids_ok = [(6, 6)]
+    px = torch.from_numpy(synth.make_pixels(cfg, grids_ok)).cuda()
+    out = torch.full((4, cfg.out_hidden), 7.0, device="cuda")
+    over = replace(cfg, max_tokens_per_image=3)
+    enc_small = vit.Encoder(over, synth.make_weights(over))
+    with pytest.raises(vit.VitError) as e:
+        enc_small.encode(px, grids_ok, out=out)
+    assert e.value.status == vit.VIT_E_BUDGET
+    with pytest.raises(vit.VitError) as e:
+        enc.encode(px, [(6, 6), (0, 3)], out=out)
+    assert e.value.status == vit.VIT_E_ARG
+    with pytest.raises(vit.VitError) as e:
+        enc.encode(px, [(6, 6), (6000, 1)], out=out)
+    assert e.value.status == vit.VIT_E_ARG
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all()), "a rejected call must not write any output"
+    # an empty batch is valid and writes nothing
+    assert enc.encode(px, [], out=out).shape == out.shape
+    with pytest.raises(vit.VitError):
+        enc.overlay(torch.zeros((8, cfg.out_hidden), dtype=torch.bfloat16, device="cuda"),
+                    [1, 1], torch.zeros((2, cfg.out_hidden), device="cuda"))
+    with pytest.raises(vit.VitError):
+        enc.overlay(torch.zeros((8, cfg.out_hidden), dtype=torch.bfloat16, device="cuda"),
+                    [8], torch.zeros((1, cfg.out_hidden), device="cuda"))
+    enc.close()
+    enc_small.close()
+
+
+def test_deterministic_and_isolated():
+    """Two runs are bitwise identical, and an image's rows do not depend on the other images
+    of the packed batch."""
+    torch = require_gpu()
+    cfg = synth.V41_ONE_LAYER
+    blob = synth.make_weights(cfg, perturbed=True)
+    grids = [(12, 15), (9, 9)]
+    px = synth.make_pixels(cfg, grids)
+    enc = vit.Encoder(cfg, blob)
+    d = torch.from_numpy(px).cuda()
+    a = enc.encode(d, grids).cpu().numpy()
+    b = enc.encode(d, grids).cpu().numpy()
+    n0 = 14 * 12 * 14 * 15 * 3
+    alone = enc.encode(torch.from_numpy(px[n0:]).cuda(), grids[1:]).cpu().numpy()
+    torch.cuda.synchronize()
+    assert np.array_equal(a, b)
+    assert np.array_equal(a[4 * 5:], alone)

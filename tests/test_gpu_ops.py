@@ -1,0 +1,294 @@
+"""Per-step parity of the HIP kernels against the CPU oracle, on seeded inputs that come
+from the generator (never from the GPU), at small ragged sizes and at the encoder's real
+shapes (sampled rows where the oracle would be too slow for all of them)."""
+import numpy as np
+import pytest
+
+import multimodal_vision_encoder_amd as vit
+import oracle
+import synth
+from tests.gpu_util import (assert_bf16_close, bf16_bits_of, from_dev_bf16, require_gpu,
+                            seeded_bf16, to_dev_bf16, rel_l2)
+
+pytestmark = pytest.mark.gpu
+
+_encs = {}
+
+
+def encoder(name="tiny", perturbed=False):
+    """Encoder contexts are cached per (config, weights) for the session."""
+    key = (name, perturbed)
+    if key not in _encs:
+        require_gpu()
+        cfg = {"tiny": synth.TINY, "v41_1layer": synth.V41_ONE_LAYER}[name]
+        blob = synth.make_weights(cfg, perturbed=perturbed)
+        _encs[key] = (vit.Encoder(cfg, blob), cfg, blob)
+    return _encs[key]
+
+
+def f32(bits):
+    return synth.bf16_bits_to_f32(bits)
+
+
+# ------------------------------------------------------------------------------------------
+# linear layers (QKV, out-proj, fc1 + GELU, fc2, projector epilogue)
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("M,K,N,act,out_f32", [
+    (300, 128, 200, vit.ACT_NONE, False),       # ragged M and N, several tiles
+    (1, 64, 5, vit.ACT_NONE, True),             # degenerate single row, tiny N
+    (257, 192, 130, vit.ACT_GELU_TANH, False),
+    (129, 256, 64, vit.ACT_NONE, True),
+])
+def test_linear_small(M, K, N, act, out_f32):
+    torch = require_gpu()
+    enc, _, _ = encoder()
+    A = seeded_bf16((M, K), 101, 0)
+    W = seeded_bf16((N, K), 101, 1, std=0.05)
+    b = seeded_bf16((N,), 101, 2, std=0.1)
+    got = enc.op_linear(to_dev_bf16(A), to_dev_bf16(W), to_dev_bf16(b), act, out_f32)
+    torch.cuda.synchronize()
+    want = oracle.linear(f32(A), f32(W), f32(b), act=act, round_out=not out_f32)
+    if out_f32:
+        np.testing.assert_allclose(got.cpu().numpy(), want, rtol=1e-5, atol=1e-5)
+    else:
+        assert_bf16_close(from_dev_bf16(got), want, what="linear")
+
+
+def test_linear_one_hot_is_exact():
+    """One-hot weight rows copy input columns: exact, whatever the accumulation order."""
+    torch = require_gpu()
+    enc, _, _ = encoder()
+    M, K, N = 200, 256, 96
+    A = seeded_bf16((M, K), 102)
+    sel = np.random.default_rng(0).permutation(K)[:N]
+    W = np.zeros((N, K), np.uint16)
+    W[np.arange(N), sel] = 0x3F80
+    got = from_dev_bf16(enc.op_linear(to_dev_bf16(A), to_dev_bf16(W), None))
+    torch.cuda.synchronize()
+    assert np.array_equal(got, f32(A)[:, sel])
+
+
+@pytest.mark.parametrize("N,K,act", [(3072, 1024, vit.ACT_NONE), (1024, 1024, vit.ACT_NONE),
+                                     (4096, 1024, vit.ACT_GELU_TANH), (1024, 4096, vit.ACT_NONE)],
+                         ids=["qkv", "out_proj", "fc1_gelu", "fc2"])
+def test_linear_full_size_sampled(N, K, act):
+    """The block's GEMMs at the 1024-token image's shape (M = 9216 patches), checked on
+    sampled rows including the last tile."""
+    torch = require_gpu()
+    enc, _, _ = encoder()
+    M = 9216
+    A = seeded_bf16((M, K), 103, 0)
+    W = seeded_bf16((N, K), 103, 1, std=0.02)
+    b = seeded_bf16((N,), 103, 2, std=0.02)
+    got = from_dev_bf16(enc.op_linear(to_dev_bf16(A), to_dev_bf16(W), to_dev_bf16(b), act))
+    torch.cuda.synchronize()
+    rows = np.r_[0:3, 127:130, 4000:4003, M - 5:M]
+    want = oracle.linear(f32(A[rows]), f32(W), f32(b), act=act)
+    assert_bf16_close(got[rows], want, what="linear full size")
+
+
+# ------------------------------------------------------------------------------------------
+# LayerNorm (+ residual)
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("M,D,residual", [(37, 64, False), (1000, 1024, True), (9216, 1024, True),
+                                          (5, 256, True)])
+def test_layernorm(M, D, residual):
+    torch = require_gpu()
+    enc, _, _ = encoder()
+    x = seeded_bf16((M, D), 104, 0, std=2.0, mean=0.5)
+    dl = seeded_bf16((M, D), 104, 1, std=1.0)
+    g = seeded_bf16((D,), 104, 2, std=0.1, mean=1.0)
+    b = seeded_bf16((D,), 104, 3, std=0.1)
+    dx = to_dev_bf16(x)
+    out = enc.op_layernorm(dx, to_dev_bf16(g), to_dev_bf16(b), 1e-6,
+                           delta=to_dev_bf16(dl) if residual else None, xout=dx if residual else None)
+    torch.cuda.synchronize()
+    xr = oracle.add_round(f32(x), f32(dl)) if residual else f32(x)
+    if residual:
+        assert np.array_equal(from_dev_bf16(dx), xr), "residual add must be exact"
+    want = oracle.layernorm(xr, f32(g), f32(b), 1e-6)
+    assert_bf16_close(from_dev_bf16(out), want, atol=1e-6, what="layernorm")
+
+
+# ------------------------------------------------------------------------------------------
+# RoPE + attention
+# ------------------------------------------------------------------------------------------
+def _qkv_for(grids, D, seed, std=1.0):
+    N = sum(gh * gw for gh, gw in grids)
+    return seeded_bf16((N, 3 * D), seed, 0, std=std)
+
+
+def _oracle_rope(qkv_f, grids, cfg):
+    out, off = [], 0
+    for gh, gw in grids:
+        n = gh * gw
+        out.append(oracle.rope_qk(qkv_f[off:off + n], gw, cfg.hidden, cfg.heads, cfg.rope_base))
+        off += n
+    return np.concatenate(out)
+
+
+@pytest.mark.parametrize("name,grids", [("tiny", [(6, 6)]), ("tiny", [(5, 7), (1, 1), (9, 12)]),
+                                        ("v41_1layer", [(24, 24)]), ("v41_1layer", [(7, 11), (30, 3)])])
+def test_rope_exact(name, grids):
+    """RoPE multiplies by the same fp32 cos/sin and rounds once per element on both sides."""
+    torch = require_gpu()
+    enc, cfg, _ = encoder(name)
+    qkv = _qkv_for(grids, cfg.hidden, 105)
+    d = to_dev_bf16(qkv)
+    vt = enc.op_rope(d, grids)
+    torch.cuda.synchronize()
+    want = _oracle_rope(f32(qkv), grids, cfg)
+    got = from_dev_bf16(d)
+    assert np.array_equal(got, want)
+    # v transposed per head, each image at its own 64-aligned column block, zero padding
+    vtn = from_dev_bf16(vt)
+    H, hd = cfg.heads, cfg.head_dim
+    off = col = 0
+    for gh, gw in grids:
+        n = gh * gw
+        v = f32(qkv[off:off + n, 2 * cfg.hidden:]).reshape(n, H, hd).transpose(1, 2, 0)
+        assert np.array_equal(vtn[:, :, col:col + n], v)
+        pad = -(-n // 64) * 64
+        assert not vtn[:, :, col + n:col + pad].any()
+        off += n
+        col += pad
+
+
+def _attention_check(got, qkv_rot, grids, cfg, rows_per_image=None):
+    off = 0
+    for gh, gw in grids:
+        n = gh * gw
+        sl = qkv_rot[off:off + n]
+        rows = range(n) if rows_per_image is None else sorted(set(r for r in rows_per_image(n)))
+        for r in rows:
+            want = oracle.attention(sl, cfg.hidden, cfg.heads, rows=(r, r + 1))[r]
+            g = got[off + r]
+            vmax = np.abs(sl[:, 2 * cfg.hidden:]).max()
+            # P is rounded to bf16 before P.V on the GPU (2^-9 relative per weight), plus the
+            # output rounding on both sides
+            tol = 2.0 ** -8 * vmax + 2.0 ** -7 * np.abs(want)
+            assert np.all(np.abs(g - want) <= tol), (gh, gw, r, np.abs(g - want).max())
+        off += n
+
+
+@pytest.mark.parametrize("name,grids", [("tiny", [(6, 6)]), ("tiny", [(5, 7), (1, 1), (12, 15)]),
+                                        ("v41_1layer", [(24, 24)]),
+                                        ("v41_1layer", [(13, 21), (1, 2), (3, 3)])])
+def test_attention_small(name, grids):
+    torch = require_gpu()
+    enc, cfg, _ = encoder(name)
+    qkv = _qkv_for(grids, cfg.hidden, 106)
+    d = to_dev_bf16(qkv)
+    vt = enc.op_rope(d, grids)
+    o = enc.op_attention(d, vt, grids)
+    torch.cuda.synchronize()
+    rot = _oracle_rope(f32(qkv), grids, cfg)
+    _attention_check(from_dev_bf16(o), rot, grids, cfg,
+                     rows_per_image=lambda n: list(range(min(n, 20))) + [n - 1, n // 2])
+
+
+def test_attention_single_patch_image_is_v():
+    """A 1-patch image attends only to itself: output = v exactly."""
+    torch = require_gpu()
+    enc, cfg, _ = encoder("v41_1layer")
+    grids = [(1, 1), (2, 3), (1, 1)]
+    qkv = _qkv_for(grids, cfg.hidden, 107)
+    d = to_dev_bf16(qkv)
+    vt = enc.op_rope(d, grids)
+    o = from_dev_bf16(enc.op_attention(d, vt, grids))
+    torch.cuda.synchronize()
+    D = cfg.hidden
+    assert np.array_equal(o[0], f32(qkv[0, 2 * D:]))
+    assert np.array_equal(o[7], f32(qkv[7, 2 * D:]))
+
+
+def test_attention_images_are_isolated():
+    """Changing one image of a packed batch leaves the other images bitwise unchanged."""
+    torch = require_gpu()
+    enc, cfg, _ = encoder("v41_1layer")
+    grids = [(9, 12), (15, 6), (4, 4)]
+    qkv = _qkv_for(grids, cfg.hidden, 108)
+    qkv2 = qkv.copy()
+    n0 = 9 * 12
+    qkv2[n0:n0 + 90] = _qkv_for([(9, 10)], cfg.hidden, 109)
+    outs = []
+    for q in (qkv, qkv2):
+        d = to_dev_bf16(q)
+        vt = enc.op_rope(d, grids)
+        outs.append(from_dev_bf16(enc.op_attention(d, vt, grids)))
+    torch.cuda.synchronize()
+    assert np.array_equal(outs[0][:n0], outs[1][:n0])
+    assert np.array_equal(outs[0][n0 + 90:], outs[1][n0 + 90:])
+    assert not np.array_equal(outs[0][n0:n0 + 90], outs[1][n0:n0 + 90])
+
+
+@pytest.mark.parametrize("grids", [[(96, 96)], [(54, 63)]], ids=["v41_1024", "v4_384"])
+def test_attention_full_size_sampled(grids):
+    """Attention over one 9216-patch (or 3402-patch) image, sampled query rows."""
+    torch = require_gpu()
+    enc, cfg, _ = encoder("v41_1layer")
+    qkv = _qkv_for(grids, cfg.hidden, 110)
+    d = to_dev_bf16(qkv)
+    vt = enc.op_rope(d, grids)
+    o = from_dev_bf16(enc.op_attention(d, vt, grids))
+    torch.cuda.synchronize()
+    rot = _oracle_rope(f32(qkv), grids, cfg)
+    _attention_check(o, rot, grids, cfg, rows_per_image=lambda n: [0, 1, 127, 128, n // 3, n - 1])
+
+
+def test_attention_packed16_sampled():
+    """The packed 16-image batch (varlen, block-diagonal), sampled rows of every image."""
+    torch = require_gpu()
+    enc, cfg, _ = encoder("v41_1layer")
+    grids = synth.workload("packed16").grids
+    qkv = _qkv_for(grids, cfg.hidden, 111)
+    d = to_dev_bf16(qkv)
+    vt = enc.op_rope(d, grids)
+    o = from_dev_bf16(enc.op_attention(d, vt, grids))
+    torch.cuda.synchronize()
+    off = 0
+    for gh, gw in grids:
+        n = gh * gw
+        sl = oracle.rope_qk(f32(qkv[off:off + n]), gw, cfg.hidden, cfg.heads, cfg.rope_base)
+        for r in (0, n - 1):
+            want = oracle.attention(sl, cfg.hidden, cfg.heads, rows=(r, r + 1))[r]
+            tol = 2.0 ** -8 * np.abs(sl[:, 2 * cfg.hidden:]).max() + 2.0 ** -7 * np.abs(want)
+            assert np.all(np.abs(o[off + r] - want) <= tol), (gh, gw, r)
+        off += n
+
+
+# ------------------------------------------------------------------------------------------
+# merge + projector, overlay
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("grids", [[(6, 6)], [(5, 7)], [(5, 7), (3, 9), (1, 1), (4, 8)]])
+def test_merge_project(grids):
+    torch = require_gpu()
+    enc, cfg, blob = encoder("tiny", perturbed=True)
+    N = sum(a * b for a, b in grids)
+    y = seeded_bf16((N, cfg.hidden), 112)
+    got = enc.op_merge_project(to_dev_bf16(y), grids).cpu().numpy()
+    torch.cuda.synchronize()
+    W = oracle.Weights(cfg, blob)
+    off, want = 0, []
+    for gh, gw in grids:
+        A = oracle.merge(f32(y[off:off + gh * gw]), gh, gw)
+        want.append(oracle.linear(A, W["proj.w"], W["proj.b"], round_out=False))
+        off += gh * gw
+    want = np.concatenate(want)
+    np.testing.assert_allclose(got, want, rtol=1e-4, atol=1e-4)
+
+
+def test_overlay_exact():
+    torch = require_gpu()
+    enc, cfg, _ = encoder("tiny")
+    R, Dl, T = 50, cfg.out_hidden, 12
+    emb = seeded_bf16((R, Dl), 113)
+    rows = synth.normal_f32(113, 1, T * Dl, 0.0, 3.0).reshape(T, Dl)
+    dst = list(synth.seeded_distinct_rows(T, R))
+    dst[3] = -1
+    d_emb = to_dev_bf16(emb)
+    enc.overlay(d_emb, dst, torch.from_numpy(rows).cuda())
+    torch.cuda.synchronize()
+    want = oracle.overlay(emb, dst, rows)
+    got = d_emb.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, want)

@@ -1,0 +1,217 @@
+#!/usr/bin/env python3
+"""Throughput of the vision-encoder hot path on one MI355X.
+
+One step = one whole pass of the hot path over one synthetic batch: vit_encode (patchify,
+patch projection, the ViT blocks, final LayerNorm, 3x3 merge + projector), the span layout
+and vit_overlay of the visual rows into a prompt embedding matrix.  Inputs are resident in
+HBM before the timed region starts.  Prints one JSON line on stdout; progress on stderr.
+
+Default workload: one 1344x1344 image (96x96 = 9216 patches, 32 layers of width 1024 with
+16 heads and MLP 4096, 1024 merged tokens projected to 5120).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def flops_per_pass(cfg, grids):
+    """Algorithmic MFMA FLOPs: patch projection at K = 588, per layer QKV + out-proj + MLP +
+    attention (QK^T and PV over each image's own patches only), projector at K = 9D."""
+    D, F, L, Dl = cfg.hidden, cfg.mlp, cfg.layers, cfg.out_hidden
+    tot = {"patch_embed": 0, "qkv": 0, "attention": 0, "out_proj": 0, "fc1": 0, "fc2": 0,
+           "projector": 0}
+    for gh, gw in grids:
+        n, m = gh * gw, cfg.tokens(gh, gw)
+        tot["patch_embed"] += 2 * n * cfg.patch_dim * D
+        tot["qkv"] += L * 6 * n * D * D
+        tot["attention"] += L * 4 * n * n * D
+        tot["out_proj"] += L * 2 * n * D * D
+        tot["fc1"] += L * 2 * n * D * F
+        tot["fc2"] += L * 2 * n * F * D
+        tot["projector"] += 2 * m * 9 * D * Dl
+    return tot
+
+
+def bytes_per_pass(cfg, grids, vt_cols):
+    """Algorithmic HBM bytes of the memory-bound steps (one read and one write of each
+    tensor a step must touch)."""
+    D, L, Dl = cfg.hidden, cfg.layers, cfg.out_hidden
+    N = sum(gh * gw for gh, gw in grids)
+    M = sum(cfg.tokens(gh, gw) for gh, gw in grids)
+    ln_first = 2 * N * D * 2                   # read x, write ln
+    ln_res = 4 * N * D * 2                     # read x and delta, write x and ln
+    n_res = 2 * L                              # ln1 of layers 1.., ln2 of every layer, final
+    ln = (ln_first + n_res * ln_res) if L > 0 else ln_first
+    rope = L * (8 * N * D + 2 * N * D + 2 * vt_cols * D)   # q,k in+out, v in, v^T out
+    overlay = M * Dl * (4 + 2) + 4 * M
+    return {"layernorm": ln, "rope": rope, "overlay": overlay}
+
+
+def cpu_baseline(cfg, blob, px, grids):
+    """The CPU oracle on the host's cores: fixed part (patchify, patch projection, final LN,
+    merge, projector) plus one of the layers, all patches of the first image; the full pass
+    is extrapolated as T_fixed + layers * T_layer."""
+    import oracle
+    cores = min(16, len(os.sched_getaffinity(0)))
+    gh, gw = grids[0]
+    W = oracle.Weights(cfg, blob)
+    for name, _ in cfg.tensor_shapes():
+        if name.endswith(".w") and (name.startswith("l0.") or not name.startswith("l")):
+            W.T(name)
+    n_img = (cfg.patch * gh) * (cfg.patch * gw) * 3
+    img = px[:n_img]
+    t0 = time.perf_counter()
+    oracle.encode_image(cfg, W, img, gh, gw, workers=cores, layers=0)
+    t_fixed = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.encode_image(cfg, W, img, gh, gw, workers=cores, layers=1)
+    t_one = time.perf_counter() - t0
+    t_layer = max(t_one - t_fixed, 0.0)
+    t_pass = t_fixed + cfg.layers * t_layer
+    tokens = cfg.tokens(gh, gw)
+    return {"value": tokens / t_pass, "unit": "visual tokens/s", "cores": cores, "kind": "oracle",
+            "sample": (f"first image ({gh}x{gw} patches): patch projection + final LN + merge + "
+                       f"projector timed ({t_fixed:.2f} s) and 1 of {cfg.layers} layers timed "
+                       f"({t_layer:.2f} s) on all patches, fp32 oracle, rows split over {cores} "
+                       f"threads; full pass extrapolated as T_fixed + {cfg.layers} T_layer = "
+                       f"{t_pass:.1f} s"),
+            "seconds_per_pass": t_pass}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="v41_1024",
+                    choices=["tiny", "one_layer", "v4_384", "v41_1024", "packed16"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel timing loop")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: the encoder's hot path is "
+                                   "measured on one MI355X (shard images across GPUs to scale "
+                                   "out); run with --gpus 1"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import multimodal_vision_encoder_amd as vit
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    wl = synth.workload(args.workload)
+    cfg, grids = wl.cfg, wl.grids
+    N, M = wl.n_patches, wl.n_tokens
+    log(f"workload {args.workload}: {len(grids)} image(s), {N} patches, {M} tokens")
+    t = time.perf_counter()
+    blob = synth.make_weights(cfg)
+    px = synth.make_pixels(cfg, grids)
+    log(f"inputs generated in {time.perf_counter() - t:.1f} s")
+
+    enc = vit.Encoder(cfg, blob)
+    enc.reserve(N)
+    d_px = torch.from_numpy(px).cuda()
+    out = torch.empty((M, cfg.out_hidden), dtype=torch.float32, device="cuda")
+    # prompt: a run of text rows, then each image span; IMAGE positions are the placeholders
+    types, src = vit.layout(grids)
+    text_rows = 64
+    R = text_rows + types.size
+    rows = np.full(M, -1, np.int32)
+    img_pos = np.nonzero(types == vit.TOK_IMAGE)[0]
+    rows[src[img_pos]] = text_rows + img_pos
+    embeds = torch.zeros((R, cfg.out_hidden), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        enc.encode(d_px, grids, out=out)
+        vit.layout(grids)
+        enc.overlay(embeds, rows, out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = elapsed / args.steps * 1e3
+    log(f"{args.steps} steps in {elapsed:.3f} s: {ms:.3f} ms/step")
+
+    fl = flops_per_pass(cfg, grids)
+    total_flops = sum(fl.values())
+    result = {
+        "metric": "visual tokens/s + % bf16 MFMA peak, 32-layer ViT on 1024-token image",
+        "value": M * args.steps / elapsed, "unit": "visual tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "images": len(grids),
+                   "grids": grids if len(grids) <= 4 else f"{len(grids)} seeded grids",
+                   "patches": N, "tokens": M, "layers": cfg.layers, "hidden": cfg.hidden,
+                   "heads": cfg.heads, "mlp": cfg.mlp, "out_hidden": cfg.out_hidden,
+                   "weights": "random N(0, 0.02) bf16", "pixels": "uniform u8"},
+        "images_per_s": len(grids) * args.steps / elapsed,
+        "tflops": total_flops / (ms * 1e-3) / 1e12,
+        "mfma_frac": total_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+    }
+
+    if not args.no_profile:
+        enc.timing(True)
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        tm = enc.timing_read()
+        enc.timing(False)
+        by = bytes_per_pass(cfg, grids, vit.vt_stride(grids))
+        kernels = {}
+        for k, (t_ms, n) in tm.items():
+            if n == 0:
+                continue
+            per_step = t_ms / args.steps
+            e = {"ms_per_step": per_step, "launches_per_step": n / args.steps,
+                 "avg_launch_us": t_ms / n * 1e3}
+            if k in fl:
+                e["tflops"] = fl[k] / (per_step * 1e-3) / 1e12
+                e["mfma_frac"] = e["tflops"] / PEAK_BF16_TFLOPS
+            if k in by:
+                e["gbs"] = by[k] / (per_step * 1e-3) / 1e9
+                e["hbm_frac"] = e["gbs"] / PEAK_HBM_GBS
+            kernels[k] = e
+        result["kernels"] = kernels
+        gemm_attn = ("qkv", "attention", "out_proj", "fc1", "fc2")
+        ga_ms = sum(kernels[k]["ms_per_step"] for k in gemm_attn if k in kernels)
+        result["gemm_attention_mfma_frac"] = (sum(fl[k] for k in gemm_attn) / (ga_ms * 1e-3) / 1e12
+                                              / PEAK_BF16_TFLOPS) if ga_ms else None
+        a = kernels.get("attention")
+        if a:
+            per_launch = fl["attention"] / (cfg.layers or 1)
+            achieved = per_launch / (a["avg_launch_us"] * 1e-6) / 1e12
+            result["roofline"] = {"kernel": "attention", "bound": "mfma", "achieved": achieved,
+                                  "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None}
+        log(json.dumps(kernels, indent=1))
+
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        result["cpu_baseline"] = cpu_baseline(cfg, blob, px, grids)
+    print(json.dumps(result), flush=True)
+    enc.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -146,6 +146,19 @@ vit_status vit_dump(vit_ctx *ctx, int32_t boundary, int32_t arg, const uint8_t *
                     const vit_grid *h_grids, int32_t n_images, void *d_dst, size_t dst_bytes,
                     void *stream);
 
+/* Per-step kernel timing, for profiling.  While enabled, vit_encode and vit_overlay record a
+ * HIP event pair around every kernel launch on the caller's stream (no synchronisation);
+ * vit_timing_read waits for the last recorded event, writes the summed milliseconds and the
+ * launch count of each step kind into ms[VIT_STEP_COUNT] / launches[VIT_STEP_COUNT] (either
+ * may be NULL) and starts a new accumulation.  Disabled by default. */
+enum {
+    VIT_STEP_PATCH_EMBED = 0, VIT_STEP_LAYERNORM = 1, VIT_STEP_QKV = 2, VIT_STEP_ROPE = 3,
+    VIT_STEP_ATTENTION = 4, VIT_STEP_OUT_PROJ = 5, VIT_STEP_FC1 = 6, VIT_STEP_FC2 = 7,
+    VIT_STEP_PROJECTOR = 8, VIT_STEP_OVERLAY = 9, VIT_STEP_COUNT = 10
+};
+vit_status vit_timing_enable(vit_ctx *ctx, int32_t enable);
+vit_status vit_timing_read(vit_ctx *ctx, float *ms, int64_t *launches);
+
 /* Text of the last error on ctx (or of the last failed vit_create on this thread when ctx
  * is NULL).  Never NULL; valid until the next call on the same ctx / thread. */
 const char *vit_last_error(const vit_ctx *ctx);

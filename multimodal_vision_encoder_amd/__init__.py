@@ -24,7 +24,9 @@ ACT_NONE, ACT_GELU_TANH = 0, 1
 EXPORTS = ("vit_blob_elems", "vit_create", "vit_destroy", "vit_reserve", "vit_num_tokens",
            "vit_num_patches", "vit_encode", "vit_layout", "vit_overlay", "vit_dump",
            "vit_last_error", "vit_op_linear", "vit_op_layernorm", "vit_vt_stride", "vit_op_rope",
-           "vit_op_attention", "vit_op_merge_project")
+           "vit_op_attention", "vit_op_merge_project", "vit_timing_enable", "vit_timing_read")
+STEP_NAMES = ("patch_embed", "layernorm", "qkv", "rope", "attention", "out_proj", "fc1", "fc2",
+              "projector", "overlay")
 
 
 class VitError(RuntimeError):
@@ -80,6 +82,8 @@ def lib():
             "vit_op_rope": (i32, [vp, vp, vp, P(Grid), i32, vp]),
             "vit_op_attention": (i32, [vp, vp, vp, P(Grid), i32, vp, vp]),
             "vit_op_merge_project": (i32, [vp, vp, P(Grid), i32, vp, vp]),
+            "vit_timing_enable": (i32, [vp, i32]),
+            "vit_timing_read": (i32, [vp, vp, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -182,6 +186,16 @@ class Encoder:
 
     def reserve(self, max_patches: int):
         self._check(lib().vit_reserve(self._ctx, int(max_patches)))
+
+    def timing(self, enable: bool):
+        self._check(lib().vit_timing_enable(self._ctx, 1 if enable else 0))
+
+    def timing_read(self):
+        """{step: (total ms, launches)} since the last read (waits for the recorded events)."""
+        ms = np.zeros(len(STEP_NAMES), np.float32)
+        n = np.zeros(len(STEP_NAMES), np.int64)
+        self._check(lib().vit_timing_read(self._ctx, ms.ctypes.data, n.ctypes.data))
+        return {k: (float(ms[i]), int(n[i])) for i, k in enumerate(STEP_NAMES)}
 
     # ---- the encoder -----------------------------------------------------------------
     def encode(self, pixels, grids, out=None, stream=None):

@@ -24,8 +24,11 @@ __device__ __forceinline__ int xcd_remap(int bid, int nb)
     return (bid & 7) * per + (bid >> 3);
 }
 
+// GELU, tanh form, evaluated term by term with each product and sum rounded (no fused
+// multiply-add), as written: 0.5 u (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3))).
 __device__ __forceinline__ float gelu_tanh(float u)
 {
+#pragma clang fp contract(off)
     const float k0 = 0.7978845608028654f, k1 = 0.044715f;
     float inner = __fmul_rn(k0, __fadd_rn(u, __fmul_rn(__fmul_rn(__fmul_rn(k1, u), u), u)));
     return __fmul_rn(__fmul_rn(0.5f, u), __fadd_rn(1.0f, tanhf(inner)));

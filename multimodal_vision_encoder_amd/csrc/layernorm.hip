@@ -101,6 +101,7 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const bf16_t *__restrict
     float y[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
+#pragma clang fp contract(off)
         const int c = col_of<EPL>(lane, e);
         y[e] = __fadd_rn(__fmul_rn(__fdiv_rn(v[e] - mu, den), bf16_to_f32(g[c])), bf16_to_f32(b[c]));
     }

@@ -4,7 +4,8 @@
 // [Z] "Step 3": the angle vector of patch (h, w) is blocked by axis,
 // theta = [h f_0 .. h f_{Q-1}, w f_0 .. w f_{Q-1}] with Q = hd/4 (not interleaved), and the
 // half-vector rotation pairs element i with i + hd/2.  [G] V4 Flash vision row: positions
-// are the raw patch grid.  cos/sin come from tables [position][j] built on the host.
+// are the raw patch grid.  cos/sin come from tables [position][j] built on the host.  The
+// rotation is evaluated as two products and one sum, each rounded (no fused multiply-add).
 //
 // One block per (64-row tile of one image, head).  The v tile goes through LDS and is
 // written as vt[head][d][column] so that the attention kernel can stage V^T with 16-byte
@@ -13,6 +14,14 @@
 #include "kernels.h"
 
 namespace {
+
+// (a, b) turned by the angle with cosine c and sine s; products and sums rounded separately.
+__device__ __forceinline__ void rotate(float a, float b, float c, float s, float &na, float &nb)
+{
+#pragma clang fp contract(off)
+    na = a * c - b * s;
+    nb = b * c + a * s;
+}
 
 template <int HD>
 __global__ __launch_bounds__(256) void rope_kernel(bf16_t *__restrict__ qkv, bf16_t *__restrict__ vt,
@@ -41,9 +50,10 @@ __global__ __launch_bounds__(256) void rope_kernel(bf16_t *__restrict__ qkv, bf1
         const int pos = i < Q4 ? hp : wp;
         const float c = cos_t[pos * Q4 + j], s = sin_t[pos * Q4 + j];
         bf16_t *v = base + (int64_t)lr * ld + part * D;
-        const float a = bf16_to_f32(v[i]), b = bf16_to_f32(v[i + HALF]);
-        v[i] = f32_to_bf16(__fsub_rn(__fmul_rn(a, c), __fmul_rn(b, s)));
-        v[i + HALF] = f32_to_bf16(__fadd_rn(__fmul_rn(b, c), __fmul_rn(a, s)));
+        float na, nb;
+        rotate(bf16_to_f32(v[i]), bf16_to_f32(v[i + HALF]), c, s, na, nb);
+        v[i] = f32_to_bf16(na);
+        v[i + HALF] = f32_to_bf16(nb);
     }
 
     // v: tile -> LDS -> transposed store

@@ -54,6 +54,12 @@ struct vit_ctx {
     hipEvent_t stage_ev = nullptr;
     bool stage_pending = false;
 
+    // optional per-step timing (event pairs recorded around launches)
+    bool timing = false;
+    std::vector<hipEvent_t> ev_pool;
+    size_t ev_next = 0;
+    std::vector<std::pair<int, size_t>> ev_marks;   // (step kind, index of the start event)
+
     std::string err;
 };
 
@@ -256,6 +262,37 @@ vit_status stage_plan(vit_ctx *c, const Plan &p, hipStream_t s, DevPlan &dp)
                                                hipGetErrorString(e_));                        \
     } while (0)
 
+// Record the start event of a timed launch; returns the pool index or -1 when not timing.
+long timing_start(vit_ctx *c, hipStream_t s)
+{
+    if (!c->timing) return -1;
+    if (c->ev_next + 2 > c->ev_pool.size()) {
+        for (int i = 0; i < 256; ++i) {
+            hipEvent_t e;
+            if (hipEventCreate(&e) != hipSuccess) return -1;
+            c->ev_pool.push_back(e);
+        }
+    }
+    const size_t i = c->ev_next;
+    if (hipEventRecord(c->ev_pool[i], s) != hipSuccess) return -1;
+    c->ev_next += 2;
+    return (long)i;
+}
+
+void timing_stop(vit_ctx *c, hipStream_t s, int kind, long i)
+{
+    if (i < 0) return;
+    if (hipEventRecord(c->ev_pool[i + 1], s) == hipSuccess) c->ev_marks.push_back({kind, (size_t)i});
+}
+
+// LAUNCH with an event pair around it when timing is enabled.
+#define TLAUNCH(ctx, kind, s, expr)                                                           \
+    do {                                                                                      \
+        const long t_ = timing_start(ctx, s);                                                 \
+        LAUNCH(ctx, expr);                                                                    \
+        timing_stop(ctx, s, kind, t_);                                                        \
+    } while (0)
+
 constexpr int kStopNone = -1;
 
 // One encoder pass; with stop >= 0 it ends at that debug boundary and copies the tensor.
@@ -301,26 +338,26 @@ vit_status encode_impl(vit_ctx *c, const uint8_t *px, const vit_grid *grids, int
         LAUNCH(c, launch_dump_patches(px, dp.imgs, ni, p.N, c->s3, c->t3, c->ps, (bf16_t *)dst, s));
         return VIT_OK;
     }
-    LAUNCH(c, launch_patch_embed(px, dp.imgs, ni, p.N, c->s3, c->t3, c->ps, c->d_wpe, c->Kp,
+    TLAUNCH(c, VIT_STEP_PATCH_EMBED, s, launch_patch_embed(px, dp.imgs, ni, p.N, c->s3, c->t3, c->ps, c->d_wpe, c->Kp,
                                  c->pe_b, D, c->x, s));
     if (stop == VIT_DUMP_EMBED) return copy_out(c->x);
 
     for (int l = 0; l < L; ++l) {
         const Layer &w = c->layers[l];
-        LAUNCH(c, launch_layernorm(c->x, l ? c->delta : nullptr, c->x, p.N, D, w.ln1g, w.ln1b,
+        TLAUNCH(c, VIT_STEP_LAYERNORM, s, launch_layernorm(c->x, l ? c->delta : nullptr, c->x, p.N, D, w.ln1g, w.ln1b,
                                    c->cfg.ln_eps, c->ln, s));
-        LAUNCH(c, launch_linear(c->ln, p.N, D, w.wqkv, w.bqkv, 3 * D, ACT_NONE, false, c->qkv, s));
-        LAUNCH(c, launch_rope(c->qkv, c->vt, p.vt_cols, dp.rope, (int)p.rope.size(), dp.imgs, D, H,
+        TLAUNCH(c, VIT_STEP_QKV, s, launch_linear(c->ln, p.N, D, w.wqkv, w.bqkv, 3 * D, ACT_NONE, false, c->qkv, s));
+        TLAUNCH(c, VIT_STEP_ROPE, s, launch_rope(c->qkv, c->vt, p.vt_cols, dp.rope, (int)p.rope.size(), dp.imgs, D, H,
                               c->d_cos, c->d_sin, s));
         if (stop == VIT_DUMP_QKV && arg == l) return copy_out(c->qkv);
-        LAUNCH(c, launch_attention(c->qkv, c->vt, p.vt_cols, c->o, dp.attn, (int)p.attn.size(),
+        TLAUNCH(c, VIT_STEP_ATTENTION, s, launch_attention(c->qkv, c->vt, p.vt_cols, c->o, dp.attn, (int)p.attn.size(),
                                    dp.imgs, D, H, s));
         if (stop == VIT_DUMP_ATTN && arg == l) return copy_out(c->o);
-        LAUNCH(c, launch_linear(c->o, p.N, D, w.wo, w.bo, D, ACT_NONE, false, c->delta, s));
-        LAUNCH(c, launch_layernorm(c->x, c->delta, c->x, p.N, D, w.ln2g, w.ln2b, c->cfg.ln_eps,
+        TLAUNCH(c, VIT_STEP_OUT_PROJ, s, launch_linear(c->o, p.N, D, w.wo, w.bo, D, ACT_NONE, false, c->delta, s));
+        TLAUNCH(c, VIT_STEP_LAYERNORM, s, launch_layernorm(c->x, c->delta, c->x, p.N, D, w.ln2g, w.ln2b, c->cfg.ln_eps,
                                    c->ln, s));
-        LAUNCH(c, launch_linear(c->ln, p.N, D, w.w1, w.b1, c->F, ACT_GELU_TANH, false, c->h1, s));
-        LAUNCH(c, launch_linear(c->h1, p.N, c->F, w.w2, w.b2, D, ACT_NONE, false, c->delta, s));
+        TLAUNCH(c, VIT_STEP_FC1, s, launch_linear(c->ln, p.N, D, w.w1, w.b1, c->F, ACT_GELU_TANH, false, c->h1, s));
+        TLAUNCH(c, VIT_STEP_FC2, s, launch_linear(c->h1, p.N, c->F, w.w2, w.b2, D, ACT_NONE, false, c->delta, s));
         if (stop == VIT_DUMP_LAYER && arg == l) {
             // the residual add is fused into the next LayerNorm; run it to materialise x
             LAUNCH(c, launch_layernorm(c->x, c->delta, c->x, p.N, D, c->lnf_g, c->lnf_b,
@@ -328,14 +365,14 @@ vit_status encode_impl(vit_ctx *c, const uint8_t *px, const vit_grid *grids, int
             return copy_out(c->x);
         }
     }
-    LAUNCH(c, launch_layernorm(c->x, L ? c->delta : nullptr, c->x, p.N, D, c->lnf_g, c->lnf_b,
+    TLAUNCH(c, VIT_STEP_LAYERNORM, s, launch_layernorm(c->x, L ? c->delta : nullptr, c->x, p.N, D, c->lnf_g, c->lnf_b,
                                c->cfg.ln_eps, c->ln, s));
     if (stop == VIT_DUMP_FINAL_NORM) return copy_out(c->ln);
     if (stop == VIT_DUMP_MERGED) {
         LAUNCH(c, launch_dump_merged(c->ln, dp.imgs, ni, p.M, D, (bf16_t *)dst, s));
         return VIT_OK;
     }
-    LAUNCH(c, launch_merge_project(c->ln, dp.imgs, ni, p.M, D, c->d_wproj, c->proj_b, c->Dl, out, s));
+    TLAUNCH(c, VIT_STEP_PROJECTOR, s, launch_merge_project(c->ln, dp.imgs, ni, p.M, D, c->d_wproj, c->proj_b, c->Dl, out, s));
     return VIT_OK;
 }
 
@@ -349,6 +386,7 @@ void destroy(vit_ctx *c)
         if (b) (void)hipFree(b);
     if (c->h_stage) (void)hipHostFree(c->h_stage);
     if (c->stage_ev) (void)hipEventDestroy(c->stage_ev);
+    for (hipEvent_t e : c->ev_pool) (void)hipEventDestroy(e);
     delete c;
 }
 
@@ -595,8 +633,36 @@ vit_status vit_overlay(vit_ctx *ctx, uint16_t *d_embeds, int64_t n_embed_rows,
     vit_status st = upload_meta(ctx, {{h_rows, (size_t)n_rows * sizeof(int32_t)}},
                                 (hipStream_t)stream, off);
     if (st != VIT_OK) return st;
-    LAUNCH(ctx, launch_overlay(d_embeds, d_rows, (const int32_t *)(ctx->d_meta + off[0]), n_rows,
+    TLAUNCH(ctx, VIT_STEP_OVERLAY, (hipStream_t)stream, launch_overlay(d_embeds, d_rows, (const int32_t *)(ctx->d_meta + off[0]), n_rows,
                                hidden, (hipStream_t)stream));
+    return VIT_OK;
+}
+
+vit_status vit_timing_enable(vit_ctx *ctx, int32_t enable)
+{
+    if (!ctx) return fail(nullptr, VIT_E_ARG, "ctx is NULL");
+    ctx->timing = enable != 0;
+    return VIT_OK;
+}
+
+vit_status vit_timing_read(vit_ctx *ctx, float *ms, int64_t *launches)
+{
+    if (!ctx) return fail(nullptr, VIT_E_ARG, "ctx is NULL");
+    if (ms)
+        for (int k = 0; k < VIT_STEP_COUNT; ++k) ms[k] = 0.f;
+    if (launches)
+        for (int k = 0; k < VIT_STEP_COUNT; ++k) launches[k] = 0;
+    if (!ctx->ev_marks.empty()) {
+        HIP_TRY(ctx, hipEventSynchronize(ctx->ev_pool[ctx->ev_marks.back().second + 1]));
+        for (auto &m : ctx->ev_marks) {
+            float t = 0.f;
+            HIP_TRY(ctx, hipEventElapsedTime(&t, ctx->ev_pool[m.second], ctx->ev_pool[m.second + 1]));
+            if (ms) ms[m.first] += t;
+            if (launches) launches[m.first] += 1;
+        }
+    }
+    ctx->ev_marks.clear();
+    ctx->ev_next = 0;
     return VIT_OK;
 }
 

@@ -30,6 +30,13 @@ def f32(bits):
     return synth.bf16_bits_to_f32(bits)
 
 
+def sum_bound(A, W):
+    """Absolute slack for fp32 sums taken in another order: 2^-18 * sum_k |a_k w_k| per
+    output (about sqrt(K) ulps of the largest partial sum, far below one bf16 ulp of a
+    typical output, but it covers outputs that cancel to near zero)."""
+    return 2.0 ** -18 * (np.abs(f32(A)).astype(np.float64) @ np.abs(f32(W)).astype(np.float64).T)
+
+
 # ------------------------------------------------------------------------------------------
 # linear layers (QKV, out-proj, fc1 + GELU, fc2, projector epilogue)
 # ------------------------------------------------------------------------------------------
@@ -51,7 +58,7 @@ def test_linear_small(M, K, N, act, out_f32):
     if out_f32:
         np.testing.assert_allclose(got.cpu().numpy(), want, rtol=1e-5, atol=1e-5)
     else:
-        assert_bf16_close(from_dev_bf16(got), want, what="linear")
+        assert_bf16_close(from_dev_bf16(got), want, atol=sum_bound(A, W), what="linear")
 
 
 def test_linear_one_hot_is_exact():
@@ -84,7 +91,7 @@ def test_linear_full_size_sampled(N, K, act):
     torch.cuda.synchronize()
     rows = np.r_[0:3, 127:130, 4000:4003, M - 5:M]
     want = oracle.linear(f32(A[rows]), f32(W), f32(b), act=act)
-    assert_bf16_close(got[rows], want, what="linear full size")
+    assert_bf16_close(got[rows], want, atol=sum_bound(A[rows], W), what="linear full size")
 
 
 # ------------------------------------------------------------------------------------------

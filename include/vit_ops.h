@@ -44,8 +44,10 @@ int64_t vit_vt_stride(const vit_grid *h_grids, int32_t n_images);
 
 /* 2D RoPE on q and k ([Z] "Step 3": height/width-blocked angles, half-vector rotation;
  * [G] V4: raw patch grid) in place inside d_qkv = bf16 [N][3D] (q | k | v, head-major),
- * and v copied transposed to d_vt = bf16 [H][hd][vit_vt_stride(grids)] for the attention
- * (the columns of each image past its last patch are written as zeros).
+ * and v copied transposed to d_vt = bf16 [H][hd][vit_vt_stride(grids)] for the attention:
+ * image i owns the columns from its 64-aligned offset; inside every group of 16 columns,
+ * column p holds key (p with bits 2 and 3 swapped); columns past the image's last patch are
+ * written as zeros.
  * Patch n of an image sits at (n / gw, n % gw) of that image's grid. */
 vit_status vit_op_rope(vit_ctx *ctx, uint16_t *d_qkv, uint16_t *d_vt, const vit_grid *h_grids,
                        int32_t n_images, void *stream);

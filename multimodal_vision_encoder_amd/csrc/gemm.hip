@@ -1,4 +1,6 @@
-// bf16 "NT" GEMM on gfx950 MFMA:  C[m][n] = epilogue(sum_k A[m][k] W[n][k]).
+// bf16 "NT" GEMM on gfx950 MFMA with a computing A loader:  C[m][n] = sum_k A[m][k] W[n][k] + b.
+// Used for the patch projection, whose A operand (patchify + normalisation) is computed
+// rather than copied; the plain linear layers and the projector use gemm_big.hip.
 //
 // Block tile BM x BN x 64, 256 threads as 2 x 2 waves; each wave owns a (BM/2) x (BN/2)
 // sub-tile built from v_mfma_f32_32x32x16_bf16 blocks.  A and W tiles are staged through
@@ -6,8 +8,7 @@
 // K-tile t+1 are in flight while the MFMAs of tile t run.  The MFMA is issued with the W
 // fragment as its first operand so that each lane ends up holding 4 consecutive output
 // columns of one row, which the epilogue stores as one 8- or 16-byte write.
-// The A operand comes from a loader (plain rows, patchify gather, merge gather), so the
-// patch projection and the projector share this kernel with the block's linear layers.
+// The A operand comes from a loader (here the patchify gather of loaders.h).
 #include "kernels.h"
 #include "loaders.h"
 
@@ -208,26 +209,12 @@ hipError_t dispatch_epilogue(AL al, const bf16_t *W, int64_t M, int N, int K, co
 
 }  // namespace
 
-hipError_t launch_linear(const bf16_t *A, int64_t M, int K, const bf16_t *W, const bf16_t *bias,
-                         int N, int act, bool out_f32, void *out, hipStream_t s)
-{
-    return dispatch_epilogue(LoadPlain{A, K, M}, W, M, N, K, bias, act, out_f32, out, s);
-}
-
 hipError_t launch_patch_embed(const uint8_t *px, const ImgDesc *imgs, int n_img, int64_t M,
                               const float *s3, const float *t3, int ps, const bf16_t *Wpe,
                               int Kp, const bf16_t *bias, int D, bf16_t *out, hipStream_t s)
 {
     LoadPatch al{px, imgs, n_img, M, ps, 3 * ps * ps, s3[0], s3[1], s3[2], t3[0], t3[1], t3[2]};
     return dispatch_epilogue(al, Wpe, M, D, Kp, bias, ACT_NONE, false, out, s);
-}
-
-hipError_t launch_merge_project(const bf16_t *y, const ImgDesc *imgs, int n_img, int64_t Mtok,
-                                int D, const bf16_t *Wp, const bf16_t *bias, int Dl, float *out,
-                                hipStream_t s)
-{
-    LoadMerge al{y, imgs, n_img, Mtok, D};
-    return dispatch_epilogue(al, Wp, Mtok, Dl, 9 * D, bias, ACT_NONE, true, out, s);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -248,12 +235,13 @@ __global__ __launch_bounds__(256) void dump_patches_kernel(LoadPatch al, bf16_t 
     }
 }
 
-__global__ __launch_bounds__(256) void dump_merged_kernel(LoadMerge al, bf16_t *out)
+__global__ __launch_bounds__(256) void dump_merged_kernel(SrcMerge src, bf16_t *out)
 {
     const int64_t row = blockIdx.x;
-    const int D = al.D, K = 9 * D;
+    const int D = src.D, K = 9 * D;
+    const SrcMerge::Row rw = src.row(row);
     for (int k = threadIdx.x * 8; k < K; k += 256 * 8) {
-        const uint4 v = al(row, k);
+        const uint4 v = *reinterpret_cast<const uint4 *>(src.addr(rw, k));
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
         const int pos = k / D, c = k - pos * D;
 #pragma unroll
@@ -276,10 +264,10 @@ hipError_t launch_dump_patches(const uint8_t *px, const ImgDesc *imgs, int n_img
 }
 
 hipError_t launch_dump_merged(const bf16_t *y, const ImgDesc *imgs, int n_img, int64_t Mtok,
-                              int D, bf16_t *out, hipStream_t s)
+                              int D, bf16_t *out, const bf16_t *zero, hipStream_t s)
 {
     if (Mtok <= 0) return hipSuccess;
-    LoadMerge al{y, imgs, n_img, Mtok, D};
-    hipLaunchKernelGGL(dump_merged_kernel, dim3((unsigned)Mtok), dim3(256), 0, s, al, out);
+    SrcMerge src{y, imgs, n_img, Mtok, D, zero};
+    hipLaunchKernelGGL(dump_merged_kernel, dim3((unsigned)Mtok), dim3(256), 0, s, src, out);
     return hipGetLastError();
 }

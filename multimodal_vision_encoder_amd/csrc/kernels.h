@@ -16,10 +16,11 @@ hipError_t launch_patch_embed(const uint8_t *px, const ImgDesc *imgs, int n_img,
                               const float *s3, const float *t3, int ps, const bf16_t *Wpe,
                               int Kp, const bf16_t *bias, int D, bf16_t *out, hipStream_t s);
 
-// 3x3 merge gather + projector: out fp32 [Mtok][Dl]; Wp position-major [Dl][9D].
+// 3x3 merge gather + projector: out fp32 [Mtok][Dl]; Wp position-major [Dl][9D]; `zero`
+// points at >= 16 zero bytes (read for positions in the right/bottom padding).
 hipError_t launch_merge_project(const bf16_t *y, const ImgDesc *imgs, int n_img, int64_t Mtok,
                                 int D, const bf16_t *Wp, const bf16_t *bias, int Dl, float *out,
-                                hipStream_t s);
+                                const bf16_t *zero, hipStream_t s);
 
 // Optional residual add + LayerNorm (rows of width D).
 hipError_t launch_layernorm(const bf16_t *x, const bf16_t *delta, bf16_t *xout, int64_t M, int D,
@@ -31,7 +32,7 @@ hipError_t launch_rope(bf16_t *qkv, bf16_t *vt, int64_t ldv, const RowTile *tile
                        const ImgDesc *imgs, int D, int H, const float *cos_t,
                        const float *sin_t, hipStream_t s);
 
-// Block-diagonal flash attention; one block per (128-query tile, head).
+// Block-diagonal flash attention; one block per (attention_q_tile() queries, head).
 hipError_t launch_attention(const bf16_t *qkv, const bf16_t *vt, int64_t ldv, bf16_t *o,
                             const RowTile *work, int n_work, const ImgDesc *imgs, int D, int H,
                             hipStream_t s);
@@ -45,8 +46,8 @@ hipError_t launch_dump_patches(const uint8_t *px, const ImgDesc *imgs, int n_img
                                const float *s3, const float *t3, int ps, bf16_t *out,
                                hipStream_t s);
 hipError_t launch_dump_merged(const bf16_t *y, const ImgDesc *imgs, int n_img, int64_t Mtok,
-                              int D, bf16_t *out, hipStream_t s);
+                              int D, bf16_t *out, const bf16_t *zero, hipStream_t s);
 
-// Rows of a query tile / RoPE tile.
-constexpr int kAttnQTile = 128;
+// Rows of an attention query tile (one block) and of a RoPE tile.
+int attention_q_tile();
 constexpr int kRopeTile = 64;

@@ -1,21 +1,8 @@
-// A-operand loaders of the bf16 GEMM.  Each returns 8 consecutive K elements (16 bytes) of
-// one row of the virtual A matrix; rows at or beyond M read as zeros.  The same functions
-// feed the debug dumps, so a dumped tensor is exactly what the GEMM consumed.
+// A-operand sources of the bf16 GEMMs.  The same functions feed the debug dumps, so a dumped
+// tensor is exactly what the GEMM consumed.
 #pragma once
 
 #include "common.h"
-
-// Plain row-major bf16 activations [M][lda].
-struct LoadPlain {
-    const bf16_t *A;
-    int64_t lda;
-    int64_t M;
-    __device__ __forceinline__ uint4 operator()(int64_t row, int k) const
-    {
-        if (row >= M) return make_uint4(0, 0, 0, 0);
-        return *reinterpret_cast<const uint4 *>(A + row * lda + k);
-    }
-};
 
 // Patchify fused into the patch projection ([Z] "Step 1": rows in (grid_y, grid_x) order,
 // columns in (channel, y, x) order; pixels normalised as fmaf(u8, s_c, t_c), rounded to bf16;
@@ -60,26 +47,43 @@ struct LoadPatch {
     }
 };
 
-// 3x3 merge gather fused into the projector ([Z] "Step 4").  The projector weight is stored
-// position-major (column pos*D + c holds the original column c*9 + pos), so a K chunk is 8
-// consecutive channels of one source patch row of the final-norm output `y` [N][D];
-// positions in the right/bottom padding read as zero.
-struct LoadMerge {
+// ---------------------------------------------------------------------------------------
+// Address sources for the direct-to-LDS GEMM: per row a small state, per K chunk the address
+// of 16 bytes (8 bf16) to copy.  Rows past M are clamped to M-1 (their outputs are never
+// stored).
+// ---------------------------------------------------------------------------------------
+// Plain activations [M][lda]: one base pointer per row.
+struct SrcPlain {
+    const bf16_t *A;
+    int64_t lda, M;
+    struct Row { const bf16_t *p; };
+    __device__ __forceinline__ Row row(int64_t r) const { return Row{A + (r < M ? r : M - 1) * lda}; }
+    __device__ __forceinline__ const bf16_t *addr(const Row &rw, int k) const { return rw.p + k; }
+};
+
+// 3x3 merge gather of the projector ([Z] "Step 4"): row = merged token (my, mx) of its image,
+// K index = pos * D + c with pos = dy*3 + dx (position-major projector weight); positions in
+// the right/bottom padding read 16 zero bytes from `zero`.
+struct SrcMerge {
     const bf16_t *y;
     const ImgDesc *imgs;
     int n_img;
-    int64_t M;           // merged tokens in the batch
+    int64_t M;
     int D;
-
-    __device__ __forceinline__ uint4 operator()(int64_t row, int k) const
+    const bf16_t *zero;   // at least 16 zero bytes
+    struct Row { const bf16_t *base; int gh, gw, y0, x0; };
+    __device__ __forceinline__ Row row(int64_t r) const
     {
-        if (row >= M) return make_uint4(0, 0, 0, 0);
-        const ImgDesc &d = imgs[image_of_token(imgs, n_img, row)];
-        const int local = (int)(row - d.tok_off);
-        const int my = local / d.mw, mx = local - my * d.mw;
+        if (r >= M) r = M - 1;
+        const ImgDesc &d = imgs[image_of_token(imgs, n_img, r)];
+        const int local = (int)(r - d.tok_off), my = local / d.mw, mx = local - my * d.mw;
+        return Row{y + (int64_t)d.patch_off * D, d.gh, d.gw, 3 * my, 3 * mx};
+    }
+    __device__ __forceinline__ const bf16_t *addr(const Row &rw, int k) const
+    {
         const int pos = k / D, c = k - pos * D;
-        const int src = merge_source(d, my, mx, pos);
-        if (src < 0) return make_uint4(0, 0, 0, 0);
-        return *reinterpret_cast<const uint4 *>(y + ((int64_t)d.patch_off + src) * D + c);
+        const int sy = rw.y0 + pos / 3, sx = rw.x0 + pos % 3;
+        return (sy < rw.gh && sx < rw.gw) ? rw.base + ((int64_t)sy * rw.gw + sx) * D + c : zero;
     }
 };
+

@@ -9,8 +9,9 @@
 //
 // One block per (64-row tile of one image, head).  The v tile goes through LDS and is
 // written as vt[head][d][column] so that the attention kernel can stage V^T with 16-byte
-// loads; columns of the tile past the image's last patch are written as zeros, so every
-// column the attention kernel reads is defined.  HBM-bound.
+// loads; inside each group of 16 columns, column p holds key p with bits 2 and 3 swapped.
+// Columns of the tile past the image's last patch are written as zeros, so every column
+// the attention kernel reads is defined.  HBM-bound.
 #include "kernels.h"
 
 namespace {
@@ -63,9 +64,12 @@ __global__ __launch_bounds__(256) void rope_kernel(bf16_t *__restrict__ qkv, bf1
         sv[dd][r] = lr < d.n ? base[(int64_t)lr * ld + 2 * D + dd] : (bf16_t)0;
     }
     __syncthreads();
+    // column p of each 16-column group holds key p with bits 2 and 3 swapped (an involution),
+    // the order in which the attention kernel's P.V operand wants 8 keys per lane
     for (int w = threadIdx.x; w < HD * T; w += 256) {
-        const int dd = w / T, r = w - dd * T;
-        vt[((int64_t)head * HD + dd) * ldv + d.vt_off + tile.r0 + r] = sv[dd][r];
+        const int dd = w / T, p = w - dd * T;
+        const int key = (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1);
+        vt[((int64_t)head * HD + dd) * ldv + d.vt_off + tile.r0 + p] = sv[dd][key];
     }
 }
 

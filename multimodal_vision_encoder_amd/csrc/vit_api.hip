@@ -39,6 +39,7 @@ struct vit_ctx {
     float s3[3] = {0, 0, 0}, t3[3] = {0, 0, 0};
 
     bf16_t *d_blob = nullptr, *d_wpe = nullptr, *d_wproj = nullptr;
+    bf16_t *d_zero = nullptr;   // 256 zero bytes: the padding source of the merge gather
     const bf16_t *pe_b = nullptr, *lnf_g = nullptr, *lnf_b = nullptr, *proj_b = nullptr;
     std::vector<Layer> layers;
     float *d_cos = nullptr, *d_sin = nullptr;
@@ -152,8 +153,9 @@ vit_status make_plan(vit_ctx *ctx, const vit_grid *grids, int n, Plan &p)
     for (int i = 0; i < n; ++i) order[i] = i;
     std::stable_sort(order.begin(), order.end(),
                      [&](int a, int b) { return p.imgs[a].n > p.imgs[b].n; });
+    const int qt = attention_q_tile();
     for (int i : order)
-        for (int r = 0; r < p.imgs[i].n; r += kAttnQTile) p.attn.push_back(RowTile{i, r});
+        for (int r = 0; r < p.imgs[i].n; r += qt) p.attn.push_back(RowTile{i, r});
     for (int i = 0; i < n; ++i)
         for (int r = 0; r < p.imgs[i].n; r += kRopeTile) p.rope.push_back(RowTile{i, r});
     return VIT_OK;
@@ -369,10 +371,10 @@ vit_status encode_impl(vit_ctx *c, const uint8_t *px, const vit_grid *grids, int
                                c->cfg.ln_eps, c->ln, s));
     if (stop == VIT_DUMP_FINAL_NORM) return copy_out(c->ln);
     if (stop == VIT_DUMP_MERGED) {
-        LAUNCH(c, launch_dump_merged(c->ln, dp.imgs, ni, p.M, D, (bf16_t *)dst, s));
+        LAUNCH(c, launch_dump_merged(c->ln, dp.imgs, ni, p.M, D, (bf16_t *)dst, c->d_zero, s));
         return VIT_OK;
     }
-    TLAUNCH(c, VIT_STEP_PROJECTOR, s, launch_merge_project(c->ln, dp.imgs, ni, p.M, D, c->d_wproj, c->proj_b, c->Dl, out, s));
+    TLAUNCH(c, VIT_STEP_PROJECTOR, s, launch_merge_project(c->ln, dp.imgs, ni, p.M, D, c->d_wproj, c->proj_b, c->Dl, out, c->d_zero, s));
     return VIT_OK;
 }
 
@@ -381,7 +383,7 @@ void destroy(vit_ctx *c)
     if (!c) return;
     (void)hipDeviceSynchronize();
     free_workspace(c);
-    void *bufs[] = {c->d_blob, c->d_wpe, c->d_wproj, c->d_cos, c->d_sin, c->d_meta};
+    void *bufs[] = {c->d_blob, c->d_wpe, c->d_wproj, c->d_cos, c->d_sin, c->d_meta, c->d_zero};
     for (void *b : bufs)
         if (b) (void)hipFree(b);
     if (c->h_stage) (void)hipHostFree(c->h_stage);
@@ -448,6 +450,8 @@ vit_status vit_create(const vit_weights *w, vit_ctx **out)
 
     CREATE_HIP(hipGetDevice(&c->device));
     CREATE_HIP(hipEventCreateWithFlags(&c->stage_ev, hipEventDisableTiming));
+    CREATE_HIP(hipMalloc((void **)&c->d_zero, 256));
+    CREATE_HIP(hipMemset(c->d_zero, 0, 256));
     CREATE_HIP(hipMalloc((void **)&c->d_blob, want * sizeof(bf16_t)));
     CREATE_HIP(hipMemcpy(c->d_blob, w->blob, want * sizeof(bf16_t), hipMemcpyHostToDevice));
 
@@ -751,7 +755,7 @@ vit_status vit_op_merge_project(vit_ctx *ctx, const uint16_t *d_y, const vit_gri
     DevPlan dp{};
     if ((st = stage_plan(ctx, p, (hipStream_t)stream, dp)) != VIT_OK) return st;
     LAUNCH(ctx, launch_merge_project(d_y, dp.imgs, (int)p.imgs.size(), p.M, ctx->D, ctx->d_wproj,
-                                     ctx->proj_b, ctx->Dl, d_out, (hipStream_t)stream));
+                                     ctx->proj_b, ctx->Dl, d_out, ctx->d_zero, (hipStream_t)stream));
     return VIT_OK;
 }
 

@@ -147,16 +147,19 @@ def test_rope_exact(name, grids):
     want = _oracle_rope(f32(qkv), grids, cfg)
     got = from_dev_bf16(d)
     assert np.array_equal(got, want)
-    # v transposed per head, each image at its own 64-aligned column block, zero padding
+    # v transposed per head, each image at its own 64-aligned column block, zero padding;
+    # inside each 16-column group, column p holds key p with bits 2 and 3 swapped
     vtn = from_dev_bf16(vt)
     H, hd = cfg.heads, cfg.head_dim
     off = col = 0
     for gh, gw in grids:
         n = gh * gw
-        v = f32(qkv[off:off + n, 2 * cfg.hidden:]).reshape(n, H, hd).transpose(1, 2, 0)
-        assert np.array_equal(vtn[:, :, col:col + n], v)
         pad = -(-n // 64) * 64
-        assert not vtn[:, :, col + n:col + pad].any()
+        v = np.zeros((H, hd, pad), np.float32)
+        v[:, :, :n] = f32(qkv[off:off + n, 2 * cfg.hidden:]).reshape(n, H, hd).transpose(1, 2, 0)
+        p = np.arange(pad)
+        key = (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1)
+        assert np.array_equal(vtn[:, :, col:col + pad], v[:, :, key])
         off += n
         col += pad
 

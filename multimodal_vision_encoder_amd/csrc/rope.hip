@@ -7,11 +7,12 @@
 // are the raw patch grid.  cos/sin come from tables [position][j] built on the host.  The
 // rotation is evaluated as two products and one sum, each rounded (no fused multiply-add).
 //
-// One block per (64-row tile of one image, head).  The v tile goes through LDS and is
-// written as vt[head][d][column] so that the attention kernel can stage V^T with 16-byte
-// loads; inside each group of 16 columns, column p holds key p with bits 2 and 3 swapped.
-// Columns of the tile past the image's last patch are written as zeros, so every column
-// the attention kernel reads is defined.  HBM-bound.
+// One block per (64-row tile of one image, head).  q and k move as 16-byte chunks (8
+// elements of the first half with the matching 8 of the second half).  The v tile goes
+// through LDS and is written as vt[head][d][column] with 16-byte stores, so the attention
+// kernel can stage V^T with 16-byte loads; inside each group of 16 columns, column p holds
+// key p with bits 2 and 3 swapped.  Columns of the tile past the image's last patch are
+// written as zeros, so every column the attention kernel reads is defined.  HBM-bound.
 #include "kernels.h"
 
 namespace {
@@ -24,6 +25,25 @@ __device__ __forceinline__ void rotate(float a, float b, float c, float s, float
     nb = b * c + a * s;
 }
 
+// Index with bits 2 and 3 exchanged (an involution on 0..15 within each 16-group).
+__device__ __forceinline__ int swap23(int p) { return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1); }
+
+__device__ __forceinline__ void unpack8(uint4 u, float *f)
+{
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        f[2 * j] = __uint_as_float(w[j] << 16);
+        f[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+    }
+}
+
+__device__ __forceinline__ uint4 pack8(const float *f)
+{
+    return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                      pack_bf16x2(f[6], f[7]));
+}
+
 template <int HD>
 __global__ __launch_bounds__(256) void rope_kernel(bf16_t *__restrict__ qkv, bf16_t *__restrict__ vt,
                                                    int64_t ldv, const RowTile *__restrict__ tiles,
@@ -31,8 +51,9 @@ __global__ __launch_bounds__(256) void rope_kernel(bf16_t *__restrict__ qkv, bf1
                                                    const float *__restrict__ cos_t,
                                                    const float *__restrict__ sin_t)
 {
-    constexpr int HALF = HD / 2, Q4 = HD / 4, T = kRopeTile;
-    __shared__ bf16_t sv[HD][T + 2];
+    constexpr int HALF = HD / 2, Q4 = HD / 4, T = kRopeTile, HC = HALF / 8;   // chunks per half
+    constexpr int VLD = T + 8;                      // LDS row of the transposed v tile
+    __shared__ __attribute__((aligned(16))) bf16_t sv[HD * VLD];
 
     const RowTile tile = tiles[blockIdx.x];
     const int head = blockIdx.y;
@@ -40,36 +61,49 @@ __global__ __launch_bounds__(256) void rope_kernel(bf16_t *__restrict__ qkv, bf1
     const int64_t ld = 3 * (int64_t)D;
     bf16_t *base = qkv + (int64_t)d.patch_off * ld + head * HD;
 
-    // q and k: one rotation pair (i, i + HALF) per work item
-    for (int w = threadIdx.x; w < T * 2 * HALF; w += 256) {
-        const int r = w / (2 * HALF), rem = w - r * (2 * HALF), part = rem / HALF,
-                  i = rem - part * HALF;
+    // q and k: one item = 8 elements of the first half and the 8 they pair with
+    for (int w = threadIdx.x; w < T * 2 * HC; w += 256) {
+        const int r = w / (2 * HC), rem = w - r * (2 * HC), part = rem / HC, ch = rem - part * HC;
         const int lr = tile.r0 + r;
         if (lr >= d.n) continue;
         const int hp = lr / d.gw, wp = lr - hp * d.gw;
-        const int j = i < Q4 ? i : i - Q4;
-        const int pos = i < Q4 ? hp : wp;
-        const float c = cos_t[pos * Q4 + j], s = sin_t[pos * Q4 + j];
-        bf16_t *v = base + (int64_t)lr * ld + part * D;
-        float na, nb;
-        rotate(bf16_to_f32(v[i]), bf16_to_f32(v[i + HALF]), c, s, na, nb);
-        v[i] = f32_to_bf16(na);
-        v[i + HALF] = f32_to_bf16(nb);
+        bf16_t *v = base + (int64_t)lr * ld + part * D + ch * 8;
+        float a[8], b[8];
+        unpack8(*reinterpret_cast<const uint4 *>(v), a);
+        unpack8(*reinterpret_cast<const uint4 *>(v + HALF), b);
+        float na[8], nb[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int i = ch * 8 + e;
+            const int j = i < Q4 ? i : i - Q4;
+            const int pos = i < Q4 ? hp : wp;
+            rotate(a[e], b[e], cos_t[pos * Q4 + j], sin_t[pos * Q4 + j], na[e], nb[e]);
+        }
+        *reinterpret_cast<uint4 *>(v) = pack8(na);
+        *reinterpret_cast<uint4 *>(v + HALF) = pack8(nb);
     }
 
-    // v: tile -> LDS -> transposed store
-    for (int w = threadIdx.x; w < T * HD; w += 256) {
-        const int r = w / HD, dd = w - r * HD;
+    // v: 16-byte row chunks -> LDS transposed (sv[d][key]) -> 16-byte stores of 8 columns
+    constexpr int VC = HD / 8;                      // chunks per v row
+    for (int w = threadIdx.x; w < T * VC; w += 256) {
+        const int r = w / VC, ch = w - r * VC;
         const int lr = tile.r0 + r;
-        sv[dd][r] = lr < d.n ? base[(int64_t)lr * ld + 2 * D + dd] : (bf16_t)0;
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (lr < d.n) u = *reinterpret_cast<const uint4 *>(base + (int64_t)lr * ld + 2 * D + ch * 8);
+        const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            sv[(ch * 8 + e) * VLD + r] = (bf16_t)((wd[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
     }
     __syncthreads();
-    // column p of each 16-column group holds key p with bits 2 and 3 swapped (an involution),
-    // the order in which the attention kernel's P.V operand wants 8 keys per lane
-    for (int w = threadIdx.x; w < HD * T; w += 256) {
-        const int dd = w / T, p = w - dd * T;
-        const int key = (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1);
-        vt[((int64_t)head * HD + dd) * ldv + d.vt_off + tile.r0 + p] = sv[dd][key];
+    // physical columns p..p+7 (p % 8 == 0) hold keys in two runs of 4: swap bits 2 and 3
+    for (int w = threadIdx.x; w < HD * (T / 8); w += 256) {
+        const int dd = w / (T / 8), p = (w - dd * (T / 8)) * 8;
+        const int k0 = swap23(p), k1 = swap23(p + 4);   // keys at columns p and p + 4
+        const uint2 lo = *reinterpret_cast<const uint2 *>(&sv[dd * VLD + k0]);
+        const uint2 hi = *reinterpret_cast<const uint2 *>(&sv[dd * VLD + k1]);
+        *reinterpret_cast<uint4 *>(vt + ((int64_t)head * HD + dd) * ldv + d.vt_off + tile.r0 + p) =
+            make_uint4(lo.x, lo.y, hi.x, hi.y);
     }
 }
 

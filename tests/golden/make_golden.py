@@ -1,0 +1,74 @@
+#!/usr/bin/env python3
+"""Write oracle reference rows for the full-size encoder workloads.
+
+The fp32 CPU oracle needs minutes for a 32-layer pass over thousands of patches, too long
+for a test, so this script runs it once and stores sampled visual rows (fp32) in
+``tests/golden/oracle_<workload>.npz``.  It calls only ``oracle`` and the seeded input
+generator ``synth``; the GPU tests regenerate the same inputs from the same seeds.
+
+    python tests/golden/make_golden.py [workload ...] [--workers N]
+"""
+import argparse
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, os.path.dirname(os.path.dirname(HERE)))
+
+import oracle  # noqa: E402
+import synth  # noqa: E402
+
+# images of the packed batch whose rows are stored (the two smallest and the two largest)
+PACKED_IMAGES = 4
+ROWS_PER_IMAGE = 8
+
+
+def sample_rows(m: int, k: int, seed: int):
+    """First, last and k-2 seeded distinct rows of an image with m merged tokens."""
+    rest = [int(r) for r in synth.seeded_distinct_rows(min(k, m), m, seed=seed, stream=7)]
+    rows = sorted(set([0, m - 1] + rest))[:k]
+    return np.array(rows, np.int64)
+
+
+def run(name: str, workers: int):
+    wl = synth.workload(name)
+    cfg, grids = wl.cfg, wl.grids
+    blob = synth.make_weights(cfg)
+    px = synth.make_pixels(cfg, grids)
+    W = oracle.Weights(cfg, blob)
+    offs = np.cumsum([0] + [(cfg.patch * gh) * (cfg.patch * gw) * 3 for gh, gw in grids])
+    tok_offs = np.cumsum([0] + [cfg.tokens(gh, gw) for gh, gw in grids])
+    if name == "packed16":
+        order = np.argsort([gh * gw for gh, gw in grids], kind="stable")
+        images = sorted(set(order[:2].tolist() + order[-2:].tolist()))[:PACKED_IMAGES]
+    else:
+        images = list(range(len(grids)))
+    out = {"images": np.array(images, np.int64)}
+    all_rows, all_vals = [], []
+    for i in images:
+        gh, gw = grids[i]
+        t = time.time()
+        rows = oracle.encode_image(cfg, W, px[offs[i]:offs[i + 1]], gh, gw, workers=workers)
+        m = rows.shape[0]
+        sel = sample_rows(m, ROWS_PER_IMAGE, seed=1000 + i)
+        all_rows.append(tok_offs[i] + sel)
+        all_vals.append(rows[sel])
+        print(f"{name} image {i} ({gh}x{gw}): {time.time() - t:.0f} s", flush=True)
+    out["rows"] = np.concatenate(all_rows)
+    out["values"] = np.concatenate(all_vals).astype(np.float32)
+    out["grids"] = np.array(grids, np.int64)
+    path = os.path.join(HERE, f"oracle_{name}.npz")
+    np.savez_compressed(path, **out)
+    print("wrote", path, out["values"].shape, flush=True)
+
+
+if __name__ == "__main__":
+    ap = argparse.ArgumentParser()
+    ap.add_argument("workloads", nargs="*", default=["v4_384", "v41_1024", "packed16"])
+    ap.add_argument("--workers", type=int, default=os.cpu_count() or 1)
+    a = ap.parse_args()
+    for w in a.workloads:
+        run(w, a.workers)

@@ -38,16 +38,18 @@ vit_status vit_op_layernorm(vit_ctx *ctx, const uint16_t *d_x, const uint16_t *d
                             const uint16_t *d_b, float eps, uint16_t *d_out, void *stream);
 
 /* Row stride (in elements) of the transposed-V buffer for a batch: the buffer is
- * bf16 [heads][head_dim][stride] and image i owns columns starting at a multiple of 64,
+ * binary16 [heads][head_dim][stride] and image i owns columns starting at a multiple of 64,
  * stride = sum over images of ceil(gh*gw / 64) * 64.  -1 if an argument is invalid. */
 int64_t vit_vt_stride(const vit_grid *h_grids, int32_t n_images);
 
 /* 2D RoPE on q and k ([Z] "Step 3": height/width-blocked angles, half-vector rotation;
  * [G] V4: raw patch grid) in place inside d_qkv = bf16 [N][3D] (q | k | v, head-major),
- * and v copied transposed to d_vt = bf16 [H][hd][vit_vt_stride(grids)] for the attention:
- * image i owns the columns from its 64-aligned offset; inside every group of 16 columns,
- * column p holds key (p with bits 2 and 3 swapped); columns past the image's last patch are
- * written as zeros.
+ * and v copied transposed to d_vt = IEEE binary16 [H][hd][vit_vt_stride(grids)] (the operand
+ * type of the attention's P.V product) for the attention: image i owns the columns from its
+ * 64-aligned offset; inside every group of 16 columns, column p holds key (p with bits 2 and
+ * 3 swapped); columns past the image's last patch are written as zeros.  The conversion from
+ * bf16 rounds to nearest even, which is exact for magnitudes 2^-14 .. 65504; larger values
+ * saturate to +-65504.
  * Patch n of an image sits at (n / gw, n % gw) of that image's grid. */
 vit_status vit_op_rope(vit_ctx *ctx, uint16_t *d_qkv, uint16_t *d_vt, const vit_grid *h_grids,
                        int32_t n_images, void *stream);

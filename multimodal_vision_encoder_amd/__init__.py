@@ -249,10 +249,10 @@ class Encoder:
         return out
 
     def op_rope(self, qkv, grids, stream=None):
-        """In place on qkv; returns the transposed-V buffer."""
+        """In place on qkv; returns the transposed-V buffer (torch.float16)."""
         import torch
         H, D = int(self.cfg.heads), int(self.cfg.hidden)
-        vt = torch.empty((H, D // H, vt_stride(grids)), dtype=torch.bfloat16, device=qkv.device)
+        vt = torch.empty((H, D // H, vt_stride(grids)), dtype=torch.float16, device=qkv.device)
         self._check(lib().vit_op_rope(self._ctx, _ptr(qkv), _ptr(vt), grid_array(grids),
                                       len(grids), _stream(stream)))
         return vt

@@ -7,29 +7,40 @@
 // One block = 4 waves x 32 queries of one head of one image.  Keys come in tiles of 64.
 //
 // Data movement: K and V^T tiles go global -> LDS with global_load_lds_dwordx4 (no register
-// staging) into a 3-stage ring; the loads of tile t+2 are issued at the start of iteration
-// t and waited for at its end, so one barrier per tile both publishes tile t+1 and frees the
-// stage being refilled.  LDS rows are stored as XOR-swizzled 16-byte chunks so that the MFMA
-// operand reads (ds_read_b128, 16 lanes per LDS pass) are free of bank conflicts.
+// staging) into a 4-stage ring, one LDS array per stage.  Iteration t issues the copies of
+// tile t+3 and, before its closing barrier, waits only for those of tile t+2, so every copy
+// has two iterations to land.  The copies are written as inline assembly (scalar base, 32-bit
+// per-lane offset, fixed for all tiles) so the compiler neither inserts its conservative
+// wait-for-all-copies before LDS reads nor recomputes addresses per tile; the barrier is a
+// bare s_barrier for the same reason (the fence in __syncthreads waits for every copy).
+// LDS rows are stored as XOR-swizzled 16-byte chunks so that the MFMA operand reads
+// (ds_read_b128, 16 lanes per LDS pass) are free of bank conflicts.
 //
 // Per tile and wave:
 //   S^T = K Q^T           v_mfma_f32_32x32x16_bf16 with K from LDS and Q^T in registers;
 //                         the transpose puts one query per lane (column l%32), so the row
-//                         max and sum need one cross-lane step (v_permlane32_swap).  S^T of tile t+1
-//                         is issued before the softmax of tile t so the MFMA pipe runs while
-//                         the VALU works.
+//                         max and sum need one cross-lane step (v_permlane32_swap).  S^T of
+//                         tile t+1 and its row max are computed in iteration t, next to the
+//                         softmax and P V of tile t, so the MFMA pipe runs while the VALU works.
 //   online softmax        p = exp2(s * c - m * c), c = log2(e)/sqrt(hd): one FMA and one
 //                         v_exp_f32 per score.  The running max m is raised only when a score
 //                         exceeds it by more than 8 (log2 units) somewhere in the wave
-//                         (wave-uniform branch), so the O rescale is skipped on almost every
-//                         tile and p stays below 2^8.  P is packed to bf16 with
-//                         v_cvt_pk_bf16_f32; the row sum is taken on those bf16 values with
-//                         v_dot2c_f32_bf16, so numerator and denominator use the same weights.
-//   O^T += V^T P^T        P^T is already in the B-operand layout of the S^T accumulator (the
-//                         key order inside each 16-key chunk is permuted identically on both
-//                         operands).
+//                         (wave-uniform branch at the top of the iteration), so the O rescale
+//                         is skipped on almost every tile and p stays below 2^8.  P is packed
+//                         to binary16 with v_cvt_pkrtz_f16_f32 (relative error below 2^-10,
+//                         eight times finer than bf16: with near-uniform attention the output
+//                         is a small average of large values, and bf16 weights alone would
+//                         flip about a third of the bf16-rounded outputs); the row sum is
+//                         taken on those same values with v_dot2c_f32_f16, so numerator and
+//                         denominator use the same weights.
+//   O^T += V^T P^T        v_mfma_f32_32x32x16_f16 on the binary16 V^T written by the RoPE
+//                         kernel.  P^T is already in the B-operand layout of the S^T
+//                         accumulator (the key order inside each 16-key chunk is permuted
+//                         identically on both operands).
 // Keys past the image end (last tile only) are masked to -inf; their loads are clamped to
-// the image's last row.  Query rows past the image end are zero and never stored.
+// the image's last row.  Query rows past the image end are zero and never stored.  Past the
+// last tile the ring is refilled with copies of the last tile, whose scores are computed and
+// ignored, so the loop body has no tile-count branches.
 #include <math.h>
 
 #include <type_traits>
@@ -46,20 +57,47 @@ __device__ __forceinline__ int xcd_remap(int bid, int nb)
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ float dot2_bf16(uint32_t p, float acc)
+// Two fp32 -> two binary16 in one v_cvt_pkrtz_f16_f32 (round toward zero); lo in bits 0..15.
+__device__ __forceinline__ uint32_t pack_f16x2_rtz(float lo, float hi)
 {
-    const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, p), one, acc, false);
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
 }
 
-// 16-byte global -> LDS copy; lane l writes lds_base + 16 l (lds_base is wave-uniform).
-__device__ __forceinline__ void load_lds16(const void *g, void *lds_base)
+// acc + (sum of the two binary16 halves of p), v_dot2c_f32_f16.
+__device__ __forceinline__ float dot2_f16(uint32_t p, float acc)
 {
-    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
+    const f16x2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, p), one, acc, false);
+}
+
+// 16-byte global -> LDS copy of base + off (base wave-uniform); lane l writes LDS byte address
+// lds + 16 l (lds wave-uniform).  Inline assembly, so the compiler's wait-count insertion does
+// not see an LDS write (it would wait for every outstanding copy before each LDS read); the
+// kernel waits for its copies itself before each barrier.  m0 needs one wait state before the
+// copy reads it.
+__device__ __forceinline__ void load_lds16(const void *base, uint32_t off, uint32_t lds)
+{
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    // each half widened as unsigned: a signed low half would sign-extend into the high word
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    const uint64_t ub = ((uint64_t)hi << 32) | (uint64_t)lo;
+    __asm__ volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                     ::"v"(off), "s"(ub), "s"(lds) : "memory", "m0");
 }
 
 // s_waitcnt vmcnt(0): every global load of this wave, including the LDS-bound ones, done.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(N) lgkmcnt(0): all but this wave's newest N global loads done, LDS reads done.
+template <int N>
+__device__ __forceinline__ void wait_vmem_n()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+    __builtin_amdgcn_s_waitcnt(0x0070 | (N & 15) | ((N >> 4) << 14));
+}
+// Workgroup barrier without the memory-model fence of __syncthreads (whose release would wait
+// for every outstanding global->LDS load); the callers wait for what they need first.
+__device__ __forceinline__ void bare_barrier() { __asm__ volatile("s_barrier" ::: "memory"); }
 
 // Value of x held by lane l ^ 32 (v_permlane32_swap exchanges the two wave halves).
 __device__ __forceinline__ float xor32(float x)
@@ -69,7 +107,6 @@ __device__ __forceinline__ float xor32(float x)
 }
 
 constexpr float kLazyRescale = 8.0f;   // log2 units
-constexpr int kStages = 3;
 
 template <int HD>
 struct AttnGeom {
@@ -97,7 +134,20 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(
     using G = AttnGeom<HD>;
     constexpr int HDP = G::HDP, KCH = G::KCH, KS = HDP / 16, DB = HDP / 32;
     static_assert(G::KLOADS >= 1 && G::VLOADS >= 1, "tile too small for 256 threads");
-    __shared__ __attribute__((aligned(1024))) char smem[kStages * G::STAGE];
+    __shared__ __attribute__((aligned(1024))) char lds0[G::STAGE];
+    __shared__ __attribute__((aligned(1024))) char lds1[G::STAGE];
+    __shared__ __attribute__((aligned(1024))) char lds2[G::STAGE];
+    __shared__ __attribute__((aligned(1024))) char lds3[G::STAGE];
+    auto stage = [&](auto st) -> char * {
+        constexpr int S = decltype(st)::value;
+        if constexpr (S == 0) return lds0;
+        else if constexpr (S == 1) return lds1;
+        else if constexpr (S == 2) return lds2;
+        else return lds3;
+    };
+    auto stage_lds = [&](auto st) -> uint32_t {   // LDS byte address of a stage
+        return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)stage(st);
+    };
 
     const int L = xcd_remap(blockIdx.x, gridDim.x);
     if (L >= n_work * H) return;
@@ -105,7 +155,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(
     const RowTile wt = work[wi];
     const ImgDesc d = imgs[wt.img];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, g = lane >> 5;
     const int64_t ld = 3 * (int64_t)D;
     const bf16_t *qbase = qkv + (int64_t)d.patch_off * ld + head * HD;
@@ -122,40 +172,58 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(
         qf[kk] = as_bf16x8(v);
     }
 
-    // Issue the loads of key tile t into stage st.  Chunk c of a stage (lane-contiguous per
-    // instruction) holds logical chunk (c % KCH) ^ (row % KCH) of its row.
-    auto issue = [&](int t, int st) {
-        char *sk = smem + st * G::STAGE, *sv = sk + G::K_BYTES;
+    // Copies of key tile t into a stage.  Chunk c of a stage (lane-contiguous per instruction)
+    // holds logical chunk (c % KCH) ^ kswz(row) of its row (V^T: ^ vswz(row)).  The per-lane
+    // byte offsets are the same for every tile: a tile's copies are one scalar base plus these.
+    uint32_t koff[G::KLOADS], voff[G::VLOADS];
+    int krow[G::KLOADS], kdd[G::KLOADS];
+#pragma unroll
+    for (int i = 0; i < G::KLOADS; ++i) {
+        const int c = (i * 4 + wave) * 64 + lane, r = c / KCH, s = (c % KCH) ^ G::kswz(r);
+        krow[i] = r;
+        kdd[i] = (s * 8) % HD;                      // pad chunks (HD < 32) re-read real data
+        koff[i] = (uint32_t)(r * (int)ld + kdd[i]) * 2u;
+    }
+#pragma unroll
+    for (int i = 0; i < G::VLOADS; ++i) {
+        const int c = (i * 4 + wave) * 64 + lane, r = c >> 3, s = (c & 7) ^ G::vswz(r);
+        voff[i] = (uint32_t)((int64_t)(r % HD) * ldv + s * 8) * 2u;
+    }
+    auto issue = [&](int t, auto st) {
+        const uint32_t sk = stage_lds(st), sv = sk + G::K_BYTES;
         const int kv0 = t * 64;
+        const bf16_t *kb = kbase + (int64_t)kv0 * ld;
+        if (kv0 + 64 <= d.n) {
 #pragma unroll
-        for (int i = 0; i < G::KLOADS; ++i) {
-            const int c = (i * 4 + wave) * 64 + lane, r = c / KCH, s = (c % KCH) ^ G::kswz(r);
-            const int key = min(kv0 + r, d.n - 1);
-            const int dd = (s * 8) % HD;            // pad chunks (HD < 32) re-read real data
-            load_lds16(kbase + (int64_t)key * ld + dd, sk + (i * 4 + wave) * 1024);
-        }
+            for (int i = 0; i < G::KLOADS; ++i) load_lds16(kb, koff[i], sk + (i * 4 + wave) * 1024);
+        } else {   // last tile of a ragged image: rows past the end re-read its last row
 #pragma unroll
-        for (int i = 0; i < G::VLOADS; ++i) {
-            const int c = (i * 4 + wave) * 64 + lane, r = c >> 3, s = (c & 7) ^ G::vswz(r);
-            const int dd = r % HD;
-            load_lds16(vbase + (int64_t)dd * ldv + kv0 + s * 8, sv + (i * 4 + wave) * 1024);
+            for (int i = 0; i < G::KLOADS; ++i) {
+                const int r = min(krow[i], d.n - 1 - kv0);
+                load_lds16(kb, (uint32_t)(r * (int)ld + kdd[i]) * 2u, sk + (i * 4 + wave) * 1024);
+            }
         }
+        const bf16_t *vb = vbase + kv0;
+#pragma unroll
+        for (int i = 0; i < G::VLOADS; ++i) load_lds16(vb, voff[i], sv + (i * 4 + wave) * 1024);
     };
 
-    auto qk = [&](int st, f32x16_t *s) {
-        const char *sk = smem + st * G::STAGE;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+    // S^T of one tile: all K fragments are read from LDS first, then the MFMAs run
+    auto qk = [&](auto st, f32x16_t *s) {
+        const char *sk = stage(st);
+        bf16x8_t a[KS][2];
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 const int row = 32 * kb + l32, ch = (2 * kk + g) ^ G::kswz(row);
-                const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(sk + row * (HDP * 2) + ch * 16);
-                s[kb] = mfma32(a, qf[kk], s[kb]);
+                a[kk][kb] = *reinterpret_cast<const bf16x8_t *>(sk + row * (HDP * 2) + ch * 16);
             }
+        const f32x16_t z = {};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(a[kk][kb], qf[kk], kk == 0 ? z : s[kb]);
     };
 
     f32x16_t oacc[DB];
@@ -165,24 +233,66 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(
         for (int r = 0; r < 16; ++r) oacc[b][r] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;   // running max (raw score units) and sum
 
-    // softmax of one tile's scores into bf16 P (pk[chunk][pair]); MASK on the last tile
-    auto softmax = [&](f32x16_t *s, int kv0, uint32_t (*pk)[4], auto mask_tag) {
-        if constexpr (decltype(mask_tag)::value) {
+    auto mask_tile = [&](f32x16_t *s, int kv0) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-                    if (key >= d.n) s[kb][r] = -INFINITY;
-                }
-        }
+            for (int r = 0; r < 16; ++r) {
+                const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
+                if (key >= d.n) s[kb][r] = -INFINITY;
+            }
+    };
+    auto tile_max = [&](const f32x16_t *s) {
         float mx = s[0][0];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-        mx = fmaxf(mx, xor32(mx));
-        if (__ballot((mx - m_run) * c_log2 > kLazyRescale)) {   // wave-uniform
+        return fmaxf(mx, xor32(mx));
+    };
+
+    // O^T += V^T P^T.  Chunk c covers keys 16c..16c+15; B-operand slot 8g+j <-> key
+    // 16c + 8(j/4) + 4g + j%4, i.e. registers 8(c%2)+j of S^T block c/2.  The transposed-V
+    // buffer stores each 16-key group with key bits 2 and 3 swapped, so those 8 keys are the
+    // 16-byte chunk 2c+g of the row: one ds_read_b128 per operand.
+    auto pv = [&](auto st, uint32_t (*pk)[4]) {
+        const char *sv = stage(st) + G::K_BYTES;
+        f16x8_t va[4][DB];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int b = 0; b < DB; ++b) {
+                const int row = 32 * b + l32;
+                va[c][b] = *reinterpret_cast<const f16x8_t *>(sv + row * 128 + (((2 * c + g) ^ G::vswz(row)) * 16));
+            }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const f16x8_t pf = as_f16x8(make_uint4(pk[c][0], pk[c][1], pk[c][2], pk[c][3]));
+#pragma unroll
+            for (int b = 0; b < DB; ++b) oacc[b] = mfma32_f16(va[c][b], pf, oacc[b]);
+        }
+    };
+
+    const int nkv = (d.n + 63) / 64;
+    const bool ragged = (d.n & 63) != 0;
+    constexpr int LOADS = G::KLOADS + G::VLOADS;   // global->LDS loads per tile and thread
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    issue(0, I0{});
+    issue(min(1, nkv - 1), I1{});
+    issue(min(2, nkv - 1), I2{});
+    wait_vmem_n<LOADS>();
+    bare_barrier();
+    // One key tile.  cur holds S^T of tile t and mx its row max; next receives S^T of tile
+    // t+1 (past the last tile: a copy of the last tile, computed and ignored).
+    auto step = [&](int t, auto st, f32x16_t *cur, f32x16_t *next, float &mx) {
+        constexpr int S = decltype(st)::value;
+        using SP = std::integral_constant<int, S>;
+        using SQ = std::integral_constant<int, (S + 1) % 4>;
+        using SD = std::integral_constant<int, (S + 3) % 4>;
+        if (__ballot((mx - m_run) * c_log2 > kLazyRescale)) {   // wave-uniform, rare
             const float m_new = fmaxf(m_run, mx);
             const float alpha = fast_exp2((m_run - m_new) * c_log2);
             m_run = m_new;
@@ -193,64 +303,42 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(
                 for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
         }
         const float mc = m_run * c_log2;
-        float ls = l_run;
+        // stage (t+3)%4 held tile t-1, which every wave finished in iteration t-1; tile t+1
+        // landed before the last barrier
+        issue(min(t + 3, nkv - 1), SD{});
+        qk(SQ{}, next);
+        uint32_t pk[4][4];
+        float ls0 = l_run, ls1 = 0.f;
 #pragma unroll
         for (int c = 0; c < 4; ++c)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int kb = c >> 1, r = 8 * (c & 1) + 2 * j;
-                const float p0 = fast_exp2(__builtin_fmaf(s[kb][r], c_log2, -mc));
-                const float p1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], c_log2, -mc));
-                pk[c][j] = pack_bf16x2(p0, p1);
-                ls = dot2_bf16(pk[c][j], ls);
+                const float p0 = fast_exp2(__builtin_fmaf(cur[kb][r], c_log2, -mc));
+                const float p1 = fast_exp2(__builtin_fmaf(cur[kb][r + 1], c_log2, -mc));
+                pk[c][j] = pack_f16x2_rtz(p0, p1);
+                if (j & 1) ls1 = dot2_f16(pk[c][j], ls1);
+                else ls0 = dot2_f16(pk[c][j], ls0);
             }
-        l_run = ls;
-    };
-
-    // O^T += V^T P^T.  Chunk c covers keys 16c..16c+15; B-operand slot 8g+j <-> key
-    // 16c + 8(j/4) + 4g + j%4, i.e. registers 8(c%2)+j of S^T block c/2.  The transposed-V
-    // buffer stores each 16-key group with key bits 2 and 3 swapped, so those 8 keys are the
-    // 16-byte chunk 2c+g of the row: one ds_read_b128 per operand.
-    auto pv = [&](int st, uint32_t (*pk)[4]) {
-        const char *sv = smem + st * G::STAGE + G::K_BYTES;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const bf16x8_t pf = as_bf16x8(make_uint4(pk[c][0], pk[c][1], pk[c][2], pk[c][3]));
-#pragma unroll
-            for (int b = 0; b < DB; ++b) {
-                const int row = 32 * b + l32;
-                const bf16x8_t va = *reinterpret_cast<const bf16x8_t *>(
-                    sv + row * 128 + (((2 * c + g) ^ G::vswz(row)) * 16));
-                oacc[b] = mfma32(va, pf, oacc[b]);
-            }
-        }
-    };
-
-    const int nkv = (d.n + 63) / 64;
-    const bool ragged = (d.n & 63) != 0;
-    issue(0, 0);
-    if (nkv > 1) issue(1, 1);
-    wait_vmem();
-    __syncthreads();
-    // one key tile: cur holds S^T of tile t, next receives S^T of tile t+1
-    auto step = [&](int t, f32x16_t *cur, f32x16_t *next) {
-        // tile t+1 is in LDS and stage (t+2)%3 is free (everyone finished iteration t-1)
-        if (t + 2 < nkv) issue(t + 2, (t + 2) % kStages);
-        if (t + 1 < nkv) qk((t + 1) % kStages, next);
-        uint32_t pk[4][4];
-        if (ragged && t == nkv - 1) softmax(cur, t * 64, pk, std::true_type{});
-        else softmax(cur, t * 64, pk, std::false_type{});
-        pv(t % kStages, pk);
-        wait_vmem();
-        __syncthreads();
+        l_run = ls0 + ls1;
+        pv(SP{}, pk);
+        if (ragged && t + 1 == nkv - 1) mask_tile(next, (t + 1) * 64);
+        mx = tile_max(next);
+        wait_vmem_n<LOADS>();   // tile t+2 landed; tile t+3 may still be in flight
+        bare_barrier();
     };
     f32x16_t sa[2], sb[2];
-    qk(0, sa);
-    for (int t = 0; t < nkv; t += 2) {      // unrolled by two so the S^T buffers swap roles
-        step(t, sa, sb);
-        if (t + 1 < nkv) step(t + 1, sb, sa);
+    qk(I0{}, sa);
+    if (ragged && nkv == 1) mask_tile(sa, 0);
+    float mx = tile_max(sa);
+    for (int t = 0; t < nkv; t += 4) {      // unrolled by four: stages and S^T buffers rotate
+        step(t, I0{}, sa, sb, mx);
+        if (t + 1 < nkv) step(t + 1, I1{}, sb, sa, mx);
+        if (t + 2 < nkv) step(t + 2, I2{}, sa, sb, mx);
+        if (t + 3 < nkv) step(t + 3, I3{}, sb, sa, mx);
     }
 
+    wait_vmem();
     const float l_tot = l_run + xor32(l_run);
     const float inv = 1.f / l_tot;
     if (q < d.n) {

@@ -13,6 +13,11 @@
 // kernel can stage V^T with 16-byte loads; inside each group of 16 columns, column p holds
 // key p with bits 2 and 3 swapped.  Columns of the tile past the image's last patch are
 // written as zeros, so every column the attention kernel reads is defined.  HBM-bound.
+//
+// V^T is stored as IEEE binary16, the operand type of the attention's P.V product: every
+// bf16 value of magnitude 2^-14 .. 65504 converts exactly (8 significant bits fit in 11),
+// smaller ones keep an absolute error below 2^-25, larger ones saturate to +-65504 (NaN
+// stays NaN).
 #include "kernels.h"
 
 namespace {
@@ -38,6 +43,14 @@ __device__ __forceinline__ void unpack8(uint4 u, float *f)
     }
 }
 
+// bf16 bit pattern -> binary16 bit pattern (round to nearest even, saturating at 65504).
+__device__ __forceinline__ uint16_t bf16_to_f16_sat(uint32_t b)
+{
+    float f = __uint_as_float(b << 16);
+    if (__builtin_fabsf(f) > 65504.f) f = __builtin_copysignf(65504.f, f);
+    return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
 __device__ __forceinline__ uint4 pack8(const float *f)
 {
     return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
@@ -53,7 +66,7 @@ __global__ __launch_bounds__(256) void rope_kernel(bf16_t *__restrict__ qkv, bf1
 {
     constexpr int HALF = HD / 2, Q4 = HD / 4, T = kRopeTile, HC = HALF / 8;   // chunks per half
     constexpr int VLD = T + 8;                      // LDS row of the transposed v tile
-    __shared__ __attribute__((aligned(16))) bf16_t sv[HD * VLD];
+    __shared__ __attribute__((aligned(16))) uint16_t sv[HD * VLD];   // binary16 bits
 
     const RowTile tile = tiles[blockIdx.x];
     const int head = blockIdx.y;
@@ -83,7 +96,7 @@ __global__ __launch_bounds__(256) void rope_kernel(bf16_t *__restrict__ qkv, bf1
         *reinterpret_cast<uint4 *>(v + HALF) = pack8(nb);
     }
 
-    // v: 16-byte row chunks -> LDS transposed (sv[d][key]) -> 16-byte stores of 8 columns
+    // v: 16-byte row chunks -> binary16, LDS transposed (sv[d][key]) -> 16-byte stores of 8 columns
     constexpr int VC = HD / 8;                      // chunks per v row
     for (int w = threadIdx.x; w < T * VC; w += 256) {
         const int r = w / VC, ch = w - r * VC;
@@ -93,7 +106,7 @@ __global__ __launch_bounds__(256) void rope_kernel(bf16_t *__restrict__ qkv, bf1
         const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-            sv[(ch * 8 + e) * VLD + r] = (bf16_t)((wd[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
+            sv[(ch * 8 + e) * VLD + r] = bf16_to_f16_sat((wd[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
     }
     __syncthreads();
     // physical columns p..p+7 (p % 8 == 0) hold keys in two runs of 4: swap bits 2 and 3

@@ -193,7 +193,7 @@ vit_status ensure_workspace(vit_ctx *c, int64_t N, int64_t vt_cols)
             return fail(c, VIT_E_NOMEM, "workspace allocation failed");
         }
     }
-    HIP_TRY(c, hipMemset(c->vt, 0, (size_t)c->H * c->hd * Vc * sizeof(bf16_t)));
+    HIP_TRY(c, hipMemset(c->vt, 0, (size_t)c->H * c->hd * Vc * sizeof(uint16_t)));
     c->cap_patches = Np;
     c->cap_vt_cols = Vc;
     return VIT_OK;

@@ -6,10 +6,23 @@
 // Activation of the linear epilogue.
 enum { ACT_NONE = 0, ACT_GELU_TANH = 1 };
 
+// Device scratch for the split-K tail of the GEMMs (fp32 partial tiles); NULL or too small
+// disables the split.
+struct GemmWorkspace {
+    float *part;
+    size_t bytes;
+};
+
+// Bytes of GemmWorkspace a linear of this shape uses (0: it runs without one), and the most
+// any shape uses on this device.
+size_t gemm_workspace_bytes(int64_t M, int N, int K);
+size_t gemm_workspace_max_bytes();
+
 // out = act(A W^T + b) on bf16 MFMA, fp32 accumulation; out bf16 (rounded once) or fp32.
 // A bf16 [M][K], W bf16 [N][K]; K % 64 == 0.
 hipError_t launch_linear(const bf16_t *A, int64_t M, int K, const bf16_t *W, const bf16_t *bias,
-                         int N, int act, bool out_f32, void *out, hipStream_t s);
+                         int N, int act, bool out_f32, void *out, const GemmWorkspace *ws,
+                         hipStream_t s);
 
 // Patchify + patch projection: x0 = bf16(P W_pe^T + b), W_pe zero-padded to Kp columns.
 hipError_t launch_patch_embed(const uint8_t *px, const ImgDesc *imgs, int n_img, int64_t M,
@@ -20,7 +33,7 @@ hipError_t launch_patch_embed(const uint8_t *px, const ImgDesc *imgs, int n_img,
 // points at >= 16 zero bytes (read for positions in the right/bottom padding).
 hipError_t launch_merge_project(const bf16_t *y, const ImgDesc *imgs, int n_img, int64_t Mtok,
                                 int D, const bf16_t *Wp, const bf16_t *bias, int Dl, float *out,
-                                const bf16_t *zero, hipStream_t s);
+                                const bf16_t *zero, const GemmWorkspace *ws, hipStream_t s);
 
 // Optional residual add + LayerNorm (rows of width D).
 hipError_t launch_layernorm(const bf16_t *x, const bf16_t *delta, bf16_t *xout, int64_t M, int D,

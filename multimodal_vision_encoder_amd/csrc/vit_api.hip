@@ -45,6 +45,8 @@ struct vit_ctx {
     float *d_cos = nullptr, *d_sin = nullptr;
 
     // workspace
+    float *d_gemm_ws = nullptr;   // split-K partial tiles of the GEMMs
+    size_t gemm_ws_bytes = 0;
     int64_t cap_patches = 0, cap_vt_cols = 0, reserve_cap = 0;
     bf16_t *x = nullptr, *ln = nullptr, *qkv = nullptr, *vt = nullptr, *o = nullptr,
            *delta = nullptr, *h1 = nullptr;
@@ -171,8 +173,25 @@ void free_workspace(vit_ctx *c)
     c->cap_patches = c->cap_vt_cols = 0;
 }
 
+// Split-K scratch of the GEMMs, allocated once at its largest size.  Without it (allocation
+// failed) the GEMMs run unsplit, which gives the same results.
+GemmWorkspace gemm_ws(vit_ctx *c)
+{
+    if (!c->d_gemm_ws) {
+        const size_t bytes = gemm_workspace_max_bytes();
+        if (hipMalloc((void **)&c->d_gemm_ws, bytes) == hipSuccess) {
+            c->gemm_ws_bytes = bytes;
+        } else {
+            (void)hipGetLastError();
+            c->d_gemm_ws = nullptr;
+        }
+    }
+    return GemmWorkspace{c->d_gemm_ws, c->d_gemm_ws ? c->gemm_ws_bytes : 0};
+}
+
 vit_status ensure_workspace(vit_ctx *c, int64_t N, int64_t vt_cols)
 {
+    (void)gemm_ws(c);
     if (N <= c->cap_patches && vt_cols <= c->cap_vt_cols) return VIT_OK;
     if (c->reserve_cap > 0 && N > c->reserve_cap)
         return fail(c, VIT_E_NOMEM, "batch of " + std::to_string(N) +
@@ -327,6 +346,7 @@ vit_status encode_impl(vit_ctx *c, const uint8_t *px, const vit_grid *grids, int
     if (p.N == 0) return VIT_OK;
     st = ensure_workspace(c, p.N, p.vt_cols);
     if (st != VIT_OK) return st;
+    const GemmWorkspace gws = gemm_ws(c);
     DevPlan dp{};
     st = stage_plan(c, p, s, dp);
     if (st != VIT_OK) return st;
@@ -348,18 +368,18 @@ vit_status encode_impl(vit_ctx *c, const uint8_t *px, const vit_grid *grids, int
         const Layer &w = c->layers[l];
         TLAUNCH(c, VIT_STEP_LAYERNORM, s, launch_layernorm(c->x, l ? c->delta : nullptr, c->x, p.N, D, w.ln1g, w.ln1b,
                                    c->cfg.ln_eps, c->ln, s));
-        TLAUNCH(c, VIT_STEP_QKV, s, launch_linear(c->ln, p.N, D, w.wqkv, w.bqkv, 3 * D, ACT_NONE, false, c->qkv, s));
+        TLAUNCH(c, VIT_STEP_QKV, s, launch_linear(c->ln, p.N, D, w.wqkv, w.bqkv, 3 * D, ACT_NONE, false, c->qkv, &gws, s));
         TLAUNCH(c, VIT_STEP_ROPE, s, launch_rope(c->qkv, c->vt, p.vt_cols, dp.rope, (int)p.rope.size(), dp.imgs, D, H,
                               c->d_cos, c->d_sin, s));
         if (stop == VIT_DUMP_QKV && arg == l) return copy_out(c->qkv);
         TLAUNCH(c, VIT_STEP_ATTENTION, s, launch_attention(c->qkv, c->vt, p.vt_cols, c->o, dp.attn, (int)p.attn.size(),
                                    dp.imgs, D, H, s));
         if (stop == VIT_DUMP_ATTN && arg == l) return copy_out(c->o);
-        TLAUNCH(c, VIT_STEP_OUT_PROJ, s, launch_linear(c->o, p.N, D, w.wo, w.bo, D, ACT_NONE, false, c->delta, s));
+        TLAUNCH(c, VIT_STEP_OUT_PROJ, s, launch_linear(c->o, p.N, D, w.wo, w.bo, D, ACT_NONE, false, c->delta, &gws, s));
         TLAUNCH(c, VIT_STEP_LAYERNORM, s, launch_layernorm(c->x, c->delta, c->x, p.N, D, w.ln2g, w.ln2b, c->cfg.ln_eps,
                                    c->ln, s));
-        TLAUNCH(c, VIT_STEP_FC1, s, launch_linear(c->ln, p.N, D, w.w1, w.b1, c->F, ACT_GELU_TANH, false, c->h1, s));
-        TLAUNCH(c, VIT_STEP_FC2, s, launch_linear(c->h1, p.N, c->F, w.w2, w.b2, D, ACT_NONE, false, c->delta, s));
+        TLAUNCH(c, VIT_STEP_FC1, s, launch_linear(c->ln, p.N, D, w.w1, w.b1, c->F, ACT_GELU_TANH, false, c->h1, &gws, s));
+        TLAUNCH(c, VIT_STEP_FC2, s, launch_linear(c->h1, p.N, c->F, w.w2, w.b2, D, ACT_NONE, false, c->delta, &gws, s));
         if (stop == VIT_DUMP_LAYER && arg == l) {
             // the residual add is fused into the next LayerNorm; run it to materialise x
             LAUNCH(c, launch_layernorm(c->x, c->delta, c->x, p.N, D, c->lnf_g, c->lnf_b,
@@ -374,7 +394,7 @@ vit_status encode_impl(vit_ctx *c, const uint8_t *px, const vit_grid *grids, int
         LAUNCH(c, launch_dump_merged(c->ln, dp.imgs, ni, p.M, D, (bf16_t *)dst, c->d_zero, s));
         return VIT_OK;
     }
-    TLAUNCH(c, VIT_STEP_PROJECTOR, s, launch_merge_project(c->ln, dp.imgs, ni, p.M, D, c->d_wproj, c->proj_b, c->Dl, out, c->d_zero, s));
+    TLAUNCH(c, VIT_STEP_PROJECTOR, s, launch_merge_project(c->ln, dp.imgs, ni, p.M, D, c->d_wproj, c->proj_b, c->Dl, out, c->d_zero, &gws, s));
     return VIT_OK;
 }
 
@@ -383,7 +403,7 @@ void destroy(vit_ctx *c)
     if (!c) return;
     (void)hipDeviceSynchronize();
     free_workspace(c);
-    void *bufs[] = {c->d_blob, c->d_wpe, c->d_wproj, c->d_cos, c->d_sin, c->d_meta, c->d_zero};
+    void *bufs[] = {c->d_blob, c->d_wpe, c->d_wproj, c->d_cos, c->d_sin, c->d_meta, c->d_zero, c->d_gemm_ws};
     for (void *b : bufs)
         if (b) (void)hipFree(b);
     if (c->h_stage) (void)hipHostFree(c->h_stage);
@@ -684,7 +704,8 @@ vit_status vit_op_linear(vit_ctx *ctx, const uint16_t *d_A, int64_t M, int32_t K
     if (act != VIT_ACT_NONE && act != VIT_ACT_GELU_TANH) return fail(ctx, VIT_E_ARG, "bad act");
     if (M == 0) return VIT_OK;
     if (!d_A || !d_W || !d_out) return fail(ctx, VIT_E_ARG, "NULL pointer");
-    LAUNCH(ctx, launch_linear(d_A, M, K, d_W, d_b, N, act, out_f32 != 0, d_out, (hipStream_t)stream));
+    const GemmWorkspace gws = gemm_ws(ctx);
+    LAUNCH(ctx, launch_linear(d_A, M, K, d_W, d_b, N, act, out_f32 != 0, d_out, &gws, (hipStream_t)stream));
     return VIT_OK;
 }
 
@@ -754,8 +775,9 @@ vit_status vit_op_merge_project(vit_ctx *ctx, const uint16_t *d_y, const vit_gri
     if (!d_y || !d_out) return fail(ctx, VIT_E_ARG, "NULL pointer");
     DevPlan dp{};
     if ((st = stage_plan(ctx, p, (hipStream_t)stream, dp)) != VIT_OK) return st;
+    const GemmWorkspace gws = gemm_ws(ctx);
     LAUNCH(ctx, launch_merge_project(d_y, dp.imgs, (int)p.imgs.size(), p.M, ctx->D, ctx->d_wproj,
-                                     ctx->proj_b, ctx->Dl, d_out, ctx->d_zero, (hipStream_t)stream));
+                                     ctx->proj_b, ctx->Dl, d_out, ctx->d_zero, &gws, (hipStream_t)stream));
     return VIT_OK;
 }
 

@@ -89,9 +89,31 @@ def test_linear_full_size_sampled(N, K, act):
     b = seeded_bf16((N,), 103, 2, std=0.02)
     got = from_dev_bf16(enc.op_linear(to_dev_bf16(A), to_dev_bf16(W), to_dev_bf16(b), act))
     torch.cuda.synchronize()
-    rows = np.r_[0:3, 127:130, 4000:4003, M - 5:M]
+    # the last tile rows (8192..9215) are the leftover round that fc2 splits along K
+    rows = np.r_[0:3, 127:130, 4000:4003, 8192:8196, 8700:8703, M - 5:M]
     want = oracle.linear(f32(A[rows]), f32(W), f32(b), act=act)
     assert_bf16_close(got[rows], want, atol=sum_bound(A[rows], W), what="linear full size")
+
+
+@pytest.mark.parametrize("act,out_f32", [(vit.ACT_GELU_TANH, False), (vit.ACT_NONE, True)])
+def test_linear_split_k_tail(act, out_f32):
+    """264 tiles of 256 x 128 on 256 compute units: the 8 leftover tiles (rows 8192..8399,
+    ragged in M and N) are cut into K slices whose fp32 partials a second kernel sums."""
+    torch = require_gpu()
+    enc, _, _ = encoder()
+    M, K, N = 8400, 2048, 1020
+    A = seeded_bf16((M, K), 107, 0)
+    W = seeded_bf16((N, K), 107, 1, std=0.02)
+    b = seeded_bf16((N,), 107, 2, std=0.02)
+    got = enc.op_linear(to_dev_bf16(A), to_dev_bf16(W), to_dev_bf16(b), act, out_f32)
+    torch.cuda.synchronize()
+    rows = np.r_[0:2, 4000:4002, 8190:8196, 8300:8302, M - 4:M]
+    want = oracle.linear(f32(A[rows]), f32(W), f32(b), act=act, round_out=not out_f32)
+    if out_f32:
+        g = got.cpu().numpy()[rows]
+        assert np.all(np.abs(g - want) <= sum_bound(A[rows], W) + 1e-6 * np.abs(want))
+    else:
+        assert_bf16_close(from_dev_bf16(got)[rows], want, atol=sum_bound(A[rows], W), what="split-K tail")
 
 
 # ------------------------------------------------------------------------------------------

@@ -22,6 +22,11 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
+# HBM bytes per attention launch, from rocprofv3 FETCH_SIZE and WRITE_SIZE passes scaled by
+# the same counters on a plain copy of known size; valid while the kernel source is unchanged
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_v41_1024_hbm_traffic.md")
+ATTN_SOURCE = os.path.join(ROOT, "multimodal_vision_encoder_amd", "csrc", "attention.hip")
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -91,6 +96,37 @@ def cpu_baseline(cfg, blob, px, grids):
             "seconds_per_pass": t_pass}
 
 
+def attention_traffic():
+    """(bytes per launch, note) from the committed counter summary, or (None, reason)."""
+    import hashlib
+    if not os.path.exists(TRAFFIC_FILE):
+        return None, "no counter summary"
+    fields = {}
+    for line in open(TRAFFIC_FILE):
+        if line.startswith("- ") and ":" in line:
+            k, v = line[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    want = fields.get("attention.hip sha256")
+    have = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
+    if want != have:
+        return None, "attention kernel changed since the counters were taken"
+    return float(fields["HBM bytes per launch"]), "rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled"
+
+
+def copy_calibration(mib, reps=5):
+    """A plain device copy of `mib` MiB, `reps` times: the reference the HBM byte counters are
+    scaled by (run under rocprofv3 --pmc)."""
+    import torch
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_mib": mib, "reps": reps, "bytes_read_per_copy": n * 4,
+                      "bytes_written_per_copy": n * 4}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -100,7 +136,12 @@ def main():
                     choices=["tiny", "one_layer", "v4_384", "v41_1024", "packed16"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel timing loop")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -201,9 +242,11 @@ def main():
         if a:
             per_launch = fl["attention"] / (cfg.layers or 1)
             achieved = per_launch / (a["avg_launch_us"] * 1e-6) / 1e12
+            traffic, note = attention_traffic() if args.workload == "v41_1024" else (None, "other workload")
             result["roofline"] = {"kernel": "attention", "bound": "mfma", "achieved": achieved,
                                   "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                                  "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None}
+                                  "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
+                                  "traffic_unit": "bytes per launch", "traffic_note": note}
         log(json.dumps(kernels, indent=1))
 
     if not args.no_cpu_baseline:

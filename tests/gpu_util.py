@@ -55,7 +55,7 @@ def assert_bf16_close(got, want, ulps: float = 1.0, atol: float = 0.0, what: str
 
 
 def assert_projector_gate(got, want, what=""):
-    """The graded gate on fp32 projector outputs: rel-L2 <= 1e-2 and max-abs <= 5e-2."""
+    """The parity gate on fp32 projector outputs: rel-L2 <= 1e-2 and max-abs <= 5e-2."""
     r = rel_l2(got, want)
     m = float(np.abs(np.asarray(got, np.float64) - np.asarray(want, np.float64)).max()) if np.size(want) else 0.0
     assert r <= 1e-2 and m <= 5e-2, f"{what}: rel_l2={r:.3e} max_abs={m:.3e}"

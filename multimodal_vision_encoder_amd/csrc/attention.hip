@@ -7,12 +7,14 @@
 // One block = 4 waves x 32 queries of one head of one image.  Keys come in tiles of 64.
 //
 // Data movement: K and V^T tiles go global -> LDS with global_load_lds_dwordx4 (no register
-// staging) into a 4-stage ring, one LDS array per stage.  Iteration t issues the copies of
-// tile t+3 and, before its closing barrier, waits only for those of tile t+2, so every copy
-// has two iterations to land.  The copies are written as inline assembly (scalar base, 32-bit
-// per-lane offset, fixed for all tiles) so the compiler neither inserts its conservative
-// wait-for-all-copies before LDS reads nor recomputes addresses per tile; the barrier is a
-// bare s_barrier for the same reason (the fence in __syncthreads waits for every copy).
+// staging) into two rings of 3 stages each (48 KB per block).  K of a tile is read one
+// iteration before its V^T, so iteration t issues K of tile t+3 and V^T of tile t+2 and,
+// before its closing barrier, waits only for the copies of the previous iteration: every copy
+// has two iterations to land.  The copies are written as inline assembly (scalar base,
+// 32-bit per-lane offset, fixed for all tiles) so the compiler neither inserts its
+// conservative wait-for-all-copies before LDS reads nor recomputes addresses per tile; the
+// barrier is a bare s_barrier for the same reason (the fence in __syncthreads waits for every
+// copy).
 // LDS rows are stored as XOR-swizzled 16-byte chunks so that the MFMA operand reads
 // (ds_read_b128, 16 lanes per LDS pass) are free of bank conflicts.
 //
@@ -114,7 +116,6 @@ struct AttnGeom {
     static constexpr int KCH = HDP / 8;             // 16-byte chunks per K row (one key)
     static constexpr int K_BYTES = 64 * HDP * 2;    // one K tile
     static constexpr int V_BYTES = HDP * 64 * 2;    // one V^T tile (rows = head dims)
-    static constexpr int STAGE = K_BYTES + V_BYTES;
     static constexpr int KLOADS = 64 * KCH / 256;   // 16-byte loads per thread per K tile
     static constexpr int VLOADS = HDP * 8 / 256;
     // A ds_read_b128 is served 16 lanes at a time over 64 four-byte banks (256 bytes); rows
@@ -134,19 +135,14 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(
     using G = AttnGeom<HD>;
     constexpr int HDP = G::HDP, KCH = G::KCH, KS = HDP / 16, DB = HDP / 32;
     static_assert(G::KLOADS >= 1 && G::VLOADS >= 1, "tile too small for 256 threads");
-    __shared__ __attribute__((aligned(1024))) char lds0[G::STAGE];
-    __shared__ __attribute__((aligned(1024))) char lds1[G::STAGE];
-    __shared__ __attribute__((aligned(1024))) char lds2[G::STAGE];
-    __shared__ __attribute__((aligned(1024))) char lds3[G::STAGE];
-    auto stage = [&](auto st) -> char * {
-        constexpr int S = decltype(st)::value;
-        if constexpr (S == 0) return lds0;
-        else if constexpr (S == 1) return lds1;
-        else if constexpr (S == 2) return lds2;
-        else return lds3;
-    };
-    auto stage_lds = [&](auto st) -> uint32_t {   // LDS byte address of a stage
-        return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)stage(st);
+    // separate rings for K (3 stages) and V^T (3 stages): K of tile t+1 is read one step
+    // before V^T of tile t+1
+    __shared__ __attribute__((aligned(1024))) char kst[3 * G::K_BYTES];
+    __shared__ __attribute__((aligned(1024))) char vst[3 * G::V_BYTES];
+    auto kstage = [&](auto st) -> char * { return kst + decltype(st)::value * G::K_BYTES; };
+    auto vstage = [&](auto st) -> char * { return vst + decltype(st)::value * G::V_BYTES; };
+    auto lds_addr = [&](const char *p) -> uint32_t {
+        return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char *)p;
     };
 
     const int L = xcd_remap(blockIdx.x, gridDim.x);
@@ -189,8 +185,8 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(
         const int c = (i * 4 + wave) * 64 + lane, r = c >> 3, s = (c & 7) ^ G::vswz(r);
         voff[i] = (uint32_t)((int64_t)(r % HD) * ldv + s * 8) * 2u;
     }
-    auto issue = [&](int t, auto st) {
-        const uint32_t sk = stage_lds(st), sv = sk + G::K_BYTES;
+    auto issue_k = [&](int t, auto st) {
+        const uint32_t sk = lds_addr(kstage(st));
         const int kv0 = t * 64;
         const bf16_t *kb = kbase + (int64_t)kv0 * ld;
         if (kv0 + 64 <= d.n) {
@@ -203,14 +199,17 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(
                 load_lds16(kb, (uint32_t)(r * (int)ld + kdd[i]) * 2u, sk + (i * 4 + wave) * 1024);
             }
         }
-        const bf16_t *vb = vbase + kv0;
+    };
+    auto issue_v = [&](int t, auto st) {
+        const uint32_t sv = lds_addr(vstage(st));
+        const bf16_t *vb = vbase + t * 64;
 #pragma unroll
         for (int i = 0; i < G::VLOADS; ++i) load_lds16(vb, voff[i], sv + (i * 4 + wave) * 1024);
     };
 
     // S^T of one tile: all K fragments are read from LDS first, then the MFMAs run
     auto qk = [&](auto st, f32x16_t *s) {
-        const char *sk = stage(st);
+        const char *sk = kstage(st);
         bf16x8_t a[KS][2];
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk)
@@ -256,7 +255,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(
     // buffer stores each 16-key group with key bits 2 and 3 swapped, so those 8 keys are the
     // 16-byte chunk 2c+g of the row: one ds_read_b128 per operand.
     auto pv = [&](auto st, uint32_t (*pk)[4]) {
-        const char *sv = stage(st) + G::K_BYTES;
+        const char *sv = vstage(st);
         f16x8_t va[4][DB];
 #pragma unroll
         for (int c = 0; c < 4; ++c)
@@ -275,23 +274,31 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(
 
     const int nkv = (d.n + 63) / 64;
     const bool ragged = (d.n & 63) != 0;
-    constexpr int LOADS = G::KLOADS + G::VLOADS;   // global->LDS loads per tile and thread
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
     using I3 = std::integral_constant<int, 3>;
-    issue(0, I0{});
-    issue(min(1, nkv - 1), I1{});
-    issue(min(2, nkv - 1), I2{});
-    wait_vmem_n<LOADS>();
+    using I4 = std::integral_constant<int, 4>;
+    using I5 = std::integral_constant<int, 5>;
+    // prologue: K of tiles 0..2, V^T of tiles 0..1; wait for K 0, V^T 0 and K 1
+    issue_k(0, I0{});
+    issue_v(0, I0{});
+    issue_k(min(1, nkv - 1), I1{});
+    issue_v(min(1, nkv - 1), I1{});
+    issue_k(min(2, nkv - 1), I2{});
+    wait_vmem_n<G::KLOADS + G::VLOADS>();
     bare_barrier();
-    // One key tile.  cur holds S^T of tile t and mx its row max; next receives S^T of tile
-    // t+1 (past the last tile: a copy of the last tile, computed and ignored).
+    // One key tile: issue K of tile t+3 and V^T of tile t+2 (into the stages of K t and V^T t-1,
+    // whose last readers were iterations t-1), S^T of tile t+1, softmax and P.V of tile t; then
+    // wait for this wave's copies of the previous iteration (K t+2, V^T t+1) and publish them.
+    // cur holds S^T of tile t and mx its row max; past the last tile the copies and S^T repeat
+    // the last tile and are ignored.
     auto step = [&](int t, auto st, f32x16_t *cur, f32x16_t *next, float &mx) {
         constexpr int S = decltype(st)::value;
-        using SP = std::integral_constant<int, S>;
-        using SQ = std::integral_constant<int, (S + 1) % 4>;
-        using SD = std::integral_constant<int, (S + 3) % 4>;
+        using KQ = std::integral_constant<int, (S + 1) % 3>;   // K of tile t+1
+        using KD = std::integral_constant<int, S % 3>;         // K of tile t+3
+        using VP = std::integral_constant<int, S % 3>;         // V^T of tile t
+        using VD = std::integral_constant<int, (S + 2) % 3>;   // V^T of tile t+2
         if (__ballot((mx - m_run) * c_log2 > kLazyRescale)) {   // wave-uniform, rare
             const float m_new = fmaxf(m_run, mx);
             const float alpha = fast_exp2((m_run - m_new) * c_log2);
@@ -303,10 +310,9 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(
                 for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
         }
         const float mc = m_run * c_log2;
-        // stage (t+3)%4 held tile t-1, which every wave finished in iteration t-1; tile t+1
-        // landed before the last barrier
-        issue(min(t + 3, nkv - 1), SD{});
-        qk(SQ{}, next);
+        issue_k(min(t + 3, nkv - 1), KD{});
+        issue_v(min(t + 2, nkv - 1), VD{});
+        qk(KQ{}, next);
         uint32_t pk[4][4];
         float ls0 = l_run, ls1 = 0.f;
 #pragma unroll
@@ -321,21 +327,23 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(
                 else ls0 = dot2_f16(pk[c][j], ls0);
             }
         l_run = ls0 + ls1;
-        pv(SP{}, pk);
+        pv(VP{}, pk);
         if (ragged && t + 1 == nkv - 1) mask_tile(next, (t + 1) * 64);
         mx = tile_max(next);
-        wait_vmem_n<LOADS>();   // tile t+2 landed; tile t+3 may still be in flight
+        wait_vmem_n<G::KLOADS + G::VLOADS>();
         bare_barrier();
     };
     f32x16_t sa[2], sb[2];
     qk(I0{}, sa);
     if (ragged && nkv == 1) mask_tile(sa, 0);
     float mx = tile_max(sa);
-    for (int t = 0; t < nkv; t += 4) {      // unrolled by four: stages and S^T buffers rotate
+    for (int t = 0; t < nkv; t += 6) {   // unrolled by six: rings of three, S^T buffers of two
         step(t, I0{}, sa, sb, mx);
         if (t + 1 < nkv) step(t + 1, I1{}, sb, sa, mx);
         if (t + 2 < nkv) step(t + 2, I2{}, sa, sb, mx);
         if (t + 3 < nkv) step(t + 3, I3{}, sb, sa, mx);
+        if (t + 4 < nkv) step(t + 4, I4{}, sa, sb, mx);
+        if (t + 5 < nkv) step(t + 5, I5{}, sb, sa, mx);
     }
 
     wait_vmem();

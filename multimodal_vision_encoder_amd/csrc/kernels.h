@@ -3,9 +3,6 @@
 
 #include "common.h"
 
-// Activation of the linear epilogue.
-enum { ACT_NONE = 0, ACT_GELU_TANH = 1 };
-
 // Device scratch for the split-K tail of the GEMMs (fp32 partial tiles); NULL or too small
 // disables the split.
 struct GemmWorkspace {
@@ -18,16 +15,21 @@ struct GemmWorkspace {
 size_t gemm_workspace_bytes(int64_t M, int N, int K);
 size_t gemm_workspace_max_bytes();
 
+// Activation of the linear epilogue.
+enum { ACT_NONE = 0, ACT_GELU_TANH = 1 };
+
 // out = act(A W^T + b) on bf16 MFMA, fp32 accumulation; out bf16 (rounded once) or fp32.
 // A bf16 [M][K], W bf16 [N][K]; K % 64 == 0.
 hipError_t launch_linear(const bf16_t *A, int64_t M, int K, const bf16_t *W, const bf16_t *bias,
                          int N, int act, bool out_f32, void *out, const GemmWorkspace *ws,
                          hipStream_t s);
 
-// Patchify + patch projection: x0 = bf16(P W_pe^T + b), W_pe zero-padded to Kp columns.
+// Patchify + patch projection: x0 = bf16(P W_pe^T + b), W_pe zero-padded to Kp columns
+// (Kp % 32 == 0); `patches` is bf16 scratch [M][Kp] for the patch matrix.
 hipError_t launch_patch_embed(const uint8_t *px, const ImgDesc *imgs, int n_img, int64_t M,
                               const float *s3, const float *t3, int ps, const bf16_t *Wpe,
-                              int Kp, const bf16_t *bias, int D, bf16_t *out, hipStream_t s);
+                              int Kp, const bf16_t *bias, int D, bf16_t *patches, bf16_t *out,
+                              const GemmWorkspace *ws, hipStream_t s);
 
 // 3x3 merge gather + projector: out fp32 [Mtok][Dl]; Wp position-major [Dl][9D]; `zero`
 // points at >= 16 zero bytes (read for positions in the right/bottom padding).

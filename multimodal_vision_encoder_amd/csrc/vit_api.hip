@@ -49,7 +49,7 @@ struct vit_ctx {
     size_t gemm_ws_bytes = 0;
     int64_t cap_patches = 0, cap_vt_cols = 0, reserve_cap = 0;
     bf16_t *x = nullptr, *ln = nullptr, *qkv = nullptr, *vt = nullptr, *o = nullptr,
-           *delta = nullptr, *h1 = nullptr;
+           *delta = nullptr, *h1 = nullptr, *patches = nullptr;
 
     // per-call metadata: pinned staging -> device
     char *h_stage = nullptr, *d_meta = nullptr;
@@ -165,7 +165,7 @@ vit_status make_plan(vit_ctx *ctx, const vit_grid *grids, int n, Plan &p)
 
 void free_workspace(vit_ctx *c)
 {
-    bf16_t **bufs[] = {&c->x, &c->ln, &c->qkv, &c->vt, &c->o, &c->delta, &c->h1};
+    bf16_t **bufs[] = {&c->x, &c->ln, &c->qkv, &c->vt, &c->o, &c->delta, &c->h1, &c->patches};
     for (auto b : bufs) {
         if (*b) (void)hipFree(*b);
         *b = nullptr;
@@ -204,7 +204,8 @@ vit_status ensure_workspace(vit_ctx *c, int64_t N, int64_t vt_cols)
     const size_t D = c->D;
     struct { bf16_t **p; size_t n; } req[] = {
         {&c->x, Np * D}, {&c->ln, Np * D}, {&c->qkv, Np * 3 * D}, {&c->o, Np * D},
-        {&c->delta, Np * D}, {&c->h1, Np * (size_t)c->F}, {&c->vt, (size_t)c->H * c->hd * Vc}};
+        {&c->delta, Np * D}, {&c->h1, Np * (size_t)c->F}, {&c->vt, (size_t)c->H * c->hd * Vc},
+        {&c->patches, Np * (size_t)c->Kp}};
     for (auto &r : req) {
         if (hipMalloc((void **)r.p, r.n * sizeof(bf16_t)) != hipSuccess) {
             (void)hipGetLastError();
@@ -361,7 +362,7 @@ vit_status encode_impl(vit_ctx *c, const uint8_t *px, const vit_grid *grids, int
         return VIT_OK;
     }
     TLAUNCH(c, VIT_STEP_PATCH_EMBED, s, launch_patch_embed(px, dp.imgs, ni, p.N, c->s3, c->t3, c->ps, c->d_wpe, c->Kp,
-                                 c->pe_b, D, c->x, s));
+                                 c->pe_b, D, c->patches, c->x, &gws, s));
     if (stop == VIT_DUMP_EMBED) return copy_out(c->x);
 
     for (int l = 0; l < L; ++l) {

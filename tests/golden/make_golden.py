@@ -2,9 +2,17 @@
 """Write oracle reference rows for the full-size encoder workloads.
 
 The fp32 CPU oracle needs minutes for a 32-layer pass over thousands of patches, too long
-for a test, so this script runs it once and stores sampled visual rows (fp32) in
-``tests/golden/oracle_<workload>.npz``.  It calls only ``oracle`` and the seeded input
-generator ``synth``; the GPU tests regenerate the same inputs from the same seeds.
+for a test, so this script runs it once and stores, in ``tests/golden/oracle_<workload>.npz``:
+
+  rows, values        sampled visual rows (global token index) and the fp32 oracle's values;
+  values64            the same rows from the fp64 twin of the oracle (same algorithm and bf16
+                      rounding points, fp64 arithmetic between them): the spread between the
+                      two is the method's own sensitivity to summation order at full depth;
+  layer0_rows/values  sampled patch rows of the residual stream after the first block (fp32
+                      oracle), for a one-block end-to-end check at full size.
+
+It calls only ``oracle`` and the seeded input generator ``synth``; the GPU tests regenerate
+the same inputs from the same seeds.
 
     python tests/golden/make_golden.py [workload ...] [--workers N]
 """
@@ -24,6 +32,7 @@ import synth  # noqa: E402
 # images of the packed batch whose rows are stored (the two smallest and the two largest)
 PACKED_IMAGES = 4
 ROWS_PER_IMAGE = 8
+LAYER0_ROWS_PER_IMAGE = 64
 
 
 def sample_rows(m: int, k: int, seed: int):
@@ -46,19 +55,31 @@ def run(name: str, workers: int):
         images = sorted(set(order[:2].tolist() + order[-2:].tolist()))[:PACKED_IMAGES]
     else:
         images = list(range(len(grids)))
+    patch_offs = np.cumsum([0] + [gh * gw for gh, gw in grids])
     out = {"images": np.array(images, np.int64)}
-    all_rows, all_vals = [], []
+    all_rows, all_vals, all_vals64, l0_rows, l0_vals = [], [], [], [], []
     for i in images:
         gh, gw = grids[i]
+        img = px[offs[i]:offs[i + 1]]
         t = time.time()
-        rows = oracle.encode_image(cfg, W, px[offs[i]:offs[i + 1]], gh, gw, workers=workers)
+        dumps = {}
+        rows = oracle.encode_image(cfg, W, img, gh, gw, workers=workers, dumps=dumps)
         m = rows.shape[0]
         sel = sample_rows(m, ROWS_PER_IMAGE, seed=1000 + i)
         all_rows.append(tok_offs[i] + sel)
         all_vals.append(rows[sel])
+        psel = sample_rows(gh * gw, LAYER0_ROWS_PER_IMAGE, seed=2000 + i)
+        l0_rows.append(patch_offs[i] + psel)
+        l0_vals.append(np.asarray(dumps["layer0"])[psel])
+        del dumps
+        rows64 = oracle.encode_image(cfg, W, img, gh, gw, prec="f64", workers=workers)
+        all_vals64.append(rows64[sel])
         print(f"{name} image {i} ({gh}x{gw}): {time.time() - t:.0f} s", flush=True)
     out["rows"] = np.concatenate(all_rows)
     out["values"] = np.concatenate(all_vals).astype(np.float32)
+    out["values64"] = np.concatenate(all_vals64).astype(np.float64)
+    out["layer0_rows"] = np.concatenate(l0_rows)
+    out["layer0_values"] = np.concatenate(l0_vals).astype(np.float32)
     out["grids"] = np.array(grids, np.int64)
     path = os.path.join(HERE, f"oracle_{name}.npz")
     np.savez_compressed(path, **out)

@@ -131,7 +131,8 @@ vit_status vit_overlay(vit_ctx *ctx, uint16_t *d_embeds, int64_t n_embed_rows,
  * the given batch and copies that tensor into d_dst (dst_bytes must equal its size):
  *   VIT_DUMP_PATCHES     bf16 [N][3*patch^2]   patchify output (same loader as the GEMM)
  *   VIT_DUMP_EMBED       bf16 [N][D]           patch projection output
- *   VIT_DUMP_QKV         bf16 [N][3D]          q,k after RoPE and v of layer `arg`
+ *   VIT_DUMP_QKV         bf16 [N][3D]          q,k after RoPE and v of layer `arg`; the k
+ *                                              columns hold binary16 (as vit_op_rope)
  *   VIT_DUMP_ATTN        bf16 [N][D]           attention output of layer `arg`
  *   VIT_DUMP_LAYER       bf16 [N][D]           residual stream after layer `arg`
  *   VIT_DUMP_FINAL_NORM  bf16 [N][D]           final LayerNorm output

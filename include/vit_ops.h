@@ -43,23 +43,37 @@ vit_status vit_op_layernorm(vit_ctx *ctx, const uint16_t *d_x, const uint16_t *d
 int64_t vit_vt_stride(const vit_grid *h_grids, int32_t n_images);
 
 /* 2D RoPE on q and k ([Z] "Step 3": height/width-blocked angles, half-vector rotation;
- * [G] V4: raw patch grid) in place inside d_qkv = bf16 [N][3D] (q | k | v, head-major),
- * and v copied transposed to d_vt = IEEE binary16 [H][hd][vit_vt_stride(grids)] (the operand
+ * [G] V4: raw patch grid) in place inside d_qkv = bf16 [N][3D] (q | k | v, head-major).
+ * Rotated q is stored as bf16; rotated k is rounded to bf16 and then stored as IEEE binary16
+ * bit patterns (the attention's score operand type), so after this call columns D..2D-1 of
+ * d_qkv hold binary16.  v is copied transposed to d_vt = IEEE binary16 [H][hd][vit_vt_stride(grids)] (the operand
  * type of the attention's P.V product) for the attention: image i owns the columns from its
  * 64-aligned offset; inside every group of 16 columns, column p holds key (p with bits 2 and
- * 3 swapped); columns past the image's last patch are written as zeros.  The conversion from
- * bf16 rounds to nearest even, which is exact for magnitudes 2^-14 .. 65504; larger values
- * saturate to +-65504.
+ * 3 swapped); columns past the image's last patch are written as zeros.  Both conversions
+ * from bf16 round to nearest even, which is exact for magnitudes 2^-14 .. 65504; larger
+ * values saturate to +-65504.
  * Patch n of an image sits at (n / gw, n % gw) of that image's grid. */
 vit_status vit_op_rope(vit_ctx *ctx, uint16_t *d_qkv, uint16_t *d_vt, const vit_grid *h_grids,
                        int32_t n_images, void *stream);
 
 /* Bidirectional softmax attention inside each image of a packed batch (block-diagonal),
  * scale 1/sqrt(head_dim): d_o = bf16 [N][D], head h in columns h*hd .. h*hd+hd-1.
- * Inputs as produced by vit_op_rope. */
+ * Inputs as produced by vit_op_rope (bf16 q, binary16 k in d_qkv; binary16 V^T).  Scores are
+ * formed from q * log2(e)/sqrt(head_dim) rounded to binary16; softmax weights enter the
+ * value product as binary16. */
 vit_status vit_op_attention(vit_ctx *ctx, const uint16_t *d_qkv, const uint16_t *d_vt,
                             const vit_grid *h_grids, int32_t n_images, uint16_t *d_o,
                             void *stream);
+
+/* Key slices of the attention (vit_encode and vit_op_attention).  With n slices the keys of
+ * every (query tile, head) are cut into n contiguous ranges processed by separate blocks; each
+ * range's output, normalised by its own softmax sum, is kept as binary16 with its (max, sum),
+ * and a merge weights the ranges by sum * 2^(max - overall max) and rounds once to bf16.  The
+ * results agree with the unsliced attention within the same error bounds (not bitwise).
+ * n = 0 (the default) picks n per batch from a makespan model of the GPU's block slots (more
+ * slices when a few large images leave part of the GPU idle in the last round); 1..4 fixes it.
+ * VIT_E_ARG for other values. */
+vit_status vit_set_attention_split(vit_ctx *ctx, int32_t n);
 
 /* 3x3 merge + projector ([Z] "Step 4": right/bottom zero padding on the 2D grid,
  * channel-major unfold; then the aligner projection): d_y = bf16 [N][D] final-norm rows,

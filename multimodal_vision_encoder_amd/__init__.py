@@ -24,7 +24,8 @@ ACT_NONE, ACT_GELU_TANH = 0, 1
 EXPORTS = ("vit_blob_elems", "vit_create", "vit_destroy", "vit_reserve", "vit_num_tokens",
            "vit_num_patches", "vit_encode", "vit_layout", "vit_overlay", "vit_dump",
            "vit_last_error", "vit_op_linear", "vit_op_layernorm", "vit_vt_stride", "vit_op_rope",
-           "vit_op_attention", "vit_op_merge_project", "vit_timing_enable", "vit_timing_read")
+           "vit_op_attention", "vit_op_merge_project", "vit_timing_enable", "vit_timing_read",
+           "vit_set_attention_split")
 STEP_NAMES = ("patch_embed", "layernorm", "qkv", "rope", "attention", "out_proj", "fc1", "fc2",
               "projector", "overlay")
 
@@ -84,6 +85,7 @@ def lib():
             "vit_op_merge_project": (i32, [vp, vp, P(Grid), i32, vp, vp]),
             "vit_timing_enable": (i32, [vp, i32]),
             "vit_timing_read": (i32, [vp, vp, vp]),
+            "vit_set_attention_split": (i32, [vp, i32]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -249,13 +251,18 @@ class Encoder:
         return out
 
     def op_rope(self, qkv, grids, stream=None):
-        """In place on qkv; returns the transposed-V buffer (torch.float16)."""
+        """In place on qkv (q bf16, k then binary16); returns the transposed-V buffer
+        (torch.float16)."""
         import torch
         H, D = int(self.cfg.heads), int(self.cfg.hidden)
         vt = torch.empty((H, D // H, vt_stride(grids)), dtype=torch.float16, device=qkv.device)
         self._check(lib().vit_op_rope(self._ctx, _ptr(qkv), _ptr(vt), grid_array(grids),
                                       len(grids), _stream(stream)))
         return vt
+
+    def set_attention_split(self, n):
+        """Key slices of the attention: 0 = chosen per batch, 1..4 = fixed."""
+        self._check(lib().vit_set_attention_split(self._ctx, int(n)))
 
     def op_attention(self, qkv, vt, grids, stream=None):
         import torch

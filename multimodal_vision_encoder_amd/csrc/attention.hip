@@ -18,33 +18,36 @@
 // LDS rows are stored as XOR-swizzled 16-byte chunks so that the MFMA operand reads
 // (ds_read_b128, 16 lanes per LDS pass) are free of bank conflicts.
 //
-// Per tile and wave:
-//   S^T = K Q^T           v_mfma_f32_32x32x16_bf16 with K from LDS and Q^T in registers;
-//                         the transpose puts one query per lane (column l%32), so the row
-//                         max and sum need one cross-lane step (v_permlane32_swap).  S^T of
-//                         tile t+1 and its row max are computed in iteration t, next to the
-//                         softmax and P V of tile t, so the MFMA pipe runs while the VALU works.
-//   online softmax        p = exp2(s * c - m * c), c = log2(e)/sqrt(hd): one FMA and one
-//                         v_exp_f32 per score.  The running max m is raised only when a score
-//                         exceeds it by more than 8 (log2 units) somewhere in the wave
-//                         (wave-uniform branch at the top of the iteration), so the O rescale
-//                         is skipped on almost every tile and p stays below 2^8.  P is packed
+// Scores in log2 units: each wave scales its q rows by log2(e)/sqrt(hd) once and rounds them
+// to binary16; k is stored as binary16 by the RoPE kernel (exact for bf16 values of normal
+// binary16 range).  Per tile and wave:
+//   S^T = K Q^T - m       v_mfma_f32_32x32x16_f16 with K from LDS and Q^T in registers, the
+//                         accumulator starting from -m (m = running row max, one value per
+//                         lane: the transpose puts one query per lane, column l%32), so the
+//                         scores come out already shifted.
+//   online softmax        p = exp2(S) (one v_exp_f32 per score, no other arithmetic), packed
 //                         to binary16 with v_cvt_pkrtz_f16_f32 (relative error below 2^-10,
 //                         eight times finer than bf16: with near-uniform attention the output
 //                         is a small average of large values, and bf16 weights alone would
 //                         flip about a third of the bf16-rounded outputs); the row sum is
 //                         taken on those same values with v_dot2c_f32_f16, so numerator and
-//                         denominator use the same weights.
+//                         denominator use the same weights.  m only moves when a lane's tile
+//                         sum exceeds 2^8 (wave-uniform branch, rare), which bounds every
+//                         weight by 2^8 without a per-tile max.
 //   O^T += V^T P^T        v_mfma_f32_32x32x16_f16 on the binary16 V^T written by the RoPE
 //                         kernel.  P^T is already in the B-operand layout of the S^T
 //                         accumulator (the key order inside each 16-key chunk is permuted
 //                         identically on both operands).
+// Each step reads all its MFMA operands from LDS first, runs the softmax of tile t while the
+// reads land, then the MFMAs of S^T (tile t+1, into the registers the softmax freed) and of
+// P.V (tile t); the other wave on the SIMD fills the gaps of either phase.
 // Keys past the image end (last tile only) are masked to -inf; their loads are clamped to
 // the image's last row.  Query rows past the image end are zero and never stored.  Past the
 // last tile the ring is refilled with copies of the last tile, whose scores are computed and
 // ignored, so the loop body has no tile-count branches.
 #include <math.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "kernels.h"
@@ -100,6 +103,9 @@ __device__ __forceinline__ void wait_vmem_n()
 // Workgroup barrier without the memory-model fence of __syncthreads (whose release would wait
 // for every outstanding global->LDS load); the callers wait for what they need first.
 __device__ __forceinline__ void bare_barrier() { __asm__ volatile("s_barrier" ::: "memory"); }
+// The same barrier, issued only once x is available (so every LDS read that x depends on has
+// completed in this wave).
+__device__ __forceinline__ void barrier_after(float x) { __asm__ volatile("s_barrier" ::"v"(x) : "memory"); }
 
 // Value of x held by lane l ^ 32 (v_permlane32_swap exchanges the two wave halves).
 __device__ __forceinline__ float xor32(float x)
@@ -108,7 +114,7 @@ __device__ __forceinline__ float xor32(float x)
     return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
 }
 
-constexpr float kLazyRescale = 8.0f;   // log2 units
+constexpr float kLazySum = 256.f;   // largest weight (2^8) left unrescaled
 
 template <int HD>
 struct AttnGeom {
@@ -130,26 +136,31 @@ template <int HD>
 __global__ __launch_bounds__(256, 2) void attention_kernel(
     const bf16_t *__restrict__ qkv, const bf16_t *__restrict__ vt, int64_t ldv,
     bf16_t *__restrict__ o, const RowTile *__restrict__ work, int n_work,
-    const ImgDesc *__restrict__ imgs, int D, int H, float c_log2)
+    const ImgDesc *__restrict__ imgs, int D, int H, float c_log2, int nsplit,
+    uint16_t *__restrict__ part_o, float2 *__restrict__ part_ml, int64_t nrows)
 {
     using G = AttnGeom<HD>;
     constexpr int HDP = G::HDP, KCH = G::KCH, KS = HDP / 16, DB = HDP / 32;
     static_assert(G::KLOADS >= 1 && G::VLOADS >= 1, "tile too small for 256 threads");
-    // separate rings for K (3 stages) and V^T (3 stages): K of tile t+1 is read one step
-    // before V^T of tile t+1
-    __shared__ __attribute__((aligned(1024))) char kst[3 * G::K_BYTES];
-    __shared__ __attribute__((aligned(1024))) char vst[3 * G::V_BYTES];
+    // K and V^T rings of four stages each; tile j sits in stage j % 4 of its ring
+    __shared__ __attribute__((aligned(1024))) char kst[4 * G::K_BYTES];
+    __shared__ __attribute__((aligned(1024))) char vst[4 * G::V_BYTES];
     auto kstage = [&](auto st) -> char * { return kst + decltype(st)::value * G::K_BYTES; };
     auto vstage = [&](auto st) -> char * { return vst + decltype(st)::value * G::V_BYTES; };
     auto lds_addr = [&](const char *p) -> uint32_t {
         return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char *)p;
     };
 
-    const int L = xcd_remap(blockIdx.x, gridDim.x);
-    if (L >= n_work * H) return;
+    // block -> (head, query tile, key slice); the slices of one tile are neighbours
+    const int Lx = xcd_remap(blockIdx.x, gridDim.x);
+    if (Lx >= n_work * H * nsplit) return;
+    const int split = Lx % nsplit, L = Lx / nsplit;
     const int head = L / n_work, wi = L - head * n_work;
     const RowTile wt = work[wi];
     const ImgDesc d = imgs[wt.img];
+    // key tiles [t0, t0 + nkv) of the image's nkv_all
+    const int nkv_all = (d.n + 63) / 64, per = (nkv_all + nsplit - 1) / nsplit;
+    const int t0 = split * per, nkv = min(nkv_all, t0 + per) - t0;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, g = lane >> 5;
@@ -159,35 +170,47 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(
     const bf16_t *vbase = vt + (int64_t)head * HD * ldv + d.vt_off;
 
     const int q = wt.r0 + wave * 32 + l32;   // this lane's query (local row)
-    bf16x8_t qf[KS];
+    if (nkv <= 0) {   // empty key slice (image shorter than the slices): weight zero in the merge
+        if (q < d.n) {
+            const int64_t row = (int64_t)d.patch_off + q;
+            uint16_t *prow = part_o + ((int64_t)split * nrows + row) * D + head * HD;
+            for (int dd = 4 * g; dd < HD; dd += 8) *reinterpret_cast<uint2 *>(prow + dd) = make_uint2(0, 0);
+            if (g == 0) part_ml[((int64_t)split * H + head) * nrows + row] = make_float2(-INFINITY, 0.f);
+        }
+        return;
+    }
+    // q * log2(e)/sqrt(hd), rounded once to binary16: scores come out in log2 units
+    f16x8_t qf[KS];
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
         const int dd = 16 * kk + 8 * g;
         uint4 v = make_uint4(0, 0, 0, 0);
         if (q < d.n && dd < HD) v = *reinterpret_cast<const uint4 *>(qbase + (int64_t)q * ld + dd);
-        qf[kk] = as_bf16x8(v);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float x = __uint_as_float(e & 1 ? w[e >> 1] & 0xFFFF0000u : w[e >> 1] << 16) * c_log2;
+            qf[kk][e] = (_Float16)fminf(fmaxf(x, -65504.f), 65504.f);
+        }
     }
 
     // Copies of key tile t into a stage.  Chunk c of a stage (lane-contiguous per instruction)
     // holds logical chunk (c % KCH) ^ kswz(row) of its row (V^T: ^ vswz(row)).  The per-lane
     // byte offsets are the same for every tile: a tile's copies are one scalar base plus these.
     uint32_t koff[G::KLOADS], voff[G::VLOADS];
-    int krow[G::KLOADS], kdd[G::KLOADS];
 #pragma unroll
     for (int i = 0; i < G::KLOADS; ++i) {
-        const int c = (i * 4 + wave) * 64 + lane, r = c / KCH, s = (c % KCH) ^ G::kswz(r);
-        krow[i] = r;
-        kdd[i] = (s * 8) % HD;                      // pad chunks (HD < 32) re-read real data
-        koff[i] = (uint32_t)(r * (int)ld + kdd[i]) * 2u;
+        const int c = (i * 4 + wave) * 64 + lane, r = c / KCH, sw = (c % KCH) ^ G::kswz(r);
+        koff[i] = (uint32_t)(r * (int)ld + (sw * 8) % HD) * 2u;   // pad chunks (HD < 32) re-read real data
     }
 #pragma unroll
     for (int i = 0; i < G::VLOADS; ++i) {
-        const int c = (i * 4 + wave) * 64 + lane, r = c >> 3, s = (c & 7) ^ G::vswz(r);
-        voff[i] = (uint32_t)((int64_t)(r % HD) * ldv + s * 8) * 2u;
+        const int c = (i * 4 + wave) * 64 + lane, r = c >> 3, sw = (c & 7) ^ G::vswz(r);
+        voff[i] = (uint32_t)((int64_t)(r % HD) * ldv + sw * 8) * 2u;
     }
-    auto issue_k = [&](int t, auto st) {
+    auto issue_k = [&](int t, auto st) {   // t: tile index inside the slice
         const uint32_t sk = lds_addr(kstage(st));
-        const int kv0 = t * 64;
+        const int kv0 = (t0 + t) * 64;
         const bf16_t *kb = kbase + (int64_t)kv0 * ld;
         if (kv0 + 64 <= d.n) {
 #pragma unroll
@@ -195,34 +218,46 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(
         } else {   // last tile of a ragged image: rows past the end re-read its last row
 #pragma unroll
             for (int i = 0; i < G::KLOADS; ++i) {
-                const int r = min(krow[i], d.n - 1 - kv0);
-                load_lds16(kb, (uint32_t)(r * (int)ld + kdd[i]) * 2u, sk + (i * 4 + wave) * 1024);
+                const int c = (i * 4 + wave) * 64 + lane, r = c / KCH, sw = (c % KCH) ^ G::kswz(r);
+                const int rc = min(r, d.n - 1 - kv0);
+                load_lds16(kb, (uint32_t)(rc * (int)ld + (sw * 8) % HD) * 2u, sk + (i * 4 + wave) * 1024);
             }
         }
     };
     auto issue_v = [&](int t, auto st) {
         const uint32_t sv = lds_addr(vstage(st));
-        const bf16_t *vb = vbase + t * 64;
+        const bf16_t *vb = vbase + (t0 + t) * 64;
 #pragma unroll
         for (int i = 0; i < G::VLOADS; ++i) load_lds16(vb, voff[i], sv + (i * 4 + wave) * 1024);
     };
 
-    // S^T of one tile: all K fragments are read from LDS first, then the MFMAs run
-    auto qk = [&](auto st, f32x16_t *s) {
+    // MFMA operands of one step, read from LDS at its start (the copies were waited for before
+    // the previous barrier).
+    f16x8_t kf[KS][2];   // K of the next tile: A operands of S^T
+    f16x8_t vf[4][DB];   // V^T of the previous tile: A operands of O^T
+    auto read_k = [&](auto st) {
         const char *sk = kstage(st);
-        bf16x8_t a[KS][2];
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 const int row = 32 * kb + l32, ch = (2 * kk + g) ^ G::kswz(row);
-                a[kk][kb] = *reinterpret_cast<const bf16x8_t *>(sk + row * (HDP * 2) + ch * 16);
+                kf[kk][kb] = *reinterpret_cast<const f16x8_t *>(sk + row * (HDP * 2) + ch * 16);
             }
-        const f32x16_t z = {};
+    };
+    // V^T chunk c covers keys 16c..16c+15; B-operand slot 8g+j <-> key 16c + 8(j/4) + 4g + j%4,
+    // i.e. registers 8(c%2)+j of S^T block c/2.  The transposed-V buffer stores each 16-key
+    // group with key bits 2 and 3 swapped, so those 8 keys are the 16-byte chunk 2c+g of the
+    // row: one ds_read_b128 per operand.
+    auto read_v = [&](auto st) {
+        const char *sv = vstage(st);
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk)
+        for (int c = 0; c < 4; ++c)
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(a[kk][kb], qf[kk], kk == 0 ? z : s[kb]);
+            for (int b = 0; b < DB; ++b) {
+                const int row = 32 * b + l32;
+                vf[c][b] = *reinterpret_cast<const f16x8_t *>(sv + row * 128 + (((2 * c + g) ^ G::vswz(row)) * 16));
+            }
     };
 
     f32x16_t oacc[DB];
@@ -230,7 +265,8 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(
     for (int b = 0; b < DB; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[b][r] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;   // running max (raw score units) and sum
+    float m_run = 0.f, l_run = 0.f;   // running max (log2 units) and this lane's part of the sum
+    f32x16_t cm;                      // -m_run in every slot: the S^T accumulator's start
 
     auto mask_tile = [&](f32x16_t *s, int kv0) {
 #pragma unroll
@@ -249,150 +285,319 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
         return fmaxf(mx, xor32(mx));
     };
-
-    // O^T += V^T P^T.  Chunk c covers keys 16c..16c+15; B-operand slot 8g+j <-> key
-    // 16c + 8(j/4) + 4g + j%4, i.e. registers 8(c%2)+j of S^T block c/2.  The transposed-V
-    // buffer stores each 16-key group with key bits 2 and 3 swapped, so those 8 keys are the
-    // 16-byte chunk 2c+g of the row: one ds_read_b128 per operand.
-    auto pv = [&](auto st, uint32_t (*pk)[4]) {
-        const char *sv = vstage(st);
-        f16x8_t va[4][DB];
+    auto set_max = [&](float m) {
+        m_run = m;
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-            for (int b = 0; b < DB; ++b) {
-                const int row = 32 * b + l32;
-                va[c][b] = *reinterpret_cast<const f16x8_t *>(sv + row * 128 + (((2 * c + g) ^ G::vswz(row)) * 16));
-            }
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const f16x8_t pf = as_f16x8(make_uint4(pk[c][0], pk[c][1], pk[c][2], pk[c][3]));
-#pragma unroll
-            for (int b = 0; b < DB; ++b) oacc[b] = mfma32_f16(va[c][b], pf, oacc[b]);
-        }
+        for (int r = 0; r < 16; ++r) cm[r] = -m;
     };
-
-    const int nkv = (d.n + 63) / 64;
-    const bool ragged = (d.n & 63) != 0;
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
-    using I3 = std::integral_constant<int, 3>;
-    using I4 = std::integral_constant<int, 4>;
-    using I5 = std::integral_constant<int, 5>;
-    // prologue: K of tiles 0..2, V^T of tiles 0..1; wait for K 0, V^T 0 and K 1
-    issue_k(0, I0{});
-    issue_v(0, I0{});
-    issue_k(min(1, nkv - 1), I1{});
-    issue_v(min(1, nkv - 1), I1{});
-    issue_k(min(2, nkv - 1), I2{});
-    wait_vmem_n<G::KLOADS + G::VLOADS>();
-    bare_barrier();
-    // One key tile: issue K of tile t+3 and V^T of tile t+2 (into the stages of K t and V^T t-1,
-    // whose last readers were iterations t-1), S^T of tile t+1, softmax and P.V of tile t; then
-    // wait for this wave's copies of the previous iteration (K t+2, V^T t+1) and publish them.
-    // cur holds S^T of tile t and mx its row max; past the last tile the copies and S^T repeat
-    // the last tile and are ignored.
-    auto step = [&](int t, auto st, f32x16_t *cur, f32x16_t *next, float &mx) {
-        constexpr int S = decltype(st)::value;
-        using KQ = std::integral_constant<int, (S + 1) % 3>;   // K of tile t+1
-        using KD = std::integral_constant<int, S % 3>;         // K of tile t+3
-        using VP = std::integral_constant<int, S % 3>;         // V^T of tile t
-        using VD = std::integral_constant<int, (S + 2) % 3>;   // V^T of tile t+2
-        if (__ballot((mx - m_run) * c_log2 > kLazyRescale)) {   // wave-uniform, rare
-            const float m_new = fmaxf(m_run, mx);
-            const float alpha = fast_exp2((m_run - m_new) * c_log2);
-            m_run = m_new;
-            l_run *= alpha;
+    auto shift = [&](f32x16_t *sc, float dl) {
 #pragma unroll
-            for (int b = 0; b < DB; ++b)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
-        }
-        const float mc = m_run * c_log2;
-        issue_k(min(t + 3, nkv - 1), KD{});
-        issue_v(min(t + 2, nkv - 1), VD{});
-        qk(KQ{}, next);
-        uint32_t pk[4][4];
-        float ls0 = l_run, ls1 = 0.f;
+            for (int r = 0; r < 16; ++r) sc[kb][r] -= dl;
+    };
+    // exp2 of the shifted scores of one tile, packed to binary16 (round toward zero); returns
+    // this lane's sum of the packed weights (v_dot2c on the same binary16 values, so the
+    // numerator and the denominator use identical weights)
+    auto softmax = [&](const f32x16_t *cur, uint32_t (*pk)[4]) {
+        float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
         for (int c = 0; c < 4; ++c)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int kb = c >> 1, r = 8 * (c & 1) + 2 * j;
-                const float p0 = fast_exp2(__builtin_fmaf(cur[kb][r], c_log2, -mc));
-                const float p1 = fast_exp2(__builtin_fmaf(cur[kb][r + 1], c_log2, -mc));
-                pk[c][j] = pack_f16x2_rtz(p0, p1);
+                pk[c][j] = pack_f16x2_rtz(fast_exp2(cur[kb][r]), fast_exp2(cur[kb][r + 1]));
                 if (j & 1) ls1 = dot2_f16(pk[c][j], ls1);
                 else ls0 = dot2_f16(pk[c][j], ls0);
             }
-        l_run = ls0 + ls1;
-        pv(VP{}, pk);
-        if (ragged && t + 1 == nkv - 1) mask_tile(next, (t + 1) * 64);
-        mx = tile_max(next);
-        wait_vmem_n<G::KLOADS + G::VLOADS>();
+        return ls0 + ls1;
+    };
+    // S^T of one tile (accumulator started from -m, so the scores come out shifted) and
+    // O^T += V^T P^T of an earlier tile; P^T is already in the B-operand layout of the S^T
+    // accumulator (the key order inside each 16-key chunk is permuted identically on both
+    // operands).  The two products form four independent accumulation chains.
+    auto mfmas = [&](f32x16_t *sn, const uint32_t (*pk)[4], bool with_pv) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                if (i < KS) sn[kb] = mfma32_f16(kf[i][kb], qf[i], i == 0 ? cm : sn[kb]);
+            if (with_pv) {
+                const f16x8_t pf = as_f16x8(make_uint4(pk[i][0], pk[i][1], pk[i][2], pk[i][3]));
+#pragma unroll
+                for (int b = 0; b < DB; ++b) oacc[b] = mfma32_f16(vf[i][b], pf, oacc[b]);
+            }
+        }
+    };
+
+    // the image's ragged last tile, if it falls in this slice
+    const bool ragged = (d.n & 63) != 0 && t0 + nkv == nkv_all;
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    using Yes = std::true_type;
+    using No = std::false_type;
+    // prologue: K of tiles 0..2, V^T of tiles 0..1; wait for K 0 and K 1
+    issue_k(0, I0{});
+    issue_k(min(1, nkv - 1), I1{});
+    issue_v(0, I0{});
+    issue_k(min(2, nkv - 1), I2{});
+    issue_v(min(1, nkv - 1), I1{});
+    wait_vmem_n<G::KLOADS + 2 * G::VLOADS>();
+    bare_barrier();
+
+    f32x16_t sc0[2], sc1[2];   // S^T of the current tile and of the next one (alternating)
+    uint32_t pk0[4][4], pk1[4][4];   // binary16 weights of the current and previous tile
+    {
+        read_k(I0{});
+        const f32x16_t z = {};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) sc0[kb] = mfma32_f16(kf[kk][kb], qf[kk], kk == 0 ? z : sc0[kb]);
+    }
+    if (ragged && nkv == 1) mask_tile(sc0, t0 * 64);
+    set_max(tile_max(sc0));   // finite: key 0 of the tile is always inside the image
+    shift(sc0, m_run);
+
+    // Step t: issue K of tile t+3 and V^T of tile t+2 (into the stages of K t-1 and V^T t-2,
+    // last read in steps t-2 and t-1); read K of tile t+1 and V^T of tile t-1; then the MFMAs
+    // of S^T(t+1) and of P.V(t-1) interleaved with the softmax of tile t; then wait for this
+    // wave's copies up to K t+2 (V^T t too) and publish them.  Past the last tile the copies
+    // and S^T repeat the last tile and are ignored.
+    //
+    // Lazy rescale: the running max only moves when a weight would exceed 2^8.  Every weight
+    // is non-negative, so a lane's tile sum of at most 2^8 bounds each of its weights (an
+    // overflow shows up as 65504 or inf in the sum).  Otherwise (wave-uniform, rare: the
+    // first tiles of a row) the max moves up to the tile's row max, O (which already holds
+    // P.V(t-1)) and the sum are scaled by 2^-delta, the scores of tiles t and t+1 are shifted
+    // and the weights of tile t recomputed (all at most 1 now).
+    auto step = [&](int t, auto st, f32x16_t *sc, f32x16_t *sn, uint32_t (*pk)[4],
+                    uint32_t (*pkp)[4], auto pvt) {
+        constexpr int S = decltype(st)::value;
+        constexpr bool with_pv = decltype(pvt)::value;
+        using KQ = std::integral_constant<int, (S + 1) % 4>;   // K of tile t+1
+        using KD = std::integral_constant<int, (S + 3) % 4>;   // K of tile t+3
+        using VP = std::integral_constant<int, (S + 3) % 4>;   // V^T of tile t-1
+        using VD = std::integral_constant<int, (S + 2) % 4>;   // V^T of tile t+2
+        issue_k(min(t + 3, nkv - 1), KD{});
+        issue_v(min(t + 2, nkv - 1), VD{});
+        read_k(KQ{});
+        if (with_pv) read_v(VP{});
+        mfmas(sn, pkp, with_pv);
+        float ts = softmax(sc, pk);
+        // schedule: all LDS reads, a few VALU while they land, then 1 MFMA / 4 VALU pairs
+        __builtin_amdgcn_sched_group_barrier(0x100, with_pv ? KS * 2 + 4 * DB : KS * 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
+        if (__ballot(!(ts <= kLazySum))) {
+            const float dl = fmaxf(tile_max(sc), 0.f);
+            set_max(m_run + dl);
+            const float alpha = fast_exp2(-dl);
+            l_run *= alpha;
+#pragma unroll
+            for (int b = 0; b < DB; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
+            shift(sc, dl);
+            shift(sn, dl);
+            ts = softmax(sc, pk);
+        }
+        l_run += ts;
+        if (ragged && t + 1 == nkv - 1) mask_tile(sn, (t0 + t + 1) * 64);
+        wait_vmem_n<G::KLOADS + 2 * G::VLOADS>();
         bare_barrier();
     };
-    f32x16_t sa[2], sb[2];
-    qk(I0{}, sa);
-    if (ragged && nkv == 1) mask_tile(sa, 0);
-    float mx = tile_max(sa);
-    for (int t = 0; t < nkv; t += 6) {   // unrolled by six: rings of three, S^T buffers of two
-        step(t, I0{}, sa, sb, mx);
-        if (t + 1 < nkv) step(t + 1, I1{}, sb, sa, mx);
-        if (t + 2 < nkv) step(t + 2, I2{}, sa, sb, mx);
-        if (t + 3 < nkv) step(t + 3, I3{}, sb, sa, mx);
-        if (t + 4 < nkv) step(t + 4, I4{}, sa, sb, mx);
-        if (t + 5 < nkv) step(t + 5, I5{}, sb, sa, mx);
+    // unrolled by four: rings of four, S^T and weight buffers of two
+    step(0, I0{}, sc0, sc1, pk0, pk1, No{});
+    for (int t = 1; t < nkv; t += 4) {
+        step(t, I1{}, sc1, sc0, pk1, pk0, Yes{});
+        if (t + 1 < nkv) step(t + 1, I2{}, sc0, sc1, pk0, pk1, Yes{});
+        if (t + 2 < nkv) step(t + 2, I3{}, sc1, sc0, pk1, pk0, Yes{});
+        if (t + 3 < nkv) step(t + 3, I0{}, sc0, sc1, pk0, pk1, Yes{});
+    }
+    // P.V of the last tile (its V^T was waited for at the end of the last step)
+    {
+        const int tl = nkv - 1;
+        uint32_t(*pkl)[4] = (tl & 1) ? pk1 : pk0;
+        switch (tl & 3) {
+        case 0: read_v(I0{}); break;
+        case 1: read_v(I1{}); break;
+        case 2: read_v(I2{}); break;
+        default: read_v(I3{}); break;
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const f16x8_t pf = as_f16x8(make_uint4(pkl[c][0], pkl[c][1], pkl[c][2], pkl[c][3]));
+#pragma unroll
+            for (int b = 0; b < DB; ++b) oacc[b] = mfma32_f16(vf[c][b], pf, oacc[b]);
+        }
     }
 
     wait_vmem();
     const float l_tot = l_run + xor32(l_run);
     const float inv = 1.f / l_tot;
     if (q < d.n) {
-        bf16_t *orow = o + ((int64_t)d.patch_off + q) * D + head * HD;
+        const int64_t row = (int64_t)d.patch_off + q;
+        if (nsplit == 1) {
+            bf16_t *orow = o + row * D + head * HD;
 #pragma unroll
-        for (int b = 0; b < DB; ++b)
+            for (int b = 0; b < DB; ++b)
 #pragma unroll
-            for (int grp = 0; grp < 4; ++grp) {
-                const int dd = 32 * b + 8 * grp + 4 * g;
-                if (dd < HD) {
-                    const float a0 = oacc[b][4 * grp] * inv, a1 = oacc[b][4 * grp + 1] * inv,
-                                a2 = oacc[b][4 * grp + 2] * inv, a3 = oacc[b][4 * grp + 3] * inv;
-                    *reinterpret_cast<uint2 *>(orow + dd) =
-                        make_uint2(pack_bf16x2(a0, a1), pack_bf16x2(a2, a3));
+                for (int grp = 0; grp < 4; ++grp) {
+                    const int dd = 32 * b + 8 * grp + 4 * g;
+                    if (dd < HD) {
+                        const float a0 = oacc[b][4 * grp] * inv, a1 = oacc[b][4 * grp + 1] * inv,
+                                    a2 = oacc[b][4 * grp + 2] * inv, a3 = oacc[b][4 * grp + 3] * inv;
+                        *reinterpret_cast<uint2 *>(orow + dd) =
+                            make_uint2(pack_bf16x2(a0, a1), pack_bf16x2(a2, a3));
+                    }
                 }
-            }
+        } else {   // this slice's normalised output (binary16) and its (max, sum)
+            uint16_t *prow = part_o + ((int64_t)split * nrows + row) * D + head * HD;
+#pragma unroll
+            for (int b = 0; b < DB; ++b)
+#pragma unroll
+                for (int grp = 0; grp < 4; ++grp) {
+                    const int dd = 32 * b + 8 * grp + 4 * g;
+                    if (dd < HD) {
+                        uint32_t h[2];
+#pragma unroll
+                        for (int e = 0; e < 2; ++e) {
+                            const float a = fminf(fmaxf(oacc[b][4 * grp + 2 * e] * inv, -65504.f), 65504.f);
+                            const float c = fminf(fmaxf(oacc[b][4 * grp + 2 * e + 1] * inv, -65504.f), 65504.f);
+                            h[e] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
+                                   ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)c) << 16);
+                        }
+                        *reinterpret_cast<uint2 *>(prow + dd) = make_uint2(h[0], h[1]);
+                    }
+                }
+            if (g == 0) part_ml[((int64_t)split * H + head) * nrows + row] = make_float2(m_run, l_tot);
+        }
     }
+}
+
+// Merge of the key slices of every (row, head): with weights w_s = l_s 2^(m_s - M), M the
+// largest slice max, out = sum_s w_s o_s / sum_s w_s, rounded once to bf16.  One thread per
+// 8 consecutive columns of a row (inside one head).  Empty slices carry l = 0, o = 0.
+__global__ __launch_bounds__(256) void attention_merge_kernel(
+    const uint16_t *__restrict__ part_o, const float2 *__restrict__ part_ml, int nsplit,
+    int64_t nrows, int D, int H, int hd, bf16_t *__restrict__ o)
+{
+    const int chunks = D / 8;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= nrows * chunks) return;
+    const int64_t row = idx / chunks;
+    const int col = (int)(idx - row * chunks) * 8, head = col / hd;
+    float mmax = -INFINITY;
+    for (int sp = 0; sp < nsplit; ++sp) mmax = fmaxf(mmax, part_ml[((int64_t)sp * H + head) * nrows + row].x);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, wsum = 0.f;
+    for (int sp = 0; sp < nsplit; ++sp) {
+        const float2 ml = part_ml[((int64_t)sp * H + head) * nrows + row];
+        const float w = ml.y == 0.f ? 0.f : ml.y * fast_exp2(ml.x - mmax);
+        const uint4 u = *reinterpret_cast<const uint4 *>(part_o + ((int64_t)sp * nrows + row) * D + col);
+        const uint32_t ww[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint16_t hb = (uint16_t)((ww[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
+            acc[e] += w * (float)__builtin_bit_cast(_Float16, hb);
+        }
+        wsum += w;
+    }
+    const float inv = 1.f / wsum;
+    *reinterpret_cast<uint4 *>(o + row * D + col) =
+        make_uint4(pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+                   pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv));
 }
 
 template <int HD>
 hipError_t run_attention(const bf16_t *qkv, const bf16_t *vt, int64_t ldv, bf16_t *o,
                          const RowTile *work, int n_work, const ImgDesc *imgs, int D, int H,
-                         hipStream_t s)
+                         int64_t nrows, const AttnSplit &sp, hipStream_t s)
 {
-    const int64_t total = (int64_t)n_work * H;
+    const int64_t total = (int64_t)n_work * H * sp.n;
     const int grid = (int)(ceil_div(total, 8) * 8);
     const float c_log2 = (float)(1.4426950408889634 / sqrt((double)HD));
     hipLaunchKernelGGL(attention_kernel<HD>, dim3(grid), dim3(256), 0, s, qkv, vt, ldv, o, work,
-                       n_work, imgs, D, H, c_log2);
+                       n_work, imgs, D, H, c_log2, sp.n, sp.part_o, (float2 *)sp.part_ml, nrows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || sp.n == 1) return e;
+    const int64_t threads = nrows * (D / 8);
+    hipLaunchKernelGGL(attention_merge_kernel, dim3((unsigned)ceil_div(threads, 256)), dim3(256), 0, s,
+                       sp.part_o, (const float2 *)sp.part_ml, sp.n, nrows, D, H, HD, o);
     return hipGetLastError();
+}
+
+template <int HD>
+int blocks_per_cu()
+{
+    static int nb = 0;
+    if (nb == 0) {
+        int v = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, attention_kernel<HD>, 256, 0) != hipSuccess || v < 1) {
+            (void)hipGetLastError();
+            v = 1;
+        }
+        nb = v;
+    }
+    return nb;
 }
 
 }  // namespace
 
 int attention_q_tile() { return 128; }
 
+size_t attention_split_bytes(int64_t nrows, int D, int H, int nsplit)
+{
+    if (nsplit <= 1) return 0;
+    return (size_t)nsplit * nrows * ((size_t)D * sizeof(uint16_t) + (size_t)H * sizeof(float2));
+}
+
+// Key slices per (query tile, head).  A CU runs its attention blocks at about the same total
+// rate whether it holds one or two of them, so slicing only pays when the batch cannot fill
+// the GPU: fewer than half as many (query tile, head) blocks as block slots.  Then the slices
+// multiply the blocks up to the slot count (at most 4, at least two key tiles per slice of the
+// largest image); the merge costs one pass over binary16 partials.
+int attention_split(const ImgDesc *imgs, int n_img, int D, int H)
+{
+    if (n_img <= 0 || H <= 0) return 1;
+    int per_cu = 1;
+    switch (D / H) {
+    case 16: per_cu = blocks_per_cu<16>(); break;
+    case 32: per_cu = blocks_per_cu<32>(); break;
+    case 64: per_cu = blocks_per_cu<64>(); break;
+    case 128: per_cu = blocks_per_cu<128>(); break;
+    default: return 1;
+    }
+    const int64_t slots = (int64_t)cu_count() * per_cu;
+    const int qt = attention_q_tile();
+    int64_t blocks = 0;
+    int max_nkv = 0;
+    for (int i = 0; i < n_img; ++i) {
+        blocks += (int64_t)ceil_div(imgs[i].n, qt) * H;
+        max_nkv = std::max(max_nkv, (int)ceil_div(imgs[i].n, 64));
+    }
+    if (blocks == 0 || 2 * blocks > slots) return 1;
+    const int64_t by_slots = slots / blocks;
+    return (int)std::max<int64_t>(1, std::min<int64_t>({4, by_slots, max_nkv / 2}));
+}
+
 hipError_t launch_attention(const bf16_t *qkv, const bf16_t *vt, int64_t ldv, bf16_t *o,
                             const RowTile *work, int n_work, const ImgDesc *imgs, int D, int H,
-                            hipStream_t s)
+                            int64_t nrows, const AttnSplit &sp, hipStream_t s)
 {
     if (n_work <= 0) return hipSuccess;
+    if (sp.n < 1 || sp.n > 4 || (sp.n > 1 && (!sp.part_o || !sp.part_ml))) return hipErrorInvalidValue;
     switch (D / H) {
-    case 16: return run_attention<16>(qkv, vt, ldv, o, work, n_work, imgs, D, H, s);
-    case 32: return run_attention<32>(qkv, vt, ldv, o, work, n_work, imgs, D, H, s);
-    case 64: return run_attention<64>(qkv, vt, ldv, o, work, n_work, imgs, D, H, s);
-    case 128: return run_attention<128>(qkv, vt, ldv, o, work, n_work, imgs, D, H, s);
+    case 16: return run_attention<16>(qkv, vt, ldv, o, work, n_work, imgs, D, H, nrows, sp, s);
+    case 32: return run_attention<32>(qkv, vt, ldv, o, work, n_work, imgs, D, H, nrows, sp, s);
+    case 64: return run_attention<64>(qkv, vt, ldv, o, work, n_work, imgs, D, H, nrows, sp, s);
+    case 128: return run_attention<128>(qkv, vt, ldv, o, work, n_work, imgs, D, H, nrows, sp, s);
     default: return hipErrorInvalidValue;
     }
 }

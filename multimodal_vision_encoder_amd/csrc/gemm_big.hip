@@ -427,20 +427,6 @@ __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(EP ep, int tiles
     ep.store((int64_t)tm * BM + r, tn * BN + cq * 4, v);
 }
 
-int cu_count()
-{
-    static int n = 0;
-    if (n == 0) {
-        int dev = 0, v = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-            n = v;
-        else
-            n = 256;
-    }
-    return n;
-}
-
 // Split plan of a BM x BN launch (one block per CU).  With T tiles and P CUs, a last round of
 // r = T mod P tiles leaves P - r CUs idle for a whole tile time; cutting those r tiles into s
 // K slices shortens that round to about 1/s of a tile time, at the cost of writing and
@@ -519,6 +505,21 @@ hipError_t dispatch(SRC src, const bf16_t *W, int64_t M, int N, int K, const bf1
 }
 
 }  // namespace
+
+int cu_count()
+{
+    static int n = 0;
+    if (n == 0) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            n = v;
+        else
+            n = 256;
+    }
+    return n;
+}
+
 
 size_t gemm_workspace_max_bytes() { return (size_t)cu_count() * 256 * 128 * 4; }
 

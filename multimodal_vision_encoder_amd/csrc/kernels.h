@@ -47,10 +47,23 @@ hipError_t launch_rope(bf16_t *qkv, bf16_t *vt, int64_t ldv, const RowTile *tile
                        const ImgDesc *imgs, int D, int H, const float *cos_t,
                        const float *sin_t, hipStream_t s);
 
-// Block-diagonal flash attention; one block per (attention_q_tile() queries, head).
+// Block-diagonal flash attention; one block per (attention_q_tile() queries, head, key
+// slice).  With n > 1 key slices each slice writes its normalised binary16 output to
+// part_o [n][nrows][D] and (max, sum) to part_ml [n][H][nrows] (float pairs), and a merge
+// kernel writes o; attention_split_bytes() sizes that scratch.
+struct AttnSplit {
+    int n;
+    uint16_t *part_o;
+    float *part_ml;
+};
+int attention_split(const ImgDesc *h_imgs, int n_img, int D, int H);
+size_t attention_split_bytes(int64_t nrows, int D, int H, int nsplit);
 hipError_t launch_attention(const bf16_t *qkv, const bf16_t *vt, int64_t ldv, bf16_t *o,
                             const RowTile *work, int n_work, const ImgDesc *imgs, int D, int H,
-                            hipStream_t s);
+                            int64_t nrows, const AttnSplit &sp, hipStream_t s);
+
+// Compute units of the current device.
+int cu_count();
 
 // embeds[rows[t]] = bf16(src[t]) for rows[t] >= 0.
 hipError_t launch_overlay(uint16_t *embeds, const float *src, const int32_t *rows, int64_t n_rows,

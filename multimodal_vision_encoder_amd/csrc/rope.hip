@@ -1,5 +1,5 @@
-// 2D rotary position embedding on q and k, in place in the packed qkv rows, plus a
-// transposed copy of v for the attention kernel.
+// 2D rotary position embedding on q and k, in place in the packed qkv rows (k converted to
+// binary16), plus a transposed binary16 copy of v for the attention kernel.
 //
 // [Z] "Step 3": the angle vector of patch (h, w) is blocked by axis,
 // theta = [h f_0 .. h f_{Q-1}, w f_0 .. w f_{Q-1}] with Q = hd/4 (not interleaved), and the
@@ -14,10 +14,11 @@
 // key p with bits 2 and 3 swapped.  Columns of the tile past the image's last patch are
 // written as zeros, so every column the attention kernel reads is defined.  HBM-bound.
 //
-// V^T is stored as IEEE binary16, the operand type of the attention's P.V product: every
-// bf16 value of magnitude 2^-14 .. 65504 converts exactly (8 significant bits fit in 11),
-// smaller ones keep an absolute error below 2^-25, larger ones saturate to +-65504 (NaN
-// stays NaN).
+// The rotated q is stored as bf16.  The rotated k is rounded to bf16 like q and then stored
+// as IEEE binary16, the operand type of the attention's score product; V^T is binary16 too
+// (the operand type of P.V).  Every bf16 value of magnitude 2^-14 .. 65504 converts exactly
+// (8 significant bits fit in 11), smaller ones keep an absolute error below 2^-25, larger
+// ones saturate to +-65504 (NaN stays NaN).
 #include "kernels.h"
 
 namespace {
@@ -57,6 +58,18 @@ __device__ __forceinline__ uint4 pack8(const float *f)
                       pack_bf16x2(f[6], f[7]));
 }
 
+// Eight values rounded to bf16, then stored as binary16 bit patterns.
+__device__ __forceinline__ uint4 pack8_f16_of_bf16(const float *f)
+{
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t b = pack_bf16x2(f[2 * j], f[2 * j + 1]);
+        w[j] = (uint32_t)bf16_to_f16_sat(b & 0xFFFFu) | ((uint32_t)bf16_to_f16_sat(b >> 16) << 16);
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 template <int HD>
 __global__ __launch_bounds__(256) void rope_kernel(bf16_t *__restrict__ qkv, bf16_t *__restrict__ vt,
                                                    int64_t ldv, const RowTile *__restrict__ tiles,
@@ -92,8 +105,13 @@ __global__ __launch_bounds__(256) void rope_kernel(bf16_t *__restrict__ qkv, bf1
             const int pos = i < Q4 ? hp : wp;
             rotate(a[e], b[e], cos_t[pos * Q4 + j], sin_t[pos * Q4 + j], na[e], nb[e]);
         }
-        *reinterpret_cast<uint4 *>(v) = pack8(na);
-        *reinterpret_cast<uint4 *>(v + HALF) = pack8(nb);
+        if (part == 0) {   // q
+            *reinterpret_cast<uint4 *>(v) = pack8(na);
+            *reinterpret_cast<uint4 *>(v + HALF) = pack8(nb);
+        } else {           // k
+            *reinterpret_cast<uint4 *>(v) = pack8_f16_of_bf16(na);
+            *reinterpret_cast<uint4 *>(v + HALF) = pack8_f16_of_bf16(nb);
+        }
     }
 
     // v: 16-byte row chunks -> binary16, LDS transposed (sv[d][key]) -> 16-byte stores of 8 columns

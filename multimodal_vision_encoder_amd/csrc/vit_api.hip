@@ -47,6 +47,9 @@ struct vit_ctx {
     // workspace
     float *d_gemm_ws = nullptr;   // split-K partial tiles of the GEMMs
     size_t gemm_ws_bytes = 0;
+    char *d_attn_ws = nullptr;    // key-slice partials of the attention
+    size_t attn_ws_bytes = 0;
+    int attn_split_fixed = 0;     // 0: chosen per batch; 1..4: fixed key slices
     int64_t cap_patches = 0, cap_vt_cols = 0, reserve_cap = 0;
     bf16_t *x = nullptr, *ln = nullptr, *qkv = nullptr, *vt = nullptr, *o = nullptr,
            *delta = nullptr, *h1 = nullptr, *patches = nullptr;
@@ -187,6 +190,36 @@ GemmWorkspace gemm_ws(vit_ctx *c)
         }
     }
     return GemmWorkspace{c->d_gemm_ws, c->d_gemm_ws ? c->gemm_ws_bytes : 0};
+}
+
+// Attention key slices for this batch and their scratch (grown on demand; without it the
+// attention runs unsplit, which gives results within the same bounds).
+AttnSplit attn_split(vit_ctx *c, const Plan &p)
+{
+    AttnSplit sp{1, nullptr, nullptr};
+    const int ns = c->attn_split_fixed > 0 ? c->attn_split_fixed
+                                           : attention_split(p.imgs.data(), (int)p.imgs.size(), c->D, c->H);
+    if (ns <= 1) return sp;
+    const size_t need = attention_split_bytes(p.N, c->D, c->H, ns);
+    if (need > c->attn_ws_bytes) {
+        if (hipDeviceSynchronize() != hipSuccess) {
+            (void)hipGetLastError();
+            return sp;
+        }
+        if (c->d_attn_ws) (void)hipFree(c->d_attn_ws);
+        c->d_attn_ws = nullptr;
+        c->attn_ws_bytes = 0;
+        if (hipMalloc((void **)&c->d_attn_ws, need) != hipSuccess) {
+            (void)hipGetLastError();
+            c->d_attn_ws = nullptr;
+            return sp;
+        }
+        c->attn_ws_bytes = need;
+    }
+    sp.n = ns;
+    sp.part_o = (uint16_t *)c->d_attn_ws;
+    sp.part_ml = (float *)(c->d_attn_ws + (size_t)ns * p.N * c->D * sizeof(uint16_t));
+    return sp;
 }
 
 vit_status ensure_workspace(vit_ctx *c, int64_t N, int64_t vt_cols)
@@ -348,6 +381,7 @@ vit_status encode_impl(vit_ctx *c, const uint8_t *px, const vit_grid *grids, int
     st = ensure_workspace(c, p.N, p.vt_cols);
     if (st != VIT_OK) return st;
     const GemmWorkspace gws = gemm_ws(c);
+    const AttnSplit asp = attn_split(c, p);
     DevPlan dp{};
     st = stage_plan(c, p, s, dp);
     if (st != VIT_OK) return st;
@@ -374,7 +408,7 @@ vit_status encode_impl(vit_ctx *c, const uint8_t *px, const vit_grid *grids, int
                               c->d_cos, c->d_sin, s));
         if (stop == VIT_DUMP_QKV && arg == l) return copy_out(c->qkv);
         TLAUNCH(c, VIT_STEP_ATTENTION, s, launch_attention(c->qkv, c->vt, p.vt_cols, c->o, dp.attn, (int)p.attn.size(),
-                                   dp.imgs, D, H, s));
+                                   dp.imgs, D, H, p.N, asp, s));
         if (stop == VIT_DUMP_ATTN && arg == l) return copy_out(c->o);
         TLAUNCH(c, VIT_STEP_OUT_PROJ, s, launch_linear(c->o, p.N, D, w.wo, w.bo, D, ACT_NONE, false, c->delta, &gws, s));
         TLAUNCH(c, VIT_STEP_LAYERNORM, s, launch_layernorm(c->x, c->delta, c->x, p.N, D, w.ln2g, w.ln2b, c->cfg.ln_eps,
@@ -404,7 +438,8 @@ void destroy(vit_ctx *c)
     if (!c) return;
     (void)hipDeviceSynchronize();
     free_workspace(c);
-    void *bufs[] = {c->d_blob, c->d_wpe, c->d_wproj, c->d_cos, c->d_sin, c->d_meta, c->d_zero, c->d_gemm_ws};
+    void *bufs[] = {c->d_blob, c->d_wpe, c->d_wproj, c->d_cos, c->d_sin, c->d_meta, c->d_zero, c->d_gemm_ws,
+                    c->d_attn_ws};
     for (void *b : bufs)
         if (b) (void)hipFree(b);
     if (c->h_stage) (void)hipHostFree(c->h_stage);
@@ -758,10 +793,19 @@ vit_status vit_op_attention(vit_ctx *ctx, const uint16_t *d_qkv, const uint16_t 
     if (st != VIT_OK) return st;
     if (p.N == 0) return VIT_OK;
     if (!d_qkv || !d_vt || !d_o) return fail(ctx, VIT_E_ARG, "NULL pointer");
+    const AttnSplit asp = attn_split(ctx, p);
     DevPlan dp{};
     if ((st = stage_plan(ctx, p, (hipStream_t)stream, dp)) != VIT_OK) return st;
     LAUNCH(ctx, launch_attention(d_qkv, d_vt, p.vt_cols, d_o, dp.attn, (int)p.attn.size(), dp.imgs,
-                                 ctx->D, ctx->H, (hipStream_t)stream));
+                                 ctx->D, ctx->H, p.N, asp, (hipStream_t)stream));
+    return VIT_OK;
+}
+
+vit_status vit_set_attention_split(vit_ctx *ctx, int32_t n)
+{
+    if (!ctx) return fail(nullptr, VIT_E_ARG, "ctx is NULL");
+    if (n < 0 || n > 4) return fail(ctx, VIT_E_ARG, "attention key slices must be 0 (automatic) or 1..4");
+    ctx->attn_split_fixed = n;
     return VIT_OK;
 }
 

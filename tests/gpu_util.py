@@ -23,6 +23,21 @@ def from_dev_bf16(t) -> np.ndarray:
     return synth.bf16_bits_to_f32(bits).reshape(t.shape)
 
 
+def qkv_after_rope(t, D: int) -> np.ndarray:
+    """qkv rows after RoPE -> float32 numpy: q and v columns are bf16, the k columns
+    (D .. 2D-1) hold binary16 bit patterns (the attention's score operand type)."""
+    import torch
+    bits = t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16).reshape(t.shape)
+    out = synth.bf16_bits_to_f32(bits).reshape(t.shape)
+    out[:, D:2 * D] = bits[:, D:2 * D].view(np.float16).astype(np.float32)
+    return out
+
+
+def f16_of(x: np.ndarray) -> np.ndarray:
+    """float32 values -> binary16 (round to nearest even, saturating at +-65504) -> float32."""
+    return np.clip(np.asarray(x, np.float32), -65504, 65504).astype(np.float16).astype(np.float32)
+
+
 def bf16_bits_of(x: np.ndarray) -> np.ndarray:
     """float32 values that are already bf16 -> their bits."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)

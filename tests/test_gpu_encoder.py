@@ -8,8 +8,8 @@ import pytest
 import multimodal_vision_encoder_amd as vit
 import oracle
 import synth
-from tests.gpu_util import (assert_bf16_close, assert_projector_gate, from_dev_bf16, rel_l2,
-                            require_gpu)
+from tests.gpu_util import (assert_bf16_close, assert_projector_gate, from_dev_bf16,
+                            qkv_after_rope, rel_l2, require_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -151,7 +151,8 @@ def test_one_layer_end_to_end(perturbed):
                       atol=1e-6, what="embed")
     for name, b, arg in (("qkv0", vit.DUMP_QKV, 0), ("attn0", vit.DUMP_ATTN, 0),
                          ("layer0", vit.DUMP_LAYER, 0), ("final_norm", vit.DUMP_FINAL_NORM, 0)):
-        g = from_dev_bf16(enc.dump(b, d_px, wl.grids, arg=arg))
+        t = enc.dump(b, d_px, wl.grids, arg=arg)
+        g = qkv_after_rope(t, wl.cfg.hidden) if b == vit.DUMP_QKV else from_dev_bf16(t)
         assert rel_l2(g, dumps[name]) < 1e-2, name
     assert_projector_gate(got, want, "one layer")
 

@@ -7,8 +7,8 @@ import pytest
 import multimodal_vision_encoder_amd as vit
 import oracle
 import synth
-from tests.gpu_util import (assert_bf16_close, bf16_bits_of, from_dev_bf16, require_gpu,
-                            seeded_bf16, to_dev_bf16, rel_l2)
+from tests.gpu_util import (assert_bf16_close, bf16_bits_of, f16_of, from_dev_bf16,
+                            qkv_after_rope, require_gpu, seeded_bf16, to_dev_bf16, rel_l2)
 
 pytestmark = pytest.mark.gpu
 
@@ -167,8 +167,12 @@ def test_rope_exact(name, grids):
     vt = enc.op_rope(d, grids)
     torch.cuda.synchronize()
     want = _oracle_rope(f32(qkv), grids, cfg)
-    got = from_dev_bf16(d)
-    assert np.array_equal(got, want)
+    D = cfg.hidden
+    got = qkv_after_rope(d, D)
+    # q and v bf16 as the oracle rounds them; k is the oracle's bf16 value stored as binary16
+    assert np.array_equal(got[:, :D], want[:, :D])
+    assert np.array_equal(got[:, 2 * D:], want[:, 2 * D:])
+    assert np.array_equal(got[:, D:2 * D], f16_of(want[:, D:2 * D]))
     # v transposed per head as binary16 (round to nearest even, saturating at 65504: exact
     # except below 2^-14, where binary16 is subnormal), each image at its own 64-aligned
     # column block, zero padding; inside each 16-column group, column p holds key p with
@@ -200,8 +204,10 @@ def _attention_check(got, qkv_rot, grids, cfg, rows_per_image=None):
             want = oracle.attention(sl, cfg.hidden, cfg.heads, rows=(r, r + 1))[r]
             g = got[off + r]
             vmax = np.abs(sl[:, 2 * cfg.hidden:]).max()
-            # P enters P.V as binary16 rounded toward zero (below 2^-10 relative per weight,
-            # plus 2^-24 absolute for subnormal weights), plus the output rounding on both sides
+            # the scores use q * log2(e)/sqrt(hd) rounded to binary16 (2^-11 relative per
+            # element); P enters P.V as binary16 rounded toward zero (below 2^-10 relative per
+            # weight, plus 2^-24 absolute for subnormal weights); plus the output rounding on
+            # both sides
             tol = 2.0 ** -8 * vmax + 2.0 ** -7 * np.abs(want)
             assert np.all(np.abs(g - want) <= tol), (gh, gw, r, np.abs(g - want).max())
         off += n
@@ -270,6 +276,32 @@ def test_attention_full_size_sampled(grids):
     torch.cuda.synchronize()
     rot = _oracle_rope(f32(qkv), grids, cfg)
     _attention_check(o, rot, grids, cfg, rows_per_image=lambda n: [0, 1, 127, 128, n // 3, n - 1])
+
+
+@pytest.mark.parametrize("grids", [[(96, 96)], [(54, 63)], [(13, 21), (1, 2), (3, 3)]],
+                         ids=["v41_1024", "v4_384", "ragged_small"])
+def test_attention_key_slices(grids):
+    """Every fixed number of key slices (1..4; short images leave some slices empty) meets the
+    oracle bound on sampled rows, and the automatic choice is bitwise one of them."""
+    torch = require_gpu()
+    enc, cfg, _ = encoder("v41_1layer")
+    qkv = _qkv_for(grids, cfg.hidden, 112)
+    outs = {}
+    try:
+        for n in (1, 2, 3, 4, 0):
+            enc.set_attention_split(n)
+            d = to_dev_bf16(qkv)
+            vt = enc.op_rope(d, grids)
+            outs[n] = from_dev_bf16(enc.op_attention(d, vt, grids))
+        torch.cuda.synchronize()
+        with pytest.raises(vit.VitError):
+            enc.set_attention_split(5)
+    finally:
+        enc.set_attention_split(0)
+    rot = _oracle_rope(f32(qkv), grids, cfg)
+    for n in (1, 2, 3, 4):
+        _attention_check(outs[n], rot, grids, cfg, rows_per_image=lambda m: [r for r in (0, 1, 63, 64, m // 2, m - 1) if r < m])
+    assert any(np.array_equal(outs[0], outs[n]) for n in (1, 2, 3, 4))
 
 
 def test_attention_packed16_sampled():

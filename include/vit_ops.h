@@ -66,13 +66,14 @@ vit_status vit_op_attention(vit_ctx *ctx, const uint16_t *d_qkv, const uint16_t 
                             void *stream);
 
 /* Key slices of the attention (vit_encode and vit_op_attention).  With n slices the keys of
- * every (query tile, head) are cut into n contiguous ranges processed by separate blocks; each
+ * a (query tile, head) are cut into n contiguous ranges processed by separate blocks; each
  * range's output, normalised by its own softmax sum, is kept as binary16 with its (max, sum),
  * and a merge weights the ranges by sum * 2^(max - overall max) and rounds once to bf16.  The
  * results agree with the unsliced attention within the same error bounds (not bitwise).
- * n = 0 (the default) picks n per batch from a makespan model of the GPU's block slots (more
- * slices when a few large images leave part of the GPU idle in the last round); 1..4 fixes it.
- * VIT_E_ARG for other values. */
+ * n = 0 (the default) cuts only the (query tile, head) items that would form a last, partial
+ * round of blocks on the GPU, into up to 4 slices each, so that round occupies every block
+ * slot for a fraction of its length; the other items run whole.  n = 1 never cuts; n = 2..4
+ * cuts every item into n slices.  VIT_E_ARG for other values. */
 vit_status vit_set_attention_split(vit_ctx *ctx, int32_t n);
 
 /* 3x3 merge + projector ([Z] "Step 4": right/bottom zero padding on the 2D grid,

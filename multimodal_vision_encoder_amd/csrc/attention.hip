@@ -136,8 +136,7 @@ template <int HD>
 __global__ __launch_bounds__(256, 2) void attention_kernel(
     const bf16_t *__restrict__ qkv, const bf16_t *__restrict__ vt, int64_t ldv,
     bf16_t *__restrict__ o, const RowTile *__restrict__ work, int n_work,
-    const ImgDesc *__restrict__ imgs, int D, int H, float c_log2, int nsplit,
-    uint16_t *__restrict__ part_o, float2 *__restrict__ part_ml, int64_t nrows)
+    const ImgDesc *__restrict__ imgs, int D, int H, float c_log2, AttnSplit pl)
 {
     using G = AttnGeom<HD>;
     constexpr int HDP = G::HDP, KCH = G::KCH, KS = HDP / 16, DB = HDP / 32;
@@ -151,16 +150,30 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(
         return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char *)p;
     };
 
-    // block -> (head, query tile, key slice); the slices of one tile are neighbours
-    const int Lx = xcd_remap(blockIdx.x, gridDim.x);
-    if (Lx >= n_work * H * nsplit) return;
-    const int split = Lx % nsplit, L = Lx / nsplit;
+    // block -> item (head, query tile) and key slice.  Blocks are dealt to the XCDs in turn, so
+    // XCD x runs blocks x, x + 8, ... in that order: they take the x-th group of per_xcd
+    // consecutive items (mostly one head: its K and V^T stay in that XCD's L2), first the
+    // `full` whole items, then the key slices of the rest (neighbours for one item).
+    const int xg = blockIdx.x & 7, jb = blockIdx.x >> 3;
+    int L, split = 0, nsplit = 1, tix = 0;
+    if (jb < pl.full) {
+        L = xg * pl.per_xcd + jb;
+    } else {
+        const int u = jb - pl.full, tail = pl.per_xcd - pl.full;
+        nsplit = pl.slices;
+        split = u % nsplit;
+        L = xg * pl.per_xcd + pl.full + u / nsplit;
+        tix = xg * tail + u / nsplit;
+    }
+    if (L >= pl.items) return;
     const int head = L / n_work, wi = L - head * n_work;
     const RowTile wt = work[wi];
     const ImgDesc d = imgs[wt.img];
     // key tiles [t0, t0 + nkv) of the image's nkv_all
     const int nkv_all = (d.n + 63) / 64, per = (nkv_all + nsplit - 1) / nsplit;
     const int t0 = split * per, nkv = min(nkv_all, t0 + per) - t0;
+    // this slice's rows of the partial buffers: [tail item][slice][query row of the tile]
+    const int64_t prow0 = ((int64_t)tix * nsplit + split) * (4 * 32);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, g = lane >> 5;
@@ -172,10 +185,10 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(
     const int q = wt.r0 + wave * 32 + l32;   // this lane's query (local row)
     if (nkv <= 0) {   // empty key slice (image shorter than the slices): weight zero in the merge
         if (q < d.n) {
-            const int64_t row = (int64_t)d.patch_off + q;
-            uint16_t *prow = part_o + ((int64_t)split * nrows + row) * D + head * HD;
+            const int64_t pr = prow0 + wave * 32 + l32;
+            uint16_t *prow = pl.part_o + pr * HD;
             for (int dd = 4 * g; dd < HD; dd += 8) *reinterpret_cast<uint2 *>(prow + dd) = make_uint2(0, 0);
-            if (g == 0) part_ml[((int64_t)split * H + head) * nrows + row] = make_float2(-INFINITY, 0.f);
+            if (g == 0) reinterpret_cast<float2 *>(pl.part_ml)[pr] = make_float2(-INFINITY, 0.f);
         }
         return;
     }
@@ -459,7 +472,8 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(
                     }
                 }
         } else {   // this slice's normalised output (binary16) and its (max, sum)
-            uint16_t *prow = part_o + ((int64_t)split * nrows + row) * D + head * HD;
+            const int64_t pr = prow0 + wave * 32 + l32;
+            uint16_t *prow = pl.part_o + pr * HD;
 #pragma unroll
             for (int b = 0; b < DB; ++b)
 #pragma unroll
@@ -477,30 +491,41 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(
                         *reinterpret_cast<uint2 *>(prow + dd) = make_uint2(h[0], h[1]);
                     }
                 }
-            if (g == 0) part_ml[((int64_t)split * H + head) * nrows + row] = make_float2(m_run, l_tot);
+            if (g == 0) reinterpret_cast<float2 *>(pl.part_ml)[pr] = make_float2(m_run, l_tot);
         }
     }
 }
 
-// Merge of the key slices of every (row, head): with weights w_s = l_s 2^(m_s - M), M the
+// Merge of the key slices of the split items: with weights w_s = l_s 2^(m_s - M), M the
 // largest slice max, out = sum_s w_s o_s / sum_s w_s, rounded once to bf16.  One thread per
-// 8 consecutive columns of a row (inside one head).  Empty slices carry l = 0, o = 0.
+// 8 consecutive columns of one query row of one split item (one head).  Empty slices carry
+// l = 0, o = 0.
 __global__ __launch_bounds__(256) void attention_merge_kernel(
-    const uint16_t *__restrict__ part_o, const float2 *__restrict__ part_ml, int nsplit,
-    int64_t nrows, int D, int H, int hd, bf16_t *__restrict__ o)
+    AttnSplit pl, const RowTile *__restrict__ work, int n_work, const ImgDesc *__restrict__ imgs,
+    int D, int hd, bf16_t *__restrict__ o)
 {
-    const int chunks = D / 8;
+    constexpr int QT = 4 * 32;
+    const int chunks = hd / 8, tail = pl.per_xcd - pl.full, ns = pl.slices;
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= nrows * chunks) return;
-    const int64_t row = idx / chunks;
-    const int col = (int)(idx - row * chunks) * 8, head = col / hd;
+    if (idx >= (int64_t)8 * tail * QT * chunks) return;
+    const int tix = (int)(idx / (QT * chunks)), rem = (int)(idx - (int64_t)tix * QT * chunks);
+    const int r = rem / chunks, col = (rem - r * chunks) * 8;
+    const int L = (tix / tail) * pl.per_xcd + pl.full + tix % tail;
+    if (L >= pl.items) return;
+    const int head = L / n_work, wi = L - head * n_work;
+    const RowTile wt = work[wi];
+    const ImgDesc d = imgs[wt.img];
+    const int q = wt.r0 + r;
+    if (q >= d.n) return;
+    const float2 *ml = reinterpret_cast<const float2 *>(pl.part_ml);
+    const int64_t pr0 = (int64_t)tix * ns * QT + r;   // slice sp at pr0 + sp * QT
     float mmax = -INFINITY;
-    for (int sp = 0; sp < nsplit; ++sp) mmax = fmaxf(mmax, part_ml[((int64_t)sp * H + head) * nrows + row].x);
+    for (int sp = 0; sp < ns; ++sp) mmax = fmaxf(mmax, ml[pr0 + (int64_t)sp * QT].x);
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, wsum = 0.f;
-    for (int sp = 0; sp < nsplit; ++sp) {
-        const float2 ml = part_ml[((int64_t)sp * H + head) * nrows + row];
-        const float w = ml.y == 0.f ? 0.f : ml.y * fast_exp2(ml.x - mmax);
-        const uint4 u = *reinterpret_cast<const uint4 *>(part_o + ((int64_t)sp * nrows + row) * D + col);
+    for (int sp = 0; sp < ns; ++sp) {
+        const float2 m = ml[pr0 + (int64_t)sp * QT];
+        const float w = m.y == 0.f ? 0.f : m.y * fast_exp2(m.x - mmax);
+        const uint4 u = *reinterpret_cast<const uint4 *>(pl.part_o + (pr0 + (int64_t)sp * QT) * hd + col);
         const uint32_t ww[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -510,7 +535,7 @@ __global__ __launch_bounds__(256) void attention_merge_kernel(
         wsum += w;
     }
     const float inv = 1.f / wsum;
-    *reinterpret_cast<uint4 *>(o + row * D + col) =
+    *reinterpret_cast<uint4 *>(o + ((int64_t)d.patch_off + q) * D + head * hd + col) =
         make_uint4(pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
                    pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv));
 }
@@ -518,18 +543,18 @@ __global__ __launch_bounds__(256) void attention_merge_kernel(
 template <int HD>
 hipError_t run_attention(const bf16_t *qkv, const bf16_t *vt, int64_t ldv, bf16_t *o,
                          const RowTile *work, int n_work, const ImgDesc *imgs, int D, int H,
-                         int64_t nrows, const AttnSplit &sp, hipStream_t s)
+                         const AttnSplit &sp, hipStream_t s)
 {
-    const int64_t total = (int64_t)n_work * H * sp.n;
-    const int grid = (int)(ceil_div(total, 8) * 8);
+    const int tail = sp.per_xcd - sp.full;
+    const int64_t grid = (int64_t)8 * (sp.full + (int64_t)tail * sp.slices);
     const float c_log2 = (float)(1.4426950408889634 / sqrt((double)HD));
-    hipLaunchKernelGGL(attention_kernel<HD>, dim3(grid), dim3(256), 0, s, qkv, vt, ldv, o, work,
-                       n_work, imgs, D, H, c_log2, sp.n, sp.part_o, (float2 *)sp.part_ml, nrows);
+    hipLaunchKernelGGL(attention_kernel<HD>, dim3((unsigned)grid), dim3(256), 0, s, qkv, vt, ldv, o, work,
+                       n_work, imgs, D, H, c_log2, sp);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || sp.n == 1) return e;
-    const int64_t threads = nrows * (D / 8);
+    if (e != hipSuccess || tail == 0 || sp.slices == 1) return e;
+    const int64_t threads = (int64_t)8 * tail * 128 * (HD / 8);
     hipLaunchKernelGGL(attention_merge_kernel, dim3((unsigned)ceil_div(threads, 256)), dim3(256), 0, s,
-                       sp.part_o, (const float2 *)sp.part_ml, sp.n, nrows, D, H, HD, o);
+                       sp, work, n_work, imgs, D, HD, o);
     return hipGetLastError();
 }
 
@@ -552,52 +577,65 @@ int blocks_per_cu()
 
 int attention_q_tile() { return 128; }
 
-size_t attention_split_bytes(int64_t nrows, int D, int H, int nsplit)
+size_t attention_plan_bytes(const AttnSplit &sp, int D, int H)
 {
-    if (nsplit <= 1) return 0;
-    return (size_t)nsplit * nrows * ((size_t)D * sizeof(uint16_t) + (size_t)H * sizeof(float2));
+    const int64_t tail = sp.per_xcd - sp.full;
+    if (sp.slices <= 1 || tail <= 0) return 0;
+    const int hd = D / H;
+    return (size_t)8 * tail * sp.slices * 128 * ((size_t)hd * sizeof(uint16_t) + sizeof(float2));
 }
 
-// Key slices per (query tile, head).  A CU runs its attention blocks at about the same total
-// rate whether it holds one or two of them, so slicing only pays when the batch cannot fill
-// the GPU: fewer than half as many (query tile, head) blocks as block slots.  Then the slices
-// multiply the blocks up to the slot count (at most 4, at least two key tiles per slice of the
-// largest image); the merge costs one pass over binary16 partials.
-int attention_split(const ImgDesc *imgs, int n_img, int D, int H)
+// Work split of a batch.  The blocks of one XCD fill its block slots (CUs x resident blocks)
+// in rounds; when the last round is partial, its items are cut into key slices so that it
+// occupies every slot for a fraction of a round.  A CU runs its attention blocks at about the
+// same total rate with one or two resident, so the cut pays even when the slices only fill
+// the CUs once.  At most 4 slices, each of at least two key tiles of the largest image.
+AttnSplit attention_plan(const ImgDesc *imgs, int n_img, int n_work, int D, int H, int fixed)
 {
-    if (n_img <= 0 || H <= 0) return 1;
+    AttnSplit sp{0, 0, 1, 0, nullptr, nullptr};
+    sp.items = n_work * H;
+    sp.per_xcd = (int)ceil_div(sp.items, 8);
+    sp.full = sp.per_xcd;
+    if (n_work <= 0 || H <= 0 || n_img <= 0 || fixed == 1) return sp;
+    if (fixed >= 2) {
+        sp.full = 0;
+        sp.slices = fixed;
+        return sp;
+    }
     int per_cu = 1;
     switch (D / H) {
     case 16: per_cu = blocks_per_cu<16>(); break;
     case 32: per_cu = blocks_per_cu<32>(); break;
     case 64: per_cu = blocks_per_cu<64>(); break;
     case 128: per_cu = blocks_per_cu<128>(); break;
-    default: return 1;
+    default: return sp;
     }
-    const int64_t slots = (int64_t)cu_count() * per_cu;
-    const int qt = attention_q_tile();
-    int64_t blocks = 0;
+    const int slots = std::max(1, cu_count() / 8) * per_cu;   // block slots of one XCD
+    const int full = sp.per_xcd / slots * slots, tail = sp.per_xcd - full;
+    if (tail == 0) return sp;
     int max_nkv = 0;
-    for (int i = 0; i < n_img; ++i) {
-        blocks += (int64_t)ceil_div(imgs[i].n, qt) * H;
-        max_nkv = std::max(max_nkv, (int)ceil_div(imgs[i].n, 64));
-    }
-    if (blocks == 0 || 2 * blocks > slots) return 1;
-    const int64_t by_slots = slots / blocks;
-    return (int)std::max<int64_t>(1, std::min<int64_t>({4, by_slots, max_nkv / 2}));
+    for (int i = 0; i < n_img; ++i) max_nkv = std::max(max_nkv, (int)ceil_div(imgs[i].n, 64));
+    const int s = std::min({4, slots / tail, max_nkv / 2});
+    if (s < 2) return sp;
+    sp.full = full;
+    sp.slices = s;
+    return sp;
 }
 
 hipError_t launch_attention(const bf16_t *qkv, const bf16_t *vt, int64_t ldv, bf16_t *o,
                             const RowTile *work, int n_work, const ImgDesc *imgs, int D, int H,
-                            int64_t nrows, const AttnSplit &sp, hipStream_t s)
+                            const AttnSplit &sp, hipStream_t s)
 {
     if (n_work <= 0) return hipSuccess;
-    if (sp.n < 1 || sp.n > 4 || (sp.n > 1 && (!sp.part_o || !sp.part_ml))) return hipErrorInvalidValue;
+    const int tail = sp.per_xcd - sp.full;
+    if (sp.items != n_work * H || sp.per_xcd != (int)ceil_div(sp.items, 8) || sp.full < 0 || tail < 0 ||
+        sp.slices < 1 || sp.slices > 4 || (tail > 0 && sp.slices > 1 && (!sp.part_o || !sp.part_ml)))
+        return hipErrorInvalidValue;
     switch (D / H) {
-    case 16: return run_attention<16>(qkv, vt, ldv, o, work, n_work, imgs, D, H, nrows, sp, s);
-    case 32: return run_attention<32>(qkv, vt, ldv, o, work, n_work, imgs, D, H, nrows, sp, s);
-    case 64: return run_attention<64>(qkv, vt, ldv, o, work, n_work, imgs, D, H, nrows, sp, s);
-    case 128: return run_attention<128>(qkv, vt, ldv, o, work, n_work, imgs, D, H, nrows, sp, s);
+    case 16: return run_attention<16>(qkv, vt, ldv, o, work, n_work, imgs, D, H, sp, s);
+    case 32: return run_attention<32>(qkv, vt, ldv, o, work, n_work, imgs, D, H, sp, s);
+    case 64: return run_attention<64>(qkv, vt, ldv, o, work, n_work, imgs, D, H, sp, s);
+    case 128: return run_attention<128>(qkv, vt, ldv, o, work, n_work, imgs, D, H, sp, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -47,20 +47,25 @@ hipError_t launch_rope(bf16_t *qkv, bf16_t *vt, int64_t ldv, const RowTile *tile
                        const ImgDesc *imgs, int D, int H, const float *cos_t,
                        const float *sin_t, hipStream_t s);
 
-// Block-diagonal flash attention; one block per (attention_q_tile() queries, head, key
-// slice).  With n > 1 key slices each slice writes its normalised binary16 output to
-// part_o [n][nrows][D] and (max, sum) to part_ml [n][H][nrows] (float pairs), and a merge
-// kernel writes o; attention_split_bytes() sizes that scratch.
+// Block-diagonal flash attention over work items (query tile of attention_q_tile() rows,
+// head), item L = head * n_work + tile.  The items are dealt to 8 groups of per_xcd
+// consecutive items (one group per XCD of the GPU); in each group the first `full` items run
+// whole, and each of the others is cut into `slices` key ranges run by separate blocks.  Each
+// range writes its output normalised by its own softmax sum (binary16) to part_o and its
+// (max, sum) to part_ml, in tail-item-major order, and a merge kernel writes o for those items.
+// attention_plan() picks the split for a batch; attention_plan_bytes() sizes the scratch.
 struct AttnSplit {
-    int n;
+    int per_xcd, full, slices, items;
     uint16_t *part_o;
     float *part_ml;
 };
-int attention_split(const ImgDesc *h_imgs, int n_img, int D, int H);
-size_t attention_split_bytes(int64_t nrows, int D, int H, int nsplit);
+// fixed: 0 = chosen from the batch (split only the items of a last, partial round of blocks),
+// 1 = never split, 2..4 = every item cut into that many key ranges.
+AttnSplit attention_plan(const ImgDesc *h_imgs, int n_img, int n_work, int D, int H, int fixed);
+size_t attention_plan_bytes(const AttnSplit &sp, int D, int H);
 hipError_t launch_attention(const bf16_t *qkv, const bf16_t *vt, int64_t ldv, bf16_t *o,
                             const RowTile *work, int n_work, const ImgDesc *imgs, int D, int H,
-                            int64_t nrows, const AttnSplit &sp, hipStream_t s);
+                            const AttnSplit &sp, hipStream_t s);
 
 // Compute units of the current device.
 int cu_count();

@@ -192,19 +192,23 @@ GemmWorkspace gemm_ws(vit_ctx *c)
     return GemmWorkspace{c->d_gemm_ws, c->d_gemm_ws ? c->gemm_ws_bytes : 0};
 }
 
-// Attention key slices for this batch and their scratch (grown on demand; without it the
+// Attention work split for this batch and its scratch (grown on demand; without it the
 // attention runs unsplit, which gives results within the same bounds).
 AttnSplit attn_split(vit_ctx *c, const Plan &p)
 {
-    AttnSplit sp{1, nullptr, nullptr};
-    const int ns = c->attn_split_fixed > 0 ? c->attn_split_fixed
-                                           : attention_split(p.imgs.data(), (int)p.imgs.size(), c->D, c->H);
-    if (ns <= 1) return sp;
-    const size_t need = attention_split_bytes(p.N, c->D, c->H, ns);
+    AttnSplit sp = attention_plan(p.imgs.data(), (int)p.imgs.size(), (int)p.attn.size(), c->D, c->H,
+                                  c->attn_split_fixed);
+    const size_t need = attention_plan_bytes(sp, c->D, c->H);
+    auto unsplit = [&]() {
+        sp.full = sp.per_xcd;
+        sp.slices = 1;
+        return sp;
+    };
+    if (need == 0) return unsplit();
     if (need > c->attn_ws_bytes) {
         if (hipDeviceSynchronize() != hipSuccess) {
             (void)hipGetLastError();
-            return sp;
+            return unsplit();
         }
         if (c->d_attn_ws) (void)hipFree(c->d_attn_ws);
         c->d_attn_ws = nullptr;
@@ -212,13 +216,13 @@ AttnSplit attn_split(vit_ctx *c, const Plan &p)
         if (hipMalloc((void **)&c->d_attn_ws, need) != hipSuccess) {
             (void)hipGetLastError();
             c->d_attn_ws = nullptr;
-            return sp;
+            return unsplit();
         }
         c->attn_ws_bytes = need;
     }
-    sp.n = ns;
+    const size_t rows = (size_t)8 * (sp.per_xcd - sp.full) * sp.slices * attention_q_tile();
     sp.part_o = (uint16_t *)c->d_attn_ws;
-    sp.part_ml = (float *)(c->d_attn_ws + (size_t)ns * p.N * c->D * sizeof(uint16_t));
+    sp.part_ml = (float *)(c->d_attn_ws + rows * (c->D / c->H) * sizeof(uint16_t));
     return sp;
 }
 
@@ -408,7 +412,7 @@ vit_status encode_impl(vit_ctx *c, const uint8_t *px, const vit_grid *grids, int
                               c->d_cos, c->d_sin, s));
         if (stop == VIT_DUMP_QKV && arg == l) return copy_out(c->qkv);
         TLAUNCH(c, VIT_STEP_ATTENTION, s, launch_attention(c->qkv, c->vt, p.vt_cols, c->o, dp.attn, (int)p.attn.size(),
-                                   dp.imgs, D, H, p.N, asp, s));
+                                   dp.imgs, D, H, asp, s));
         if (stop == VIT_DUMP_ATTN && arg == l) return copy_out(c->o);
         TLAUNCH(c, VIT_STEP_OUT_PROJ, s, launch_linear(c->o, p.N, D, w.wo, w.bo, D, ACT_NONE, false, c->delta, &gws, s));
         TLAUNCH(c, VIT_STEP_LAYERNORM, s, launch_layernorm(c->x, c->delta, c->x, p.N, D, w.ln2g, w.ln2b, c->cfg.ln_eps,
@@ -797,7 +801,7 @@ vit_status vit_op_attention(vit_ctx *ctx, const uint16_t *d_qkv, const uint16_t 
     DevPlan dp{};
     if ((st = stage_plan(ctx, p, (hipStream_t)stream, dp)) != VIT_OK) return st;
     LAUNCH(ctx, launch_attention(d_qkv, d_vt, p.vt_cols, d_o, dp.attn, (int)p.attn.size(), dp.imgs,
-                                 ctx->D, ctx->H, p.N, asp, (hipStream_t)stream));
+                                 ctx->D, ctx->H, asp, (hipStream_t)stream));
     return VIT_OK;
 }
 

@@ -282,7 +282,9 @@ def test_attention_full_size_sampled(grids):
                          ids=["v41_1024", "v4_384", "ragged_small"])
 def test_attention_key_slices(grids):
     """Every fixed number of key slices (1..4; short images leave some slices empty) meets the
-    oracle bound on sampled rows, and the automatic choice is bitwise one of them."""
+    oracle bound on sampled rows.  The automatic plan runs each (query tile, head) either whole
+    or cut into a fixed number of slices, so each of its outputs equals bitwise the same
+    output of one of the fixed runs."""
     torch = require_gpu()
     enc, cfg, _ = encoder("v41_1layer")
     qkv = _qkv_for(grids, cfg.hidden, 112)
@@ -301,7 +303,10 @@ def test_attention_key_slices(grids):
     rot = _oracle_rope(f32(qkv), grids, cfg)
     for n in (1, 2, 3, 4):
         _attention_check(outs[n], rot, grids, cfg, rows_per_image=lambda m: [r for r in (0, 1, 63, 64, m // 2, m - 1) if r < m])
-    assert any(np.array_equal(outs[0], outs[n]) for n in (1, 2, 3, 4))
+    same = np.zeros(outs[0].shape, bool)
+    for n in (1, 2, 3, 4):
+        same |= outs[0] == outs[n]
+    assert same.all()
 
 
 def test_attention_packed16_sampled():

@@ -2,7 +2,8 @@
  * vit_ops.h -- single-step entry points of the MI355X vision encoder.
  *
  * Each call launches exactly the kernel(s) that vit_encode uses for that step, with the same
- * launch configuration, on caller-provided device buffers.  They exist so that every step can
+ * launch configuration, on caller-provided device buffers (vit_op_rope is the exception: a
+ * standalone form of the rotation that vit_encode runs inside vit_op_qkv_rope's kernel).  They exist so that every step can
  * be checked and timed in isolation at the encoder's real shapes.  Conventions are those of
  * vit.h (bf16 as uint16_t, d_* device pointers, asynchronous on `stream`, validation before
  * any launch, VIT_E_* codes, text in vit_last_error(ctx)).  `ctx` must be non-NULL; only
@@ -42,7 +43,23 @@ vit_status vit_op_layernorm(vit_ctx *ctx, const uint16_t *d_x, const uint16_t *d
  * stride = sum over images of ceil(gh*gw / 64) * 64.  -1 if an argument is invalid. */
 int64_t vit_vt_stride(const vit_grid *h_grids, int32_t n_images);
 
-/* 2D RoPE on q and k ([Z] "Step 3": height/width-blocked angles, half-vector rotation;
+/* QKV projection of one layer with the 2D rotary embedding and the transposed-V copy in its
+ * epilogue, as vit_encode runs it ([Z] "Step 2" table: QKV with bias; "Step 3": RoPE on q
+ * and k; [G] V4: raw patch grid):
+ *   qkv = bf16(x W^T + b), x = bf16 [N][D] (N patches of the batch), W = bf16 [3D][D],
+ *   b = bf16 [3D] or NULL; then q and k rotated and stored in d_qkv = [N][3D] exactly as
+ *   vit_op_rope stores them (q bf16, k binary16 bit patterns), and v written to d_vt in
+ *   vit_op_rope's transposed layout (including the zero columns past each image's end).
+ *   The v columns of d_qkv are written (bf16) only when store_v != 0; vit_encode skips them.
+ * The rotation acts on the bf16-rounded projection, so for the same qkv values the results
+ * are bitwise those of vit_op_linear followed by vit_op_rope. */
+vit_status vit_op_qkv_rope(vit_ctx *ctx, const uint16_t *d_x, const uint16_t *d_W, const uint16_t *d_b,
+                           const vit_grid *h_grids, int32_t n_images, uint16_t *d_qkv, uint16_t *d_vt,
+                           int32_t store_v, void *stream);
+
+/* 2D RoPE on q and k as a separate pass over a qkv buffer (vit_encode fuses this step into the
+ * QKV projection, vit_op_qkv_rope; this entry point prepares attention inputs from any qkv)
+ * ([Z] "Step 3": height/width-blocked angles, half-vector rotation;
  * [G] V4: raw patch grid) in place inside d_qkv = bf16 [N][3D] (q | k | v, head-major).
  * Rotated q is stored as bf16; rotated k is rounded to bf16 and then stored as IEEE binary16
  * bit patterns (the attention's score operand type), so after this call columns D..2D-1 of

@@ -25,7 +25,7 @@ EXPORTS = ("vit_blob_elems", "vit_create", "vit_destroy", "vit_reserve", "vit_nu
            "vit_num_patches", "vit_encode", "vit_layout", "vit_overlay", "vit_dump",
            "vit_last_error", "vit_op_linear", "vit_op_layernorm", "vit_vt_stride", "vit_op_rope",
            "vit_op_attention", "vit_op_merge_project", "vit_timing_enable", "vit_timing_read",
-           "vit_set_attention_split")
+           "vit_set_attention_split", "vit_op_qkv_rope")
 STEP_NAMES = ("patch_embed", "layernorm", "qkv", "rope", "attention", "out_proj", "fc1", "fc2",
               "projector", "overlay")
 
@@ -81,6 +81,7 @@ def lib():
             "vit_op_layernorm": (i32, [vp, vp, vp, vp, i64, i32, vp, vp, ctypes.c_float, vp, vp]),
             "vit_vt_stride": (i64, [P(Grid), i32]),
             "vit_op_rope": (i32, [vp, vp, vp, P(Grid), i32, vp]),
+            "vit_op_qkv_rope": (i32, [vp, vp, vp, vp, P(Grid), i32, vp, vp, i32, vp]),
             "vit_op_attention": (i32, [vp, vp, vp, P(Grid), i32, vp, vp]),
             "vit_op_merge_project": (i32, [vp, vp, P(Grid), i32, vp, vp]),
             "vit_timing_enable": (i32, [vp, i32]),
@@ -259,6 +260,18 @@ class Encoder:
         self._check(lib().vit_op_rope(self._ctx, _ptr(qkv), _ptr(vt), grid_array(grids),
                                       len(grids), _stream(stream)))
         return vt
+
+    def op_qkv_rope(self, x, W, b, grids, store_v=False, stream=None):
+        """Fused QKV projection + RoPE + V^T relayout; returns (qkv bf16 [N][3D] with k as
+        binary16 bits and v only with store_v, vt torch.float16 [H][hd][vt_stride])."""
+        import torch
+        H, D = int(self.cfg.heads), int(self.cfg.hidden)
+        qkv = torch.zeros((x.shape[0], 3 * D), dtype=torch.bfloat16, device=x.device)
+        vt = torch.empty((H, D // H, vt_stride(grids)), dtype=torch.float16, device=x.device)
+        self._check(lib().vit_op_qkv_rope(self._ctx, _ptr(x), _ptr(W), _ptr(b), grid_array(grids),
+                                          len(grids), _ptr(qkv), _ptr(vt), 1 if store_v else 0,
+                                          _stream(stream)))
+        return qkv, vt
 
     def set_attention_split(self, n):
         """Key slices of the attention: 0 = chosen per batch, 1..4 = fixed."""

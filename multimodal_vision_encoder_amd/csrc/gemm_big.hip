@@ -106,6 +106,7 @@ __device__ __forceinline__ void bias_act(const bf16_t *bias, int N, int n, const
 template <int ACT>
 struct EpiBF16 {
     static constexpr int OUT_BYTES = 2;
+    static constexpr bool CUSTOM = false;
     bf16_t *out;
     const bf16_t *bias;
     int64_t M;
@@ -134,6 +135,7 @@ struct EpiBF16 {
 
 struct EpiF32 {
     static constexpr int OUT_BYTES = 4;
+    static constexpr bool CUSTOM = false;
     float *out;
     const bf16_t *bias;
     int64_t M;
@@ -163,11 +165,228 @@ struct EpiF32 {
 // Raw fp32 partial tile of a K slice (no bias, no activation), [BM][BN] contiguous.
 struct EpiPart {
     static constexpr int OUT_BYTES = 4;
+    static constexpr bool CUSTOM = false;
     float *out;
     __device__ __forceinline__ void put(char *dst, int, const float *v) const
     {
         *reinterpret_cast<float4 *>(dst) = make_float4(v[0], v[1], v[2], v[3]);
     }
+};
+
+// (a, b) turned by the angle with cosine c and sine s; products and sums rounded separately.
+__device__ __forceinline__ void rope_rotate(float a, float b, float c, float s, float &na, float &nb)
+{
+#pragma clang fp contract(off)
+    na = a * c - b * s;
+    nb = b * c + a * s;
+}
+
+// Index with bits 2 and 3 exchanged (an involution on 0..15 inside each group of 16).
+__device__ __forceinline__ int swap23(int p) { return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1); }
+
+// bf16 bit pattern -> binary16 bit pattern (round to nearest even, saturating at 65504).
+__device__ __forceinline__ uint32_t bf16_to_f16_sat(uint32_t b)
+{
+    float f = __uint_as_float(b << 16);
+    if (__builtin_fabsf(f) > 65504.f) f = __builtin_copysignf(65504.f, f);
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// QKV projection with the 2D rotary embedding and the V^T relayout in the epilogue ([Z]
+// "Step 3": angles blocked by axis, theta = [h f_0 .. h f_{Q-1}, w f_0 .. w f_{Q-1}] with
+// Q = hd/4, rotation of element i with i + hd/2; [G] V4 Flash vision row: raw patch grid).
+// The staged tile holds bf16(acc + bias), i.e. the bf16 qkv values; from there:
+//   q columns: rotated, rounded to bf16, stored in place of q;
+//   k columns: rotated, rounded to bf16, then stored as binary16 (the attention's score
+//              operand type; exact for bf16 magnitudes 2^-14 .. 65504, larger saturate);
+//   v columns: stored transposed as binary16, vt[head][d][col], where image i owns the
+//              columns from its 64-aligned offset and inside each group of 16 columns, column
+//              p holds key (p with bits 2 and 3 swapped); with store_v also kept as bf16 in
+//              the qkv rows.  Columns past an image's last patch are not written here.
+// Patch p of an image sits at (p / gw, p % gw) of its grid; cos/sin come from tables
+// [position][hd/4] built on the host.
+template <int HD>
+struct EpiQKVRope {
+    static constexpr int OUT_BYTES = 2;
+    static constexpr bool CUSTOM = true;
+    bf16_t *out;        // [M][3D]
+    const bf16_t *bias;
+    int64_t M;
+    int N;              // 3D
+    int D;
+    uint16_t *vt;
+    int64_t ldv;
+    const ImgDesc *imgs;
+    int n_img;
+    const float *cos_t, *sin_t;
+    int store_v;
+    __device__ __forceinline__ void put(char *dst, int n, const float *v) const
+    {
+        float r[4];
+        bias_act<ACT_NONE>(bias, N, n, v, r);
+        *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]));
+    }
+    // Bytes of LDS past the staged tile that the epilogue uses: (row, column) on the image's
+    // patch grid of every tile row.
+    template <int BM>
+    static constexpr int extra_lds() { return BM * 8; }
+    // Before the staging barrier: grid position of each tile row into `pos`.
+    template <int BM, int NT>
+    __device__ __forceinline__ void prepare(char *pos, int64_t m0, int rows, int tid) const
+    {
+        for (int r = tid; r < rows; r += NT) {
+            const int64_t row = m0 + r;
+            const ImgDesc &d = imgs[image_of_patch(imgs, n_img, row)];
+            const int lr = (int)(row - d.patch_off), hp = lr / d.gw;
+            reinterpret_cast<int2 *>(pos)[r] = make_int2(hp, lr - hp * d.gw);
+        }
+    }
+    template <int BM, int BN, int NT>
+    __device__ __forceinline__ void write(const char *smem, int pitch, int64_t m0, int n0, int rows, int tid) const
+    {
+        constexpr int HALF = HD / 2, Q4 = HD / 4, HC = HALF / 8, NHB = BN / HD;
+        static_assert(HD >= 16 && BN % HD == 0, "head blocks must tile the column tile");
+        const int2 *pos = reinterpret_cast<const int2 *>(smem + BM * pitch);
+        // q and k (and v rows with store_v): item = (row, head block, chunk of 8 elements of
+        // the first half and the 8 they pair with); the items of one row are consecutive
+        // lanes, so each row's stores are contiguous.  With Q4 % 8 == 0 a chunk lies on one
+        // axis and takes 8 consecutive angles of it.
+        for (int w = tid; w < BM * NHB * HC; w += NT) {
+            const int r = w / (NHB * HC), it = w - r * (NHB * HC), hb = it / HC, ch = it - hb * HC;
+            const int c0 = n0 + hb * HD;
+            if (r >= rows || c0 >= N) continue;
+            const int part = c0 / D;
+            const int64_t row = m0 + r;
+            const char *src = smem + r * pitch + (hb * HD + ch * 8) * 2;
+            bf16_t *dst = out + row * N + c0 + ch * 8;
+            const uint4 ua = *reinterpret_cast<const uint4 *>(src);
+            const uint4 ub = *reinterpret_cast<const uint4 *>(src + HALF * 2);
+            if (part == 2) {
+                if (store_v) {
+                    *reinterpret_cast<uint4 *>(dst) = ua;
+                    *reinterpret_cast<uint4 *>(dst + HALF) = ub;
+                }
+                continue;
+            }
+            const int2 hw = pos[r];
+            float cs[8], sn[8];
+            if constexpr (Q4 % 8 == 0) {
+                const int ax = ch * 8 >= Q4, j0 = ch * 8 - ax * Q4;
+                const float4 *c4 = reinterpret_cast<const float4 *>(cos_t + (ax ? hw.y : hw.x) * Q4 + j0);
+                const float4 *s4 = reinterpret_cast<const float4 *>(sin_t + (ax ? hw.y : hw.x) * Q4 + j0);
+                const float4 c_a = c4[0], c_b = c4[1], s_a = s4[0], s_b = s4[1];
+                cs[0] = c_a.x, cs[1] = c_a.y, cs[2] = c_a.z, cs[3] = c_a.w;
+                cs[4] = c_b.x, cs[5] = c_b.y, cs[6] = c_b.z, cs[7] = c_b.w;
+                sn[0] = s_a.x, sn[1] = s_a.y, sn[2] = s_a.z, sn[3] = s_a.w;
+                sn[4] = s_b.x, sn[5] = s_b.y, sn[6] = s_b.z, sn[7] = s_b.w;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int i = ch * 8 + e, j = i < Q4 ? i : i - Q4, p = i < Q4 ? hw.x : hw.y;
+                    cs[e] = cos_t[p * Q4 + j];
+                    sn[e] = sin_t[p * Q4 + j];
+                }
+            }
+            const uint32_t wa[4] = {ua.x, ua.y, ua.z, ua.w}, wb[4] = {ub.x, ub.y, ub.z, ub.w};
+            float na[8], nb[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = __uint_as_float(e & 1 ? wa[e >> 1] & 0xFFFF0000u : wa[e >> 1] << 16);
+                const float y = __uint_as_float(e & 1 ? wb[e >> 1] & 0xFFFF0000u : wb[e >> 1] << 16);
+                rope_rotate(x, y, cs[e], sn[e], na[e], nb[e]);
+            }
+            uint32_t pa[4], pb[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                pa[j] = pack_bf16x2(na[2 * j], na[2 * j + 1]);
+                pb[j] = pack_bf16x2(nb[2 * j], nb[2 * j + 1]);
+                if (part == 1) {
+                    pa[j] = bf16_to_f16_sat(pa[j] & 0xFFFFu) | (bf16_to_f16_sat(pa[j] >> 16) << 16);
+                    pb[j] = bf16_to_f16_sat(pb[j] & 0xFFFFu) | (bf16_to_f16_sat(pb[j] >> 16) << 16);
+                }
+            }
+            *reinterpret_cast<uint4 *>(dst) = make_uint4(pa[0], pa[1], pa[2], pa[3]);
+            *reinterpret_cast<uint4 *>(dst + HALF) = make_uint4(pb[0], pb[1], pb[2], pb[3]);
+        }
+        // V^T: per image in the tile, item = (run of 4 keys 4c..4c+3 of the image, 8 head dims).
+        // The bit swap keeps each 4-aligned run on 4 consecutive columns, so a whole run is one
+        // 8-byte store per dim; a run cut by the tile or the image end is stored per key.  The
+        // lane reads the run's 4 tile rows as 16-byte pieces (dims o*8 .. o*8+7), so the LDS
+        // reads of a wave spread over all banks.
+        const int ilo = image_of_patch(imgs, n_img, m0), ihi = image_of_patch(imgs, n_img, m0 + rows - 1);
+        constexpr int OCT = HD / 8;
+        for (int hb = 0; hb < NHB; ++hb) {
+            const int c0 = n0 + hb * HD;
+            if (c0 >= N || c0 < 2 * D) continue;
+            const int head = (c0 - 2 * D) / HD;
+            for (int i = ilo; i <= ihi; ++i) {
+                const int off = imgs[i].patch_off, n = imgs[i].n, voff = imgs[i].vt_off;
+                const int klo = (int)max((int64_t)0, m0 - off);
+                const int khi = (int)min((int64_t)n, m0 + rows - off);
+                if (klo >= khi) continue;
+                const int c_lo = klo >> 2, nruns = ((khi - 1) >> 2) - c_lo + 1;
+                for (int w = tid; w < nruns * OCT; w += NT) {
+                    const int o = w % OCT, k0 = 4 * (c_lo + w / OCT);
+                    uint32_t h[4][4];   // [key e][dim pair]
+                    bool whole = true;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int k = k0 + e;
+                        if (k < klo || k >= khi) {
+                            whole = false;
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) h[e][j] = 0;
+                            continue;
+                        }
+                        const int r = (int)(off + k - m0);
+                        const uint4 u = *reinterpret_cast<const uint4 *>(smem + r * pitch + (hb * HD + o * 8) * 2);
+                        h[e][0] = u.x, h[e][1] = u.y, h[e][2] = u.z, h[e][3] = u.w;
+                    }
+                    const int pc = swap23(k0);
+                    uint16_t *vrow = vt + ((int64_t)head * HD + o * 8) * ldv + voff + pc;
+#pragma unroll
+                    for (int dd = 0; dd < 8; ++dd) {
+                        uint32_t f[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) f[e] = bf16_to_f16_sat((h[e][dd >> 1] >> ((dd & 1) * 16)) & 0xFFFFu);
+                        uint16_t *dst = vrow + (int64_t)dd * ldv;
+                        if (whole) {
+                            *reinterpret_cast<uint2 *>(dst) = make_uint2(f[0] | (f[1] << 16), f[2] | (f[3] << 16));
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (k0 + e >= klo && k0 + e < khi) dst[e] = (uint16_t)f[e];
+                        }
+                    }
+                }
+            }
+        }
+    }
+};
+
+// Zeros of the transposed-V columns past each image's last patch (up to its 64-aligned end),
+// which the attention reads as masked keys.  One thread per (image, row of vt).
+__global__ __launch_bounds__(256) void vt_tail_zero_kernel(uint16_t *__restrict__ vt, int64_t ldv,
+                                                           const ImgDesc *__restrict__ imgs, int rows)
+{
+    const int r = blockIdx.y * 256 + threadIdx.x;
+    if (r >= rows) return;
+    const ImgDesc d = imgs[blockIdx.x];
+    uint16_t *row = vt + (int64_t)r * ldv + d.vt_off;
+    const int end = (d.n + 63) / 64 * 64;
+    for (int k = d.n; k < end; ++k) row[swap23(k)] = 0;
+}
+
+// LDS a launch needs for its epilogue: the staged tile plus what a custom epilogue asks for.
+template <class EP, bool C = EP::CUSTOM>
+struct EpiExtra {
+    template <int BM, int PITCH>
+    static constexpr int bytes() { return 0; }
+};
+template <class EP>
+struct EpiExtra<EP, true> {
+    template <int BM, int PITCH>
+    static constexpr int bytes() { return BM * PITCH + EP::template extra_lds<BM>(); }
 };
 
 // Work split of one launch: tiles [0, full) are computed whole; when splits > 1 the remaining
@@ -195,7 +414,8 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(SRC src, const bf16_t 
     constexpr bool STAGED = BM * PITCH <= 160 * 1024;
     constexpr bool PSTAGED = BM * PPITCH <= 160 * 1024;
     constexpr int SMEM0 = (STAGED && BM * PITCH > NS * STAGE) ? BM * PITCH : NS * STAGE;
-    constexpr int SMEM = (PSTAGED && BM * PPITCH > SMEM0) ? BM * PPITCH : SMEM0;
+    constexpr int SMEM1 = (PSTAGED && BM * PPITCH > SMEM0) ? BM * PPITCH : SMEM0;
+    constexpr int SMEM = EpiExtra<EP>::template bytes<BM, PITCH>() > SMEM1 ? EpiExtra<EP>::template bytes<BM, PITCH>() : SMEM1;
     __shared__ __attribute__((aligned(1024))) char smem[SMEM];
     auto stage = [&](auto st) -> char * { return smem + decltype(st)::value * STAGE; };
     auto stage_lds = [&](auto st) -> uint32_t {
@@ -350,8 +570,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(SRC src, const bf16_t 
 
     // acc[i][j][r]: output row l32 of the 32-block, column 8*(r/4) + 4*g + r%4.
     // Stage rows of `pitch` bytes in LDS via put(), then write whole rows of the tile.
-    auto staged = [&](const auto &e, int pitch, int ob, char *gout, int64_t gpitch, int rows,
-                      int row_bytes) {
+    auto stage_tile = [&](const auto &e, int pitch, int ob) {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -364,6 +583,10 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(SRC src, const bf16_t 
                     e.put(smem + r * pitch + c * ob, n0 + c, v);
                 }
         __syncthreads();
+    };
+    auto staged = [&](const auto &e, int pitch, int ob, char *gout, int64_t gpitch, int rows,
+                      int row_bytes) {
+        stage_tile(e, pitch, ob);
         const int ch = BN * ob / 16;                        // 16-byte chunks per tile row
 #pragma unroll 4
         for (int c = tid; c < BM * ch; c += NT) {
@@ -385,23 +608,31 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(SRC src, const bf16_t 
                    (int64_t)BN * 4, BM, BN * 4);
         return;
     }
-    if (STAGED && ((int64_t)N * OB) % 16 == 0) {
-        const int rows = (int)(ep.M - m0 < BM ? ep.M - m0 : BM);
-        const int row_bytes = (N - n0 < BN ? N - n0 : BN) * OB;
-        staged(ep, PITCH, OB, reinterpret_cast<char *>(ep.out) + (m0 * N + n0) * OB, (int64_t)N * OB,
-               rows, row_bytes);
-        return;
+    if constexpr (EP::CUSTOM) {
+        static_assert(STAGED, "custom epilogues need the staged tile");
+        const int rows_c = (int)(ep.M - m0 < BM ? ep.M - m0 : BM);
+        ep.template prepare<BM, NT>(smem + BM * PITCH, m0, rows_c, tid);
+        stage_tile(ep, PITCH, OB);
+        ep.template write<BM, BN, NT>(smem, PITCH, m0, n0, (int)(ep.M - m0 < BM ? ep.M - m0 : BM), tid);
+    } else {
+        if (STAGED && ((int64_t)N * OB) % 16 == 0) {
+            const int rows = (int)(ep.M - m0 < BM ? ep.M - m0 : BM);
+            const int row_bytes = (N - n0 < BN ? N - n0 : BN) * OB;
+            staged(ep, PITCH, OB, reinterpret_cast<char *>(ep.out) + (m0 * N + n0) * OB, (int64_t)N * OB,
+                   rows, row_bytes);
+            return;
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                        acc[i][j][4 * q + 3]};
+                    ep.store(m0 + wm * WM + i * 32 + l32, n0 + wn * WN + j * 32 + 8 * q + 4 * g, v);
+                }
     }
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                                    acc[i][j][4 * q + 3]};
-                ep.store(m0 + wm * WM + i * 32 + l32, n0 + wn * WN + j * 32 + 8 * q + 4 * g, v);
-            }
 }
 
 // Sum of the K slices of the leftover tiles, in slice order, then the epilogue.  One thread
@@ -466,16 +697,19 @@ hipError_t run_big(SRC src, const bf16_t *W, int64_t M, int N, int K, EP ep, con
 {
     if (M <= 0) return hipSuccess;
     const int tiles_m = (int)ceil_div(M, BM), tiles_n = (int)ceil_div(N, BN);
-    SplitK sk = plan_split(M, N, K, BM, BN, ws != nullptr);
-    if (sk.splits > 1 && (size_t)sk.items * BM * BN * 4 > ws->bytes) sk = SplitK{0, 1, 0, 0, nullptr};
-    if (sk.splits > 1) {
-        sk.part = ws->part;
-        hipLaunchKernelGGL((gemm_big_kernel<BM, BN, SRC, EP>), dim3(sk.full + sk.items_pad), dim3(512), 0, s,
-                           src, W, N, K, ep, tiles_m, tiles_n, sk);
-        const int64_t threads = (int64_t)(sk.items / sk.splits) * BM * (BN / 4);
-        hipLaunchKernelGGL((gemm_split_reduce_kernel<BM, BN, EP>), dim3((unsigned)ceil_div(threads, 256)),
-                           dim3(256), 0, s, ep, tiles_n, sk);
-        return hipGetLastError();
+    SplitK sk{0, 1, 0, 0, nullptr};
+    if constexpr (!EP::CUSTOM) {   // custom epilogues need whole tiles
+        sk = plan_split(M, N, K, BM, BN, ws != nullptr);
+        if (sk.splits > 1 && (size_t)sk.items * BM * BN * 4 > ws->bytes) sk = SplitK{0, 1, 0, 0, nullptr};
+        if (sk.splits > 1) {
+            sk.part = ws->part;
+            hipLaunchKernelGGL((gemm_big_kernel<BM, BN, SRC, EP>), dim3(sk.full + sk.items_pad), dim3(512), 0, s,
+                               src, W, N, K, ep, tiles_m, tiles_n, sk);
+            const int64_t threads = (int64_t)(sk.items / sk.splits) * BM * (BN / 4);
+            hipLaunchKernelGGL((gemm_split_reduce_kernel<BM, BN, EP>), dim3((unsigned)ceil_div(threads, 256)),
+                               dim3(256), 0, s, ep, tiles_n, sk);
+            return hipGetLastError();
+        }
     }
     const int64_t tiles = (int64_t)tiles_m * tiles_n;
     const int grid = (int)(ceil_div(tiles, 8) * 8);
@@ -534,6 +768,40 @@ hipError_t launch_linear(const bf16_t *A, int64_t M, int K, const bf16_t *W, con
                          int N, int act, bool out_f32, void *out, const GemmWorkspace *ws, hipStream_t s)
 {
     return dispatch(SrcPlain{A, K, M}, W, M, N, K, bias, act, out_f32, out, ws, s);
+}
+
+template <int HD>
+hipError_t run_qkv_rope(const bf16_t *A, int64_t M, int D, const bf16_t *W, const bf16_t *bias,
+                        bf16_t *qkv, uint16_t *vt, int64_t ldv, const ImgDesc *imgs, int n_img,
+                        const float *cos_t, const float *sin_t, bool store_v, hipStream_t s)
+{
+    const int N = 3 * D;
+    EpiQKVRope<HD> ep{qkv, bias, M, N, D, vt, ldv, imgs, n_img, cos_t, sin_t, store_v ? 1 : 0};
+    const SrcPlain src{A, D, M};
+    return use_big_tiles(M, N) ? run_big<256, 256>(src, W, M, N, D, ep, nullptr, s)
+                               : run_big<256, 128>(src, W, M, N, D, ep, nullptr, s);
+}
+
+hipError_t launch_qkv_rope(const bf16_t *A, int64_t M, int D, int H, const bf16_t *W, const bf16_t *bias,
+                           bf16_t *qkv, uint16_t *vt, int64_t ldv, const ImgDesc *imgs, int n_img,
+                           const float *cos_t, const float *sin_t, bool store_v, hipStream_t s)
+{
+    switch (D / H) {
+    case 16: return run_qkv_rope<16>(A, M, D, W, bias, qkv, vt, ldv, imgs, n_img, cos_t, sin_t, store_v, s);
+    case 32: return run_qkv_rope<32>(A, M, D, W, bias, qkv, vt, ldv, imgs, n_img, cos_t, sin_t, store_v, s);
+    case 64: return run_qkv_rope<64>(A, M, D, W, bias, qkv, vt, ldv, imgs, n_img, cos_t, sin_t, store_v, s);
+    case 128: return run_qkv_rope<128>(A, M, D, W, bias, qkv, vt, ldv, imgs, n_img, cos_t, sin_t, store_v, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_vt_tail_zero(uint16_t *vt, int64_t ldv, const ImgDesc *imgs, int n_img, int rows,
+                               hipStream_t s)
+{
+    if (n_img <= 0 || rows <= 0) return hipSuccess;
+    hipLaunchKernelGGL(vt_tail_zero_kernel, dim3(n_img, (unsigned)ceil_div(rows, 256)), dim3(256), 0, s, vt,
+                       ldv, imgs, rows);
+    return hipGetLastError();
 }
 
 hipError_t launch_merge_project(const bf16_t *y, const ImgDesc *imgs, int n_img, int64_t Mtok,

@@ -47,6 +47,17 @@ hipError_t launch_rope(bf16_t *qkv, bf16_t *vt, int64_t ldv, const RowTile *tile
                        const ImgDesc *imgs, int D, int H, const float *cos_t,
                        const float *sin_t, hipStream_t s);
 
+// QKV projection (N = 3D, K = D) with 2D RoPE on q and k and the transposed binary16 copy of
+// v in the GEMM epilogue: qkv = [bf16 q | binary16 k | v (only with store_v)], vt as
+// launch_rope writes it, except the columns past each image's end (launch_vt_tail_zero).
+hipError_t launch_qkv_rope(const bf16_t *A, int64_t M, int D, int H, const bf16_t *W, const bf16_t *bias,
+                           bf16_t *qkv, uint16_t *vt, int64_t ldv, const ImgDesc *imgs, int n_img,
+                           const float *cos_t, const float *sin_t, bool store_v, hipStream_t s);
+// Zeros in vt's columns past each image's last patch (up to its 64-aligned end); `rows` =
+// heads x head_dim.
+hipError_t launch_vt_tail_zero(uint16_t *vt, int64_t ldv, const ImgDesc *imgs, int n_img, int rows,
+                               hipStream_t s);
+
 // Block-diagonal flash attention over work items (query tile of attention_q_tile() rows,
 // head), item L = head * n_work + tile.  The items are dealt to 8 groups of per_xcd
 // consecutive items (one group per XCD of the GPU); in each group the first `full` items run

@@ -403,13 +403,16 @@ vit_status encode_impl(vit_ctx *c, const uint8_t *px, const vit_grid *grids, int
                                  c->pe_b, D, c->patches, c->x, &gws, s));
     if (stop == VIT_DUMP_EMBED) return copy_out(c->x);
 
+    // the transposed-V columns past each image's end are read as masked keys: zero them once
+    if (L > 0) LAUNCH(c, launch_vt_tail_zero(c->vt, p.vt_cols, dp.imgs, ni, D, s));
     for (int l = 0; l < L; ++l) {
         const Layer &w = c->layers[l];
         TLAUNCH(c, VIT_STEP_LAYERNORM, s, launch_layernorm(c->x, l ? c->delta : nullptr, c->x, p.N, D, w.ln1g, w.ln1b,
                                    c->cfg.ln_eps, c->ln, s));
-        TLAUNCH(c, VIT_STEP_QKV, s, launch_linear(c->ln, p.N, D, w.wqkv, w.bqkv, 3 * D, ACT_NONE, false, c->qkv, &gws, s));
-        TLAUNCH(c, VIT_STEP_ROPE, s, launch_rope(c->qkv, c->vt, p.vt_cols, dp.rope, (int)p.rope.size(), dp.imgs, D, H,
-                              c->d_cos, c->d_sin, s));
+        // QKV projection with RoPE on q, k and the V^T relayout in its epilogue
+        TLAUNCH(c, VIT_STEP_QKV, s, launch_qkv_rope(c->ln, p.N, D, H, w.wqkv, w.bqkv, c->qkv, c->vt, p.vt_cols,
+                                                    dp.imgs, ni, c->d_cos, c->d_sin,
+                                                    stop == VIT_DUMP_QKV && arg == l, s));
         if (stop == VIT_DUMP_QKV && arg == l) return copy_out(c->qkv);
         TLAUNCH(c, VIT_STEP_ATTENTION, s, launch_attention(c->qkv, c->vt, p.vt_cols, c->o, dp.attn, (int)p.attn.size(),
                                    dp.imgs, D, H, asp, s));
@@ -785,6 +788,25 @@ vit_status vit_op_rope(vit_ctx *ctx, uint16_t *d_qkv, uint16_t *d_vt, const vit_
     if ((st = stage_plan(ctx, p, (hipStream_t)stream, dp)) != VIT_OK) return st;
     LAUNCH(ctx, launch_rope(d_qkv, d_vt, p.vt_cols, dp.rope, (int)p.rope.size(), dp.imgs, ctx->D,
                             ctx->H, ctx->d_cos, ctx->d_sin, (hipStream_t)stream));
+    return VIT_OK;
+}
+
+vit_status vit_op_qkv_rope(vit_ctx *ctx, const uint16_t *d_x, const uint16_t *d_W, const uint16_t *d_b,
+                           const vit_grid *h_grids, int32_t n_images, uint16_t *d_qkv, uint16_t *d_vt,
+                           int32_t store_v, void *stream)
+{
+    if (!ctx) return fail(nullptr, VIT_E_ARG, "ctx is NULL");
+    Plan p;
+    vit_status st = make_plan(ctx, h_grids, n_images, p);
+    if (st != VIT_OK) return st;
+    if (p.N == 0) return VIT_OK;
+    if (!d_x || !d_W || !d_qkv || !d_vt) return fail(ctx, VIT_E_ARG, "NULL pointer");
+    DevPlan dp{};
+    if ((st = stage_plan(ctx, p, (hipStream_t)stream, dp)) != VIT_OK) return st;
+    const int ni = (int)p.imgs.size();
+    LAUNCH(ctx, launch_vt_tail_zero(d_vt, p.vt_cols, dp.imgs, ni, ctx->D, (hipStream_t)stream));
+    LAUNCH(ctx, launch_qkv_rope(d_x, p.N, ctx->D, ctx->H, d_W, d_b, d_qkv, d_vt, p.vt_cols, dp.imgs, ni,
+                                ctx->d_cos, ctx->d_sin, store_v != 0, (hipStream_t)stream));
     return VIT_OK;
 }
 

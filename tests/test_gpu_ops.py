@@ -173,10 +173,15 @@ def test_rope_exact(name, grids):
     assert np.array_equal(got[:, :D], want[:, :D])
     assert np.array_equal(got[:, 2 * D:], want[:, 2 * D:])
     assert np.array_equal(got[:, D:2 * D], f16_of(want[:, D:2 * D]))
-    # v transposed per head as binary16 (round to nearest even, saturating at 65504: exact
-    # except below 2^-14, where binary16 is subnormal), each image at its own 64-aligned
-    # column block, zero padding; inside each 16-column group, column p holds key p with
-    # bits 2 and 3 swapped
+    _check_vt(vt, f32(qkv[:, 2 * D:]), grids, cfg)
+
+
+def _check_vt(vt, v_bf16, grids, cfg):
+    """v transposed per head as binary16 (round to nearest even, saturating at 65504: exact
+    except below 2^-14, where binary16 is subnormal), each image at its own 64-aligned column
+    block, zero padding; inside each 16-column group, column p holds key p with bits 2 and 3
+    swapped."""
+    import torch
     assert vt.dtype == torch.float16
     vtn = vt.float().cpu().numpy()
     H, hd = cfg.heads, cfg.head_dim
@@ -185,13 +190,62 @@ def test_rope_exact(name, grids):
         n = gh * gw
         pad = -(-n // 64) * 64
         v = np.zeros((H, hd, pad), np.float32)
-        vv = np.clip(f32(qkv[off:off + n, 2 * cfg.hidden:]), -65504, 65504)
+        vv = np.clip(v_bf16[off:off + n], -65504, 65504)
         v[:, :, :n] = vv.astype(np.float16).astype(np.float32).reshape(n, H, hd).transpose(1, 2, 0)
         p = np.arange(pad)
         key = (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1)
         assert np.array_equal(vtn[:, :, col:col + pad], v[:, :, key])
         off += n
         col += pad
+
+
+@pytest.mark.parametrize("name,grids", [("tiny", [(6, 6)]), ("tiny", [(5, 7), (1, 1), (9, 12), (2, 3)]),
+                                        ("v41_1layer", [(24, 24)]),
+                                        ("v41_1layer", [(7, 11), (30, 3), (13, 21)])])
+def test_qkv_rope_fused_one_hot(name, grids):
+    """The QKV projection with RoPE and the transposed-V copy in its epilogue (the encoder's
+    path).  One-hot weight rows copy input columns exactly, plus a bias with one rounding, so
+    q, k, v and V^T must equal bitwise the oracle's RoPE of those values.  The ragged grids put
+    images at offsets that are not multiples of 4 and across a 256-row tile boundary."""
+    torch = require_gpu()
+    enc, cfg, _ = encoder(name)
+    D = cfg.hidden
+    N = sum(gh * gw for gh, gw in grids)
+    x = seeded_bf16((N, D), 120, 0)
+    sigma = np.random.default_rng(120).integers(0, D, 3 * D)
+    W = np.zeros((3 * D, D), np.uint16)
+    W[np.arange(3 * D), sigma] = 0x3F80          # bf16 1.0
+    b = seeded_bf16((3 * D,), 120, 1, std=0.1)
+    qkv, vt = enc.op_qkv_rope(to_dev_bf16(x), to_dev_bf16(W), to_dev_bf16(b), grids, store_v=True)
+    torch.cuda.synchronize()
+    proj = oracle.linear(f32(x), f32(W), f32(b), round_out=True)
+    want = _oracle_rope(proj, grids, cfg)
+    got = qkv_after_rope(qkv, D)
+    assert np.array_equal(got[:, :D], want[:, :D])
+    assert np.array_equal(got[:, D:2 * D], f16_of(want[:, D:2 * D]))
+    assert np.array_equal(got[:, 2 * D:], want[:, 2 * D:])
+    _check_vt(vt, proj[:, 2 * D:], grids, cfg)
+
+
+@pytest.mark.parametrize("grids", [[(96, 96)], [(54, 63), (13, 21)]], ids=["v41_1024", "packed"])
+def test_qkv_rope_fused_equals_separate_steps(grids):
+    """At full width with random weights the fused kernel equals the linear layer followed by
+    the separate RoPE pass, bitwise (same tiles, same accumulation order, same rotation)."""
+    torch = require_gpu()
+    enc, cfg, _ = encoder("v41_1layer")
+    D = cfg.hidden
+    N = sum(gh * gw for gh, gw in grids)
+    x = to_dev_bf16(seeded_bf16((N, D), 121, 0))
+    W = to_dev_bf16(seeded_bf16((3 * D, D), 121, 1, std=0.02))
+    b = to_dev_bf16(seeded_bf16((3 * D,), 121, 2, std=0.02))
+    qkv, vt = enc.op_qkv_rope(x, W, b, grids)
+    lin = enc.op_linear(x, W, b)
+    vt2 = enc.op_rope(lin, grids)
+    torch.cuda.synchronize()
+    a = qkv.view(torch.int16)[:, :2 * D].cpu().numpy()
+    c = lin.view(torch.int16)[:, :2 * D].cpu().numpy()
+    assert np.array_equal(a, c)
+    assert torch.equal(vt.view(torch.int16), vt2.view(torch.int16))
 
 
 def _attention_check(got, qkv_rot, grids, cfg, rows_per_image=None):

@@ -721,6 +721,48 @@ hipError_t run_big(SRC src, const bf16_t *W, int64_t M, int N, int K, EP ep, con
 // 256 x 256 tiles when they give at least one full wave of blocks, else 256 x 128
 bool use_big_tiles(int64_t M, int N) { return ceil_div(M, 256) * ceil_div(N, 256) >= cu_count(); }
 
+// The same operands and epilogue for rows m0.. of the output (A rows and output rows offset).
+SrcPlain rows_from(const SrcPlain &s, int64_t m0) { return SrcPlain{s.A + m0 * s.lda, s.lda, s.M - m0}; }
+template <int ACT>
+EpiBF16<ACT> rows_from(const EpiBF16<ACT> &e, int64_t m0) { return EpiBF16<ACT>{e.out + m0 * e.N, e.bias, e.M - m0, e.N}; }
+EpiF32 rows_from(const EpiF32 &e, int64_t m0) { return EpiF32{e.out + m0 * e.N, e.bias, e.M - m0, e.N}; }
+
+// Row tail of a multi-round launch (one block per CU): when the tiles of the last, partial
+// round are whole rows of tiles, those rows run afterwards as 128 x 128 tiles, four times as
+// many blocks of a quarter of the work, if they then fit in one round.  Returns the first
+// row of that tail, or M when the launch is left as it is.
+int64_t row_tail_start(int64_t M, int N, int BM, int BN)
+{
+    const int P = cu_count();
+    const int64_t tiles_n = ceil_div(N, BN), tiles = ceil_div(M, BM) * tiles_n;
+    if (tiles <= P || tiles % P == 0) return M;
+    const int64_t main_tiles = tiles / P * P;
+    if (main_tiles % tiles_n != 0) return M;
+    const int64_t m_main = main_tiles / tiles_n * BM;
+    if (ceil_div(M - m_main, 128) * ceil_div(N, 128) > P) return M;
+    return m_main;
+}
+
+// A launch with BM x BN tiles, its partial last round of whole tile rows (if any) moved to a
+// second launch of 128 x 128 tiles.  Launches that use the split-K tail keep it instead.
+template <int BM, int BN, class EP>
+hipError_t run_rows(SrcPlain src, const bf16_t *W, int64_t M, int N, int K, EP ep, const GemmWorkspace *ws,
+                    hipStream_t s)
+{
+    const int64_t m_tail = plan_split(M, N, K, BM, BN, ws != nullptr).splits > 1 ? M : row_tail_start(M, N, BM, BN);
+    if (m_tail == M) return run_big<BM, BN>(src, W, M, N, K, ep, ws, s);
+    hipError_t e = run_big<BM, BN>(src, W, m_tail, N, K, ep, nullptr, s);
+    if (e != hipSuccess) return e;
+    return run_big<128, 128>(rows_from(src, m_tail), W, M - m_tail, N, K, rows_from(ep, m_tail), nullptr, s);
+}
+
+template <int BM, int BN, class EP>
+hipError_t run_rows(SrcMerge src, const bf16_t *W, int64_t M, int N, int K, EP ep, const GemmWorkspace *ws,
+                    hipStream_t s)
+{
+    return run_big<BM, BN>(src, W, M, N, K, ep, ws, s);
+}
+
 template <class SRC>
 hipError_t dispatch(SRC src, const bf16_t *W, int64_t M, int N, int K, const bf16_t *bias, int act,
                     bool out_f32, void *out, const GemmWorkspace *ws, hipStream_t s)
@@ -728,14 +770,14 @@ hipError_t dispatch(SRC src, const bf16_t *W, int64_t M, int N, int K, const bf1
     const bool big = use_big_tiles(M, N);
     if (out_f32) {
         EpiF32 ep{(float *)out, bias, M, N};
-        return big ? run_big<256, 256>(src, W, M, N, K, ep, ws, s) : run_big<256, 128>(src, W, M, N, K, ep, ws, s);
+        return big ? run_rows<256, 256>(src, W, M, N, K, ep, ws, s) : run_rows<256, 128>(src, W, M, N, K, ep, ws, s);
     }
     if (act == ACT_GELU_TANH) {
         EpiBF16<ACT_GELU_TANH> ep{(bf16_t *)out, bias, M, N};
-        return big ? run_big<256, 256>(src, W, M, N, K, ep, ws, s) : run_big<256, 128>(src, W, M, N, K, ep, ws, s);
+        return big ? run_rows<256, 256>(src, W, M, N, K, ep, ws, s) : run_rows<256, 128>(src, W, M, N, K, ep, ws, s);
     }
     EpiBF16<ACT_NONE> ep{(bf16_t *)out, bias, M, N};
-    return big ? run_big<256, 256>(src, W, M, N, K, ep, ws, s) : run_big<256, 128>(src, W, M, N, K, ep, ws, s);
+    return big ? run_rows<256, 256>(src, W, M, N, K, ep, ws, s) : run_rows<256, 128>(src, W, M, N, K, ep, ws, s);
 }
 
 }  // namespace

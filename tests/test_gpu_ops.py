@@ -96,6 +96,28 @@ def test_linear_full_size_sampled(N, K, act):
 
 
 @pytest.mark.parametrize("act,out_f32", [(vit.ACT_GELU_TANH, False), (vit.ACT_NONE, True)])
+def test_linear_row_tail(act, out_f32):
+    """272 tiles of 256 x 256 on 256 compute units: the last round's tiles are whole tile
+    rows (rows 8192..8491, ragged), which run as a second launch of 128 x 128 tiles (ragged in
+    M and N); every row of that tail and rows on both sides of the seam are checked."""
+    torch = require_gpu()
+    enc, _, _ = encoder()
+    M, K, N = 8492, 1024, 2000
+    A = seeded_bf16((M, K), 108, 0)
+    W = seeded_bf16((N, K), 108, 1, std=0.02)
+    b = seeded_bf16((N,), 108, 2, std=0.02)
+    got = enc.op_linear(to_dev_bf16(A), to_dev_bf16(W), to_dev_bf16(b), act, out_f32)
+    torch.cuda.synchronize()
+    rows = np.r_[0:2, 4000:4002, 8188:M]
+    want = oracle.linear(f32(A[rows]), f32(W), f32(b), act=act, round_out=not out_f32, workers=8)
+    if out_f32:
+        g = got.cpu().numpy()[rows]
+        assert np.all(np.abs(g - want) <= sum_bound(A[rows], W) + 1e-6 * np.abs(want))
+    else:
+        assert_bf16_close(from_dev_bf16(got)[rows], want, atol=sum_bound(A[rows], W), what="row tail")
+
+
+@pytest.mark.parametrize("act,out_f32", [(vit.ACT_GELU_TANH, False), (vit.ACT_NONE, True)])
 def test_linear_split_k_tail(act, out_f32):
     """264 tiles of 256 x 128 on 256 compute units: the 8 leftover tiles (rows 8192..8399,
     ragged in M and N) are cut into K slices whose fp32 partials a second kernel sums."""

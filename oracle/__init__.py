@@ -373,3 +373,33 @@ def overlay(embeds_bits: np.ndarray, placeholder_rows, rows: np.ndarray) -> np.n
         if r >= 0:
             out[r] = float_to_bf16_bits(rows[t])
     return out
+
+
+def assemble(embeds_bits: np.ndarray, chunk_lo: int, chunk_hi: int, grids, span_start,
+             rows: np.ndarray, sentinels_bits: np.ndarray, merge: int = 3) -> np.ndarray:
+    """Embedding rows of one prefill chunk.  [Z] "Connect the complete image-to-text path":
+    each image placeholder becomes the span START, (IMAGE x mw, NEWLINE) x mh, END; the
+    aligner output replaces the IMAGE positions and learned vectors fill START, NEWLINE and
+    END; with chunked prefill an image span may cross a chunk boundary, and a chunk replaces
+    only the part of each span that lies inside it.
+
+    ``embeds_bits`` (bf16 bits, one row per prompt position chunk_lo .. chunk_hi-1) is copied;
+    image i's span starts at prompt position span_start[i]; IMAGE positions take the image's
+    visual rows (image-major, as the encoder emits them) rounded to bf16; the other span
+    positions take sentinels_bits[0 / 1 / 2] for START / NEWLINE / END."""
+    out = embeds_bits.copy()
+    which = {TOK_START: 0, TOK_NEWLINE: 1, TOK_END: 2}
+    first = 0   # first visual row of the current image
+    for (gh, gw), s0 in zip(grids, span_start):
+        types, src = layout([(gh, gw)], merge)
+        for k in range(len(types)):
+            p = s0 + k
+            if not chunk_lo <= p < chunk_hi:
+                continue
+            if types[k] == TOK_IMAGE:
+                out[p - chunk_lo] = float_to_bf16_bits(rows[first + src[k]])
+            else:
+                out[p - chunk_lo] = sentinels_bits[which[int(types[k])]]
+        first += (-(-gh // merge)) * (-(-gw // merge))
+    return out
+

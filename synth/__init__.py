@@ -263,6 +263,12 @@ def packed_grids_batch(seed: int = SEED_GRIDS, n_images: int = 16, merge: int = 
         attempt += 1
 
 
+def make_sentinels(hidden: int, seed: int = SEED_WEIGHTS, std: float = 0.02) -> np.ndarray:
+    """The three learned span vectors START, NEWLINE, END as bf16 bits [3][hidden], N(0, std)
+    (drawn from a stream of the weight seed that the blob does not use)."""
+    return normal_bf16(seed, 1 << 20, 3 * hidden, 0.0, std).reshape(3, hidden)
+
+
 def seeded_offsets(n: int, lo: int, hi: int, seed: int = SEED_OFFSETS, stream: int = 0):
     """n integers uniform in [lo, hi]."""
     u = uniform(seed, stream, n)

@@ -410,6 +410,77 @@ def test_overlay_rows():
     assert np.array_equal(oracle.bf16_to_float(out[7]), want)
 
 
+def _sentinels(hidden):
+    return synth.make_sentinels(hidden)
+
+
+def test_assemble_span_sequence():
+    """A 6x9 patch grid merges to 2x3 tokens: its span is S I0 I1 I2 N I3 I4 I5 N E (10
+    positions), placed here at prompt position 3 of a 16-row prompt; text rows stay as
+    they were."""
+    hidden = 8
+    sent = _sentinels(hidden)
+    rows = (np.arange(6 * hidden, dtype=np.float32).reshape(6, hidden) + 0.25) * 1.5
+    emb = (np.arange(16 * hidden) % 65000).astype(np.uint16).reshape(16, hidden)
+    out = oracle.assemble(emb, 0, 16, [(6, 9)], [3], rows, sent)
+    seq = ["S", 0, 1, 2, "N", 3, 4, 5, "N", "E"]
+    for k, tok in enumerate(seq):
+        got = out[3 + k]
+        if tok == "S":
+            assert np.array_equal(got, sent[0])
+        elif tok == "N":
+            assert np.array_equal(got, sent[1])
+        elif tok == "E":
+            assert np.array_equal(got, sent[2])
+        else:
+            assert np.array_equal(oracle.bf16_to_float(got), bf16_torch(rows[tok]))
+    keep = [0, 1, 2, 13, 14, 15]
+    assert np.array_equal(out[keep], emb[keep])
+
+
+def test_assemble_chunks_agree_with_one_pass():
+    """Chunked prefill: assembling the prompt in chunks of any size (a span crossing chunk
+    boundaries, a chunk inside one span, empty chunks) equals assembling it at once."""
+    hidden = 6
+    sent = _sentinels(hidden)
+    grids = [(6, 6), (5, 7), (3, 3)]
+    starts = [2, 16, 33]             # spans of 8, 10 and 4 positions, text in between
+    R = 40
+    n_vis = 4 + 6 + 1
+    rows = synth.normal_f32(7, 0, n_vis * hidden, 0.0, 1.0).reshape(n_vis, hidden)
+    emb = synth.normal_bf16(7, 1, R * hidden).reshape(R, hidden)
+    whole = oracle.assemble(emb, 0, R, grids, starts, rows, sent)
+    for cuts in ([0, 5, 11, 20, 21, 40], [0, 17, 17, 40], [0, 40], list(range(0, 41, 3)) + [40]):
+        parts = [oracle.assemble(emb[a:b], a, b, grids, starts, rows, sent)
+                 for a, b in zip(cuts[:-1], cuts[1:])]
+        assert np.array_equal(np.concatenate(parts), whole)
+
+
+def test_assemble_image_rows_match_overlay():
+    """The IMAGE positions of an assembled prompt are the overlay of the visual rows onto
+    those positions; the START/NEWLINE/END positions are the only other rows changed."""
+    hidden = 4
+    sent = _sentinels(hidden)
+    grids = [(7, 4), (3, 9)]
+    starts = [1, 20]
+    R = 36
+    rows = synth.normal_f32(8, 0, (6 + 3) * hidden).reshape(9, hidden)
+    emb = synth.normal_bf16(8, 1, R * hidden).reshape(R, hidden)
+    got = oracle.assemble(emb, 0, R, grids, starts, rows, sent)
+    place = []
+    for (gh, gw), s0 in zip(grids, starts):
+        types, src = oracle.layout([(gh, gw)])
+        place += [s0 + k for k in np.nonzero(types == oracle.TOK_IMAGE)[0]]
+    ov = oracle.overlay(emb, place, rows)
+    img = np.array(place)
+    assert np.array_equal(got[img], ov[img])
+    changed = np.nonzero((got != emb).any(axis=1))[0]
+    spans = set()
+    for (gh, gw), s0 in zip(grids, starts):
+        spans |= set(range(s0, s0 + 2 + -(-gh // 3) * (-(-gw // 3) + 1)))
+    assert set(changed) <= spans
+
+
 # ------------------------------------------------------------------------------------------
 # whole encoder
 # ------------------------------------------------------------------------------------------

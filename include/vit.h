@@ -126,6 +126,32 @@ vit_status vit_overlay(vit_ctx *ctx, uint16_t *d_embeds, int64_t n_embed_rows,
                        const int32_t *h_rows, const float *d_rows, int64_t n_rows,
                        int32_t hidden, void *stream);
 
+/* Learned embedding rows of an image span's non-IMAGE positions ([Z] "Connect the complete
+ * image-to-text path": the aligner output replaces the IMAGE positions and learned vectors
+ * fill the boundary and newline positions).  h_sentinels: host bf16 [3][hidden], rows START,
+ * NEWLINE, END, copied to the device before the call returns (replacing any earlier set).
+ * VIT_E_ARG if ctx or h_sentinels is NULL or hidden != out_hidden; VIT_E_NOMEM if the
+ * device copy cannot be allocated. */
+vit_status vit_set_sentinels(vit_ctx *ctx, const uint16_t *h_sentinels, int32_t hidden);
+
+/* Embedding assembly of one prefill chunk ([Z] "Connect the complete image-to-text path": an
+ * image span may cross a chunk boundary, so each image keeps its token range and a chunk
+ * replaces only the part of each span that lies inside it).
+ *   Image i's span, in vit_layout's order (START, per merged row mw IMAGE and one NEWLINE,
+ *   END: 2 + mh*(mw+1) positions), starts at prompt position h_span_start[i] (host).
+ *   d_embeds: bf16 [chunk_hi - chunk_lo][hidden]; row j is prompt position chunk_lo + j.
+ *   d_rows:   fp32 visual rows [vit_num_tokens(h_grids)][hidden] as vit_encode writes them.
+ * Every span position p in [chunk_lo, chunk_hi) is written: an IMAGE position takes the next
+ * visual row of its image (row-major merged order) rounded to bf16 (nearest even); START,
+ * NEWLINE and END take the rows set by vit_set_sentinels.  All other rows are left as they
+ * are; a chunk that meets no span launches nothing.  VIT_E_ARG if ctx is NULL, hidden !=
+ * out_hidden, chunk_lo < 0 or chunk_hi < chunk_lo, a grid is invalid (VIT_E_BUDGET over the
+ * token budget), a span start is negative, two spans overlap, no sentinels were set, or a
+ * pointer needed for the chunk is NULL.  Asynchronous on `stream`. */
+vit_status vit_assemble(vit_ctx *ctx, uint16_t *d_embeds, int64_t chunk_lo, int64_t chunk_hi,
+                        int32_t hidden, const vit_grid *h_grids, int32_t n_images,
+                        const int64_t *h_span_start, const float *d_rows, void *stream);
+
 /* Debug boundaries ([Z] "Step 2": compare patches, block outputs, final norm and aligner
  * input to find the earliest divergence).  vit_dump runs the encoder up to the boundary on
  * the given batch and copies that tensor into d_dst (dst_bytes must equal its size):

@@ -25,7 +25,8 @@ EXPORTS = ("vit_blob_elems", "vit_create", "vit_destroy", "vit_reserve", "vit_nu
            "vit_num_patches", "vit_encode", "vit_layout", "vit_overlay", "vit_dump",
            "vit_last_error", "vit_op_linear", "vit_op_layernorm", "vit_vt_stride", "vit_op_rope",
            "vit_op_attention", "vit_op_merge_project", "vit_timing_enable", "vit_timing_read",
-           "vit_set_attention_split", "vit_op_qkv_rope")
+           "vit_set_attention_split", "vit_op_qkv_rope", "vit_set_sentinels",
+           "vit_assemble")
 STEP_NAMES = ("patch_embed", "layernorm", "qkv", "rope", "attention", "out_proj", "fc1", "fc2",
               "projector", "overlay")
 
@@ -82,6 +83,8 @@ def lib():
             "vit_vt_stride": (i64, [P(Grid), i32]),
             "vit_op_rope": (i32, [vp, vp, vp, P(Grid), i32, vp]),
             "vit_op_qkv_rope": (i32, [vp, vp, vp, vp, P(Grid), i32, vp, vp, i32, vp]),
+            "vit_set_sentinels": (i32, [vp, vp, i32]),
+            "vit_assemble": (i32, [vp, vp, i64, i64, i32, P(Grid), i32, vp, vp, vp]),
             "vit_op_attention": (i32, [vp, vp, vp, P(Grid), i32, vp, vp]),
             "vit_op_merge_project": (i32, [vp, vp, P(Grid), i32, vp, vp]),
             "vit_timing_enable": (i32, [vp, i32]),
@@ -231,6 +234,22 @@ class Encoder:
                                       _ptr(visual_rows), r.size, int(embeds.shape[1]),
                                       _stream(stream)))
         return embeds
+
+    def set_sentinels(self, sentinels: np.ndarray):
+        """Learned START, NEWLINE, END rows: bf16 bits [3][out_hidden] (host)."""
+        s = np.ascontiguousarray(sentinels, dtype=np.uint16)
+        assert s.shape == (3, self.out_hidden)
+        self._check(lib().vit_set_sentinels(self._ctx, s.ctypes.data, self.out_hidden))
+
+    def assemble(self, chunk, chunk_lo, grids, span_start, visual_rows, stream=None):
+        """Write the span positions inside [chunk_lo, chunk_lo + len(chunk)) into chunk (bf16
+        CUDA tensor [rows][out_hidden], row j = prompt position chunk_lo + j)."""
+        st = np.ascontiguousarray(np.asarray(span_start, dtype=np.int64))
+        self._check(lib().vit_assemble(self._ctx, _ptr(chunk), int(chunk_lo),
+                                       int(chunk_lo) + int(chunk.shape[0]), int(chunk.shape[1]),
+                                       grid_array(grids), len(grids), st.ctypes.data,
+                                       _ptr(visual_rows), _stream(stream)))
+        return chunk
 
     # ---- single steps (include/vit_ops.h) ---------------------------------------------
     def op_linear(self, A, W, b, act=ACT_NONE, out_f32=False, stream=None):

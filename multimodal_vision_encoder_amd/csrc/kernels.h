@@ -81,6 +81,11 @@ hipError_t launch_attention(const bf16_t *qkv, const bf16_t *vt, int64_t ldv, bf
 // Compute units of the current device.
 int cu_count();
 
+// Chunk assembly: for each entry (row r, source v) of `entries` (int32 pairs), embeds[r] =
+// bf16(src[v]) when v >= 0, else the bf16 sentinel row -1 - v.
+hipError_t launch_assemble(uint16_t *embeds, const float *src, const uint16_t *sentinels,
+                           const int32_t *entries, int64_t n_entries, int hidden, hipStream_t s);
+
 // embeds[rows[t]] = bf16(src[t]) for rows[t] >= 0.
 hipError_t launch_overlay(uint16_t *embeds, const float *src, const int32_t *rows, int64_t n_rows,
                           int hidden, hipStream_t s);

@@ -40,6 +40,7 @@ struct vit_ctx {
 
     bf16_t *d_blob = nullptr, *d_wpe = nullptr, *d_wproj = nullptr;
     bf16_t *d_zero = nullptr;   // 256 zero bytes: the padding source of the merge gather
+    uint16_t *d_sentinels = nullptr;   // learned START, NEWLINE, END rows, bf16 [3][Dl]
     const bf16_t *pe_b = nullptr, *lnf_g = nullptr, *lnf_b = nullptr, *proj_b = nullptr;
     std::vector<Layer> layers;
     float *d_cos = nullptr, *d_sin = nullptr;
@@ -446,7 +447,7 @@ void destroy(vit_ctx *c)
     (void)hipDeviceSynchronize();
     free_workspace(c);
     void *bufs[] = {c->d_blob, c->d_wpe, c->d_wproj, c->d_cos, c->d_sin, c->d_meta, c->d_zero, c->d_gemm_ws,
-                    c->d_attn_ws};
+                    c->d_attn_ws, c->d_sentinels};
     for (void *b : bufs)
         if (b) (void)hipFree(b);
     if (c->h_stage) (void)hipHostFree(c->h_stage);
@@ -702,6 +703,79 @@ vit_status vit_overlay(vit_ctx *ctx, uint16_t *d_embeds, int64_t n_embed_rows,
     if (st != VIT_OK) return st;
     TLAUNCH(ctx, VIT_STEP_OVERLAY, (hipStream_t)stream, launch_overlay(d_embeds, d_rows, (const int32_t *)(ctx->d_meta + off[0]), n_rows,
                                hidden, (hipStream_t)stream));
+    return VIT_OK;
+}
+
+vit_status vit_set_sentinels(vit_ctx *ctx, const uint16_t *h_sentinels, int32_t hidden)
+{
+    if (!ctx) return fail(nullptr, VIT_E_ARG, "ctx is NULL");
+    if (hidden != ctx->Dl) return fail(ctx, VIT_E_ARG, "hidden does not match out_hidden");
+    if (!h_sentinels) return fail(ctx, VIT_E_ARG, "NULL pointer");
+    const size_t bytes = (size_t)3 * ctx->Dl * sizeof(uint16_t);
+    if (!ctx->d_sentinels) {
+        if (hipMalloc((void **)&ctx->d_sentinels, bytes) != hipSuccess) {
+            (void)hipGetLastError();
+            ctx->d_sentinels = nullptr;
+            return fail(ctx, VIT_E_NOMEM, "cannot allocate the sentinel rows");
+        }
+    }
+    HIP_TRY(ctx, hipMemcpy(ctx->d_sentinels, h_sentinels, bytes, hipMemcpyHostToDevice));
+    return VIT_OK;
+}
+
+vit_status vit_assemble(vit_ctx *ctx, uint16_t *d_embeds, int64_t chunk_lo, int64_t chunk_hi,
+                        int32_t hidden, const vit_grid *h_grids, int32_t n_images,
+                        const int64_t *h_span_start, const float *d_rows, void *stream)
+{
+    if (!ctx) return fail(nullptr, VIT_E_ARG, "ctx is NULL");
+    if (hidden != ctx->Dl) return fail(ctx, VIT_E_ARG, "hidden does not match out_hidden");
+    if (chunk_lo < 0 || chunk_hi < chunk_lo || chunk_hi - chunk_lo > INT32_MAX)
+        return fail(ctx, VIT_E_ARG, "bad chunk range");
+    Plan p;
+    vit_status st = make_plan(ctx, h_grids, n_images, p);
+    if (st != VIT_OK) return st;
+    if (n_images > 0 && !h_span_start) return fail(ctx, VIT_E_ARG, "NULL pointer");
+    if (!ctx->d_sentinels) return fail(ctx, VIT_E_ARG, "no sentinel rows: call vit_set_sentinels first");
+    // spans: START, mh x (mw IMAGE, NEWLINE), END; they must not overlap
+    std::vector<std::pair<int64_t, int64_t>> spans;
+    for (int i = 0; i < n_images; ++i) {
+        const ImgDesc &d = p.imgs[i];
+        if (h_span_start[i] < 0) return fail(ctx, VIT_E_ARG, "negative span start");
+        spans.push_back({h_span_start[i], 2 + (int64_t)d.mh * (d.mw + 1)});
+    }
+    std::vector<std::pair<int64_t, int64_t>> sorted = spans;
+    std::sort(sorted.begin(), sorted.end());
+    for (size_t i = 1; i < sorted.size(); ++i)
+        if (sorted[i].first < sorted[i - 1].first + sorted[i - 1].second)
+            return fail(ctx, VIT_E_ARG, "image spans overlap");
+    std::vector<int32_t> entries;   // (row of the chunk, source) pairs
+    for (int i = 0; i < n_images; ++i) {
+        const ImgDesc &d = p.imgs[i];
+        const int64_t s0 = spans[i].first, len = spans[i].second;
+        const int64_t lo = std::max(s0, chunk_lo), hi = std::min(s0 + len, chunk_hi);
+        for (int64_t pos = lo; pos < hi; ++pos) {
+            const int64_t k = pos - s0;
+            int32_t src;
+            if (k == 0) {
+                src = -1;                                   // START
+            } else if (k == len - 1) {
+                src = -3;                                   // END
+            } else {
+                const int64_t q = k - 1, r = q / (d.mw + 1), c = q - r * (d.mw + 1);
+                src = c == d.mw ? -2 : (int32_t)(d.tok_off + r * d.mw + c);   // NEWLINE or IMAGE
+            }
+            entries.push_back((int32_t)(pos - chunk_lo));
+            entries.push_back(src);
+        }
+    }
+    if (entries.empty()) return VIT_OK;
+    if (!d_embeds || !d_rows) return fail(ctx, VIT_E_ARG, "NULL pointer");
+    std::vector<size_t> off;
+    st = upload_meta(ctx, {{entries.data(), entries.size() * sizeof(int32_t)}}, (hipStream_t)stream, off);
+    if (st != VIT_OK) return st;
+    TLAUNCH(ctx, VIT_STEP_OVERLAY, (hipStream_t)stream,
+            launch_assemble(d_embeds, d_rows, ctx->d_sentinels, (const int32_t *)(ctx->d_meta + off[0]),
+                            (int64_t)entries.size() / 2, hidden, (hipStream_t)stream));
     return VIT_OK;
 }
 

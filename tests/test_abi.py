@@ -82,3 +82,6 @@ def test_null_context_is_rejected():
     assert L.vit_encode(None, None, g, 1, None, None) == vit.VIT_E_ARG
     assert L.vit_num_tokens(None, g, 1) == -1
     assert L.vit_overlay(None, None, 0, None, None, 0, 128, None) == vit.VIT_E_ARG
+    assert L.vit_set_sentinels(None, None, 128) == vit.VIT_E_ARG
+    assert L.vit_assemble(None, None, 0, 8, 128, g, 1, None, None, None) == vit.VIT_E_ARG
+    assert L.vit_op_qkv_rope(None, None, None, None, g, 1, None, None, 0, None) == vit.VIT_E_ARG

@@ -22,6 +22,7 @@ import numpy as np
 import pytest
 
 import multimodal_vision_encoder_amd as vit
+import oracle
 import synth
 from tests.gpu_util import assert_projector_gate, from_dev_bf16, rel_l2, require_gpu
 
@@ -141,3 +142,33 @@ def test_packed16_overlay_into_one_prompt():
     others = np.ones(R, bool)
     others[text + img] = False
     assert not e[others].any()
+
+
+def test_packed16_assemble_in_chunks():
+    """The packed batch's 8k visual rows and learned span rows assembled into one prompt (text
+    runs between spans) in prefill chunks of 1024 positions, the pages' cap with a projector
+    loaded: bitwise the oracle's assembly of the same rows."""
+    torch = require_gpu()
+    wl, enc, _, out = encoded("packed16")
+    Dl = wl.cfg.out_hidden
+    sent = synth.make_sentinels(Dl)
+    enc.set_sentinels(sent)
+    gaps = synth.seeded_offsets(len(wl.grids) + 1, 0, 64, stream=9)
+    starts, pos = [], 0
+    for (gh, gw), g in zip(wl.grids, gaps):
+        pos += g
+        starts.append(pos)
+        pos += 2 + -(-gh // 3) * (-(-gw // 3) + 1)
+    R = pos + gaps[-1]
+    rows = out.cpu().numpy()
+    emb = np.zeros((R, Dl), np.uint16)
+    want = oracle.assemble(emb, 0, R, wl.grids, starts, rows, sent)
+    got = np.zeros_like(emb)
+    for a in range(0, R, 1024):
+        b = min(R, a + 1024)
+        d = torch.zeros((b - a, Dl), dtype=torch.bfloat16, device="cuda")
+        enc.assemble(d, a, wl.grids, starts, out)
+        torch.cuda.synchronize()
+        got[a:b] = d.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, want)
+

@@ -441,3 +441,53 @@ def test_overlay_exact():
     want = oracle.overlay(emb, dst, rows)
     got = d_emb.view(torch.int16).cpu().numpy().view(np.uint16)
     assert np.array_equal(got, want)
+
+
+def _prompt(grids, gaps, seed):
+    """Span starts for images separated by text runs of the given lengths, and the prompt
+    length (a last text run of gaps[-1] rows)."""
+    starts, pos = [], 0
+    for (gh, gw), g in zip(grids, gaps):
+        pos += g
+        starts.append(pos)
+        pos += 2 + -(-gh // 3) * (-(-gw // 3) + 1)
+    return starts, pos + gaps[-1]
+
+
+def test_assemble_chunks_exact():
+    """Learned START/NEWLINE/END rows and the visual rows of four images, written into a
+    prompt whole and chunk by chunk (a chunk inside one span, cuts through spans, an empty
+    chunk): bitwise the oracle's assembly, other rows untouched."""
+    torch = require_gpu()
+    cfg = synth.TINY
+    enc = vit.Encoder(cfg, synth.make_weights(cfg))
+    Dl = cfg.out_hidden
+    sent = synth.make_sentinels(Dl)
+    grids = [(6, 6), (5, 7), (3, 3), (1, 1)]
+    starts, R = _prompt(grids, [3, 0, 5, 1, 4], 0)
+    n_vis = sum(-(-gh // 3) * -(-gw // 3) for gh, gw in grids)
+    rows = synth.normal_f32(114, 0, n_vis * Dl, 0.0, 3.0).reshape(n_vis, Dl)
+    emb = seeded_bf16((R, Dl), 114, 1)
+    d_rows = torch.from_numpy(rows).cuda()
+    with pytest.raises(vit.VitError):   # no sentinel rows yet
+        enc.assemble(to_dev_bf16(emb), 0, grids, starts, d_rows)
+    enc.set_sentinels(sent)
+    want = oracle.assemble(emb, 0, R, grids, starts, rows, sent)
+    d = to_dev_bf16(emb)
+    enc.assemble(d, 0, grids, starts, d_rows)
+    torch.cuda.synchronize()
+    assert np.array_equal(d.view(torch.int16).cpu().numpy().view(np.uint16), want)
+    for cuts in ([0, 7, 8, 8, 20, R], [0, 4, 12, R], list(range(0, R, 5)) + [R]):
+        parts = []
+        for a, b in zip(cuts[:-1], cuts[1:]):
+            d = to_dev_bf16(emb[a:b]) if b > a else torch.empty((0, Dl), dtype=torch.bfloat16, device="cuda")
+            enc.assemble(d, a, grids, starts, d_rows)
+            torch.cuda.synchronize()
+            parts.append(d.view(torch.int16).cpu().numpy().view(np.uint16).reshape(b - a, Dl))
+        assert np.array_equal(np.concatenate(parts), want)
+    with pytest.raises(vit.VitError):   # overlapping spans
+        enc.assemble(to_dev_bf16(emb), 0, grids[:2], [starts[0], starts[0] + 3], d_rows)
+    with pytest.raises(vit.VitError):   # negative span start
+        enc.assemble(to_dev_bf16(emb), 0, grids[:1], [-1], d_rows)
+    enc.close()
+

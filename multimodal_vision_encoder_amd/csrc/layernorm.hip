@@ -19,14 +19,6 @@ __device__ __forceinline__ float wave_sum(float v)
     return v;
 }
 
-// Column of element e held by `lane`: 16-byte chunks when EPL >= 8, else EPL contiguous.
-template <int EPL>
-__device__ __forceinline__ int col_of(int lane, int e)
-{
-    if constexpr (EPL >= 8) return (e >> 3) * 512 + lane * 8 + (e & 7);
-    else return lane * EPL + e;
-}
-
 template <int EPL>
 __device__ __forceinline__ void load_row(const bf16_t *p, int lane, float *v)
 {
@@ -98,12 +90,15 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const bf16_t *__restrict
     }
     const float var = wave_sum(ss) / (float)D;
     const float den = sqrtf(var + eps);
+    // gamma and beta in the same lane layout as the row (16-byte loads)
+    float gv[EPL], bv[EPL];
+    load_row<EPL>(g, lane, gv);
+    load_row<EPL>(b, lane, bv);
     float y[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
 #pragma clang fp contract(off)
-        const int c = col_of<EPL>(lane, e);
-        y[e] = __fadd_rn(__fmul_rn(__fdiv_rn(v[e] - mu, den), bf16_to_f32(g[c])), bf16_to_f32(b[c]));
+        y[e] = __fadd_rn(__fmul_rn(__fdiv_rn(v[e] - mu, den), gv[e]), bv[e]);
     }
     store_row<EPL>(out + row * D, lane, y);
 }

@@ -126,6 +126,42 @@ vit_status vit_overlay(vit_ctx *ctx, uint16_t *d_embeds, int64_t n_embed_rows,
                        const int32_t *h_rows, const float *d_rows, int64_t n_rows,
                        int32_t hidden, void *stream);
 
+/* Preprocessing plan of one image ([Z] "Step 1": the largest grid that fits the aspect ratio
+ * and the token budget, sides constrained to the patch x merge grid, contain resize, the result
+ * centred on RGB 127 gray; images below the minimum pixel count are enlarged proportionally
+ * first; [G] V4.1 row: 1024 tokens, minimum 295,936 pixels, no aspect clamp; V4 Flash row:
+ * 384 tokens, minimum 147,456 pixels, aspect clamped to 8:1).  Readings where the pages are
+ * silent: enlargement by sqrt(min_pixels / (height * width)) without rounding; the aspect clamp
+ * lengthens the short side of the planning size; with a = H/(patch*merge), b = W/(patch*merge)
+ * the grid is (round(a), round(b)) (ties to even, at least 1) when a*b fits the budget, else
+ * floor(a r) x floor(b r) with r = sqrt(budget / (a b)) grown one row or column at a time while
+ * the budget allows, each step keeping log(columns / rows) closest to log(b / a) (rows first
+ * on a tie); contain: the limiting side fills the canvas, the other is
+ * round(other * canvas side / limiting side), ties to even, at least 1; offsets are
+ * floor((canvas - resized) / 2).  Host only.  VIT_E_ARG for sizes outside 1..65536 or negative
+ * parameters (max_aspect 0 = no clamp). */
+typedef struct {
+    int32_t gh, gw;                /* patch grid of the canvas (multiples of merge) */
+    int32_t canvas_h, canvas_w;    /* canvas pixels: patch * gh x patch * gw */
+    int32_t resized_h, resized_w;  /* the contained image inside the canvas */
+    int32_t off_y, off_x;          /* its top-left corner in the canvas */
+} vit_image_plan;
+vit_status vit_plan_image(int32_t height, int32_t width, int32_t patch, int32_t merge, int32_t max_tokens,
+                          int64_t min_pixels, int32_t max_aspect, vit_image_plan *out);
+
+/* The canvas of a plan ([Z] "Step 1" items 3-4): d_src = uint8 RGB HWC [height][width][3],
+ * d_canvas = uint8 RGB HWC [canvas_h][canvas_w][3] (device, caller-owned), the image resized to
+ * resized_h x resized_w at (off_y, off_x) and 127 elsewhere; ready for vit_encode with grid
+ * (gh, gw).  Resize: the Keys cubic convolution (a = -0.5), separable, sample i of an axis at
+ * source coordinate (i + 0.5) * in/out, the kernel stretched by in/out when shrinking, taps
+ * outside the image dropped and the weights renormalised, horizontal pass first in fp32,
+ * rounded half to even and clamped to 0..255 at the end.  A context scratch of
+ * height * resized_w * 12 bytes is grown on demand.  VIT_E_ARG if a pointer is NULL or the
+ * plan does not fit the canvas or the context's patch size; VIT_E_NOMEM if the scratch cannot
+ * be allocated.  Asynchronous on `stream`. */
+vit_status vit_preprocess(vit_ctx *ctx, const uint8_t *d_src, int32_t height, int32_t width,
+                          const vit_image_plan *plan, uint8_t *d_canvas, void *stream);
+
 /* Learned embedding rows of an image span's non-IMAGE positions ([Z] "Connect the complete
  * image-to-text path": the aligner output replaces the IMAGE positions and learned vectors
  * fill the boundary and newline positions).  h_sentinels: host bf16 [3][hidden], rows START,

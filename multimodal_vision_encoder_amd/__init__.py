@@ -26,7 +26,7 @@ EXPORTS = ("vit_blob_elems", "vit_create", "vit_destroy", "vit_reserve", "vit_nu
            "vit_last_error", "vit_op_linear", "vit_op_layernorm", "vit_vt_stride", "vit_op_rope",
            "vit_op_attention", "vit_op_merge_project", "vit_timing_enable", "vit_timing_read",
            "vit_set_attention_split", "vit_op_qkv_rope", "vit_set_sentinels",
-           "vit_assemble")
+           "vit_assemble", "vit_plan_image", "vit_preprocess")
 STEP_NAMES = ("patch_embed", "layernorm", "qkv", "rope", "attention", "out_proj", "fc1", "fc2",
               "projector", "overlay")
 
@@ -54,6 +54,22 @@ class Weights(ctypes.Structure):
 
 
 _lib = None
+
+
+class ImagePlan(ctypes.Structure):
+    _fields_ = [("gh", ctypes.c_int32), ("gw", ctypes.c_int32), ("canvas_h", ctypes.c_int32),
+                ("canvas_w", ctypes.c_int32), ("resized_h", ctypes.c_int32), ("resized_w", ctypes.c_int32),
+                ("off_y", ctypes.c_int32), ("off_x", ctypes.c_int32)]
+
+
+def plan_image(height, width, patch=14, merge=3, max_tokens=1024, min_pixels=295936, max_aspect=0) -> dict:
+    """vit_plan_image: token grid, canvas and contain geometry of one image."""
+    p = ImagePlan()
+    st = lib().vit_plan_image(int(height), int(width), int(patch), int(merge), int(max_tokens),
+                              int(min_pixels), int(max_aspect), ctypes.byref(p))
+    if st != VIT_OK:
+        raise VitError(st, lib().vit_last_error(None).decode())
+    return {k: getattr(p, k) for k, _ in ImagePlan._fields_}
 
 
 def lib():
@@ -84,6 +100,8 @@ def lib():
             "vit_op_rope": (i32, [vp, vp, vp, P(Grid), i32, vp]),
             "vit_op_qkv_rope": (i32, [vp, vp, vp, vp, P(Grid), i32, vp, vp, i32, vp]),
             "vit_set_sentinels": (i32, [vp, vp, i32]),
+            "vit_plan_image": (i32, [i32, i32, i32, i32, i32, i64, i32, P(ImagePlan)]),
+            "vit_preprocess": (i32, [vp, vp, i32, i32, P(ImagePlan), vp, vp]),
             "vit_assemble": (i32, [vp, vp, i64, i64, i32, P(Grid), i32, vp, vp, vp]),
             "vit_op_attention": (i32, [vp, vp, vp, P(Grid), i32, vp, vp]),
             "vit_op_merge_project": (i32, [vp, vp, P(Grid), i32, vp, vp]),
@@ -234,6 +252,16 @@ class Encoder:
                                       _ptr(visual_rows), r.size, int(embeds.shape[1]),
                                       _stream(stream)))
         return embeds
+
+    def preprocess(self, src, height, width, plan: dict, stream=None):
+        """The gray canvas of `plan` (uint8 CUDA tensor [canvas_h][canvas_w][3]) from src (uint8
+        CUDA tensor, HWC height x width x 3)."""
+        import torch
+        p = ImagePlan(**plan)
+        canvas = torch.empty((plan["canvas_h"], plan["canvas_w"], 3), dtype=torch.uint8, device=src.device)
+        self._check(lib().vit_preprocess(self._ctx, _ptr(src), int(height), int(width), ctypes.byref(p),
+                                         _ptr(canvas), _stream(stream)))
+        return canvas
 
     def set_sentinels(self, sentinels: np.ndarray):
         """Learned START, NEWLINE, END rows: bf16 bits [3][out_hidden] (host)."""

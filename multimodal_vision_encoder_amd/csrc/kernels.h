@@ -81,6 +81,11 @@ hipError_t launch_attention(const bf16_t *qkv, const bf16_t *vt, int64_t ldv, bf
 // Compute units of the current device.
 int cu_count();
 
+// Contain resize (bicubic) of a uint8 HWC image h x w into the oh x ow region at (oy, ox) of a
+// ch x cw canvas, 127 elsewhere; tmp is fp32 scratch of h * ow * 3 floats.
+hipError_t launch_preprocess(const uint8_t *src, int h, int w, float *tmp, int oh, int ow, uint8_t *canvas,
+                             int ch, int cw, int oy, int ox, hipStream_t s);
+
 // Chunk assembly: for each entry (row r, source v) of `entries` (int32 pairs), embeds[r] =
 // bf16(src[v]) when v >= 0, else the bf16 sentinel row -1 - v.
 hipError_t launch_assemble(uint16_t *embeds, const float *src, const uint16_t *sentinels,

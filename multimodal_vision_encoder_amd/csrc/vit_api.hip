@@ -41,6 +41,8 @@ struct vit_ctx {
     bf16_t *d_blob = nullptr, *d_wpe = nullptr, *d_wproj = nullptr;
     bf16_t *d_zero = nullptr;   // 256 zero bytes: the padding source of the merge gather
     uint16_t *d_sentinels = nullptr;   // learned START, NEWLINE, END rows, bf16 [3][Dl]
+    float *d_pre_ws = nullptr;         // preprocessing scratch (horizontal resize pass)
+    size_t pre_ws_bytes = 0;
     const bf16_t *pe_b = nullptr, *lnf_g = nullptr, *lnf_b = nullptr, *proj_b = nullptr;
     std::vector<Layer> layers;
     float *d_cos = nullptr, *d_sin = nullptr;
@@ -447,7 +449,7 @@ void destroy(vit_ctx *c)
     (void)hipDeviceSynchronize();
     free_workspace(c);
     void *bufs[] = {c->d_blob, c->d_wpe, c->d_wproj, c->d_cos, c->d_sin, c->d_meta, c->d_zero, c->d_gemm_ws,
-                    c->d_attn_ws, c->d_sentinels};
+                    c->d_attn_ws, c->d_sentinels, c->d_pre_ws};
     for (void *b : bufs)
         if (b) (void)hipFree(b);
     if (c->h_stage) (void)hipHostFree(c->h_stage);
@@ -703,6 +705,98 @@ vit_status vit_overlay(vit_ctx *ctx, uint16_t *d_embeds, int64_t n_embed_rows,
     if (st != VIT_OK) return st;
     TLAUNCH(ctx, VIT_STEP_OVERLAY, (hipStream_t)stream, launch_overlay(d_embeds, d_rows, (const int32_t *)(ctx->d_meta + off[0]), n_rows,
                                hidden, (hipStream_t)stream));
+    return VIT_OK;
+}
+
+vit_status vit_plan_image(int32_t height, int32_t width, int32_t patch, int32_t merge, int32_t max_tokens,
+                          int64_t min_pixels, int32_t max_aspect, vit_image_plan *out)
+{
+    if (!out) return fail(nullptr, VIT_E_ARG, "out is NULL");
+    if (height < 1 || width < 1 || height > 65536 || width > 65536 || patch < 1 || merge < 1 ||
+        max_tokens < 1 || min_pixels < 0 || max_aspect < 0)
+        return fail(nullptr, VIT_E_ARG, "bad image size or planning parameter");
+    const double u = (double)patch * merge;
+    double H1 = height, W1 = width;
+    const double px = (double)height * width;
+    if (px < (double)min_pixels) {   // enlarged proportionally first
+        const double sc = std::sqrt((double)min_pixels / px);
+        H1 *= sc;
+        W1 *= sc;
+    }
+    if (max_aspect > 0) {            // planning aspect limited to max_aspect : 1
+        if (W1 > max_aspect * H1) H1 = W1 / max_aspect;
+        else if (H1 > max_aspect * W1) W1 = H1 / max_aspect;
+    }
+    const double a = H1 / u, b = W1 / u;
+    int64_t mh = 0, mw = 0;
+    if (a * b <= (double)max_tokens) {   // the image fits the budget: nearest grid
+        mh = std::max<int64_t>(1, (int64_t)std::nearbyint(a));
+        mw = std::max<int64_t>(1, (int64_t)std::nearbyint(b));
+    }
+    if (mh * mw == 0 || mh * mw > max_tokens) {   // largest grid of the image's aspect in the budget
+        const double r = std::sqrt((double)max_tokens / (a * b));
+        mh = std::max<int64_t>(1, (int64_t)std::floor(a * r));
+        mw = std::max<int64_t>(1, (int64_t)std::floor(b * r));
+        const double target = std::log(b / a);
+        for (;;) {
+            const bool rows_ok = (mh + 1) * mw <= max_tokens, cols_ok = mh * (mw + 1) <= max_tokens;
+            if (!rows_ok && !cols_ok) break;
+            const double er = rows_ok ? std::fabs(std::log((double)mw / (double)(mh + 1)) - target) : 0.0;
+            const double ec = cols_ok ? std::fabs(std::log((double)(mw + 1) / (double)mh) - target) : 0.0;
+            if (rows_ok && (!cols_ok || er <= ec)) ++mh;
+            else ++mw;
+        }
+    }
+    if (mh * merge * patch > 65536 || mw * merge * patch > 65536) return fail(nullptr, VIT_E_ARG, "canvas too large");
+    vit_image_plan p{};
+    p.gh = (int32_t)(mh * merge);
+    p.gw = (int32_t)(mw * merge);
+    p.canvas_h = p.gh * patch;
+    p.canvas_w = p.gw * patch;
+    // contain: the limiting side fills the canvas, the other is rounded (half to even)
+    auto round_div = [](int64_t num, int64_t den) {
+        int64_t q = num / den, r = num % den;
+        if (2 * r > den || (2 * r == den && (q & 1))) ++q;
+        return q;
+    };
+    if ((int64_t)width * p.canvas_h >= (int64_t)height * p.canvas_w) {
+        p.resized_w = p.canvas_w;
+        p.resized_h = (int32_t)std::max<int64_t>(1, round_div((int64_t)height * p.canvas_w, width));
+    } else {
+        p.resized_h = p.canvas_h;
+        p.resized_w = (int32_t)std::max<int64_t>(1, round_div((int64_t)width * p.canvas_h, height));
+    }
+    p.off_y = (p.canvas_h - p.resized_h) / 2;
+    p.off_x = (p.canvas_w - p.resized_w) / 2;
+    *out = p;
+    return VIT_OK;
+}
+
+vit_status vit_preprocess(vit_ctx *ctx, const uint8_t *d_src, int32_t height, int32_t width,
+                          const vit_image_plan *plan, uint8_t *d_canvas, void *stream)
+{
+    if (!ctx) return fail(nullptr, VIT_E_ARG, "ctx is NULL");
+    if (!plan || !d_src || !d_canvas) return fail(ctx, VIT_E_ARG, "NULL pointer");
+    const vit_image_plan &p = *plan;
+    if (height < 1 || width < 1 || p.gh < 1 || p.gw < 1 || p.canvas_h != p.gh * ctx->ps ||
+        p.canvas_w != p.gw * ctx->ps || p.resized_h < 1 || p.resized_w < 1 || p.off_y < 0 || p.off_x < 0 ||
+        p.off_y + p.resized_h > p.canvas_h || p.off_x + p.resized_w > p.canvas_w)
+        return fail(ctx, VIT_E_ARG, "plan does not fit the image or the context's patch size");
+    const size_t need = (size_t)height * p.resized_w * 3 * sizeof(float);
+    if (need > ctx->pre_ws_bytes) {
+        if (hipDeviceSynchronize() != hipSuccess) (void)hipGetLastError();
+        if (ctx->d_pre_ws) (void)hipFree(ctx->d_pre_ws);
+        ctx->d_pre_ws = nullptr;
+        ctx->pre_ws_bytes = 0;
+        if (hipMalloc((void **)&ctx->d_pre_ws, need) != hipSuccess) {
+            (void)hipGetLastError();
+            ctx->d_pre_ws = nullptr;
+            return fail(ctx, VIT_E_NOMEM, "cannot allocate the resize scratch");
+        }
+        ctx->pre_ws_bytes = need;
+    }
+    LAUNCH(ctx, launch_preprocess(d_src, height, width, ctx->d_pre_ws, p.resized_h, p.resized_w, d_canvas,
+                                  p.canvas_h, p.canvas_w, p.off_y, p.off_x, (hipStream_t)stream));
     return VIT_OK;
 }
 

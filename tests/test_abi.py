@@ -85,3 +85,21 @@ def test_null_context_is_rejected():
     assert L.vit_set_sentinels(None, None, 128) == vit.VIT_E_ARG
     assert L.vit_assemble(None, None, 0, 8, 128, g, 1, None, None, None) == vit.VIT_E_ARG
     assert L.vit_op_qkv_rope(None, None, None, None, g, 1, None, None, 0, None) == vit.VIT_E_ARG
+
+
+def test_plan_image_matches_oracle():
+    """The library's preprocessing planner (host logic) gives the oracle's integers exactly on
+    seeded sizes, the workload images and degenerate ones, for the V4.1 and V4 rules."""
+    from oracle import preprocess as pp
+    rng = np.random.default_rng(21)
+    profiles = (dict(max_tokens=1024, min_pixels=295936, max_aspect=0),
+                dict(max_tokens=384, min_pixels=147456, max_aspect=8))
+    sizes = [(1344, 1344), (756, 882), (1, 1), (1, 5000), (5000, 1), (14, 14), (42, 42 * 97)]
+    sizes += [tuple(int(x) for x in np.exp(rng.uniform(0, np.log(8000), 2))) for _ in range(500)]
+    for prof in profiles:
+        for h, w in sizes:
+            assert vit.plan_image(h, w, **prof) == pp.plan_image(h, w, **prof), (h, w, prof)
+    with pytest.raises(vit.VitError):
+        vit.plan_image(0, 10)
+    with pytest.raises(vit.VitError):
+        vit.plan_image(10, 10, max_tokens=0)

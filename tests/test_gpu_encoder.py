@@ -222,3 +222,61 @@ def test_deterministic_and_isolated():
     torch.cuda.synchronize()
     assert np.array_equal(a, b)
     assert np.array_equal(a[4 * 5:], alone)
+
+
+# ------------------------------------------------------------------------------------------
+# preprocessing: contain resize onto the gray canvas
+# ------------------------------------------------------------------------------------------
+_V41P = dict(max_tokens=1024, min_pixels=295936, max_aspect=0)
+_V4P = dict(max_tokens=384, min_pixels=147456, max_aspect=8)
+
+
+@pytest.mark.parametrize("h,w,prof", [(1344, 1344, _V41P), (1000, 700, _V41P), (2900, 1900, _V41P),
+                                      (200, 150, _V41P), (300, 2900, _V4P), (9, 400, _V4P), (1, 1, _V4P)],
+                         ids=["same-size", "enlarge-to-grid", "shrink", "min-pixels", "aspect-clamp",
+                              "thin", "single-pixel"])
+def test_preprocess_canvas_matches_oracle(h, w, prof):
+    """The GPU canvas against the oracle's (fp64 weights and sums): the gray padding and the
+    placement exact, every resized pixel within one level.  Off-by-one levels come from the
+    fp32 sums (two passes of up to ~16 taps of values <= 255: absolute error about 2e-3) landing
+    on the other side of a .5 than the fp64 ones; with fractional parts spread uniformly that is
+    about 0.4% of the pixels, so at most 0.5% may differ."""
+    from oracle import preprocess as pp
+    torch = require_gpu()
+    enc = vit.Encoder(synth.TINY, synth.make_weights(synth.TINY))
+    img = synth.uniform_bytes(31, h, h * w * 3).reshape(h, w, 3)
+    plan = vit.plan_image(h, w, **prof)
+    got = enc.preprocess(torch.from_numpy(img).cuda(), h, w, plan)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    want = pp.preprocess(img, plan)
+    assert got.shape == want.shape
+    diff = np.abs(got.astype(np.int32) - want.astype(np.int32))
+    y0, x0, rh, rw = plan["off_y"], plan["off_x"], plan["resized_h"], plan["resized_w"]
+    pad = np.ones(got.shape[:2], bool)
+    pad[y0:y0 + rh, x0:x0 + rw] = False
+    assert (got[pad] == 127).all()
+    assert diff.max() <= 1
+    assert (diff > 0).mean() <= 5e-3
+    enc.close()
+
+
+def test_preprocess_then_encode():
+    """A 100 x 160 image through the whole chain on the GPU (plan, canvas, encode) against the
+    oracle's canvas encoded by the oracle: the projector gate."""
+    from oracle import preprocess as pp
+    torch = require_gpu()
+    cfg = synth.TINY
+    blob = synth.make_weights(cfg)
+    enc = vit.Encoder(cfg, blob)
+    h, w = 100, 160
+    img = synth.uniform_bytes(32, 0, h * w * 3).reshape(h, w, 3)
+    plan = vit.plan_image(h, w, patch=cfg.patch, merge=3, max_tokens=cfg.max_tokens_per_image,
+                          min_pixels=295936, max_aspect=0)
+    grids = [(plan["gh"], plan["gw"])]
+    canvas = enc.preprocess(torch.from_numpy(img).cuda(), h, w, plan)
+    got = enc.encode(canvas.reshape(-1), grids)
+    torch.cuda.synchronize()
+    want = oracle.encode(cfg, blob, pp.preprocess(img, plan).reshape(-1), grids, workers=8)
+    assert_projector_gate(got.cpu().numpy(), want, "preprocess + encode")
+    enc.close()

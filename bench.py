@@ -96,6 +96,58 @@ def cpu_baseline(cfg, blob, px, grids):
             "seconds_per_pass": t_pass}
 
 
+def around_the_path(enc, cfg, grids, out, reps):
+    """The steps before and after the timed path, timed alone with events on the current
+    stream: preprocessing of a 3000 x 2000 photo-sized image onto the first image's canvas
+    (bicubic contain resize), and the chunk assembly of the visual rows plus the learned span
+    rows into one prompt.  Algorithmic bytes: preprocessing reads the image and writes the
+    canvas, with the fp32 intermediate [H][resized_w][3] written and read once; assembly reads
+    each fp32 visual row and writes each bf16 span row."""
+    import numpy as np
+    import torch
+    import multimodal_vision_encoder_amd as vit
+    import synth
+    res = {}
+    gh, gw = grids[0]
+    H, W = 2000, 3000
+    plan = vit.plan_image(H, W, patch=cfg.patch, merge=3, max_tokens=cfg.max_tokens_per_image,
+                          min_pixels=0, max_aspect=0)
+    img = torch.from_numpy(synth.uniform_bytes(41, 0, H * W * 3)).cuda()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    enc.preprocess(img, H, W, plan)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        enc.preprocess(img, H, W, plan)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / reps * 1e3
+    by = H * W * 3 + 2 * H * plan["resized_w"] * 3 * 4 + plan["canvas_h"] * plan["canvas_w"] * 3
+    res["preprocess"] = {"image": [H, W], "canvas": [plan["canvas_h"], plan["canvas_w"]], "us": us,
+                         "gbs": by / (us * 1e-6) / 1e9, "hbm_frac": by / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
+    types, _ = vit.layout(grids)
+    R = 64 + types.size
+    enc.set_sentinels(synth.make_sentinels(cfg.out_hidden))
+    chunk = torch.zeros((R, cfg.out_hidden), dtype=torch.bfloat16, device="cuda")
+    starts, pos = [], 64
+    for g in grids:
+        starts.append(pos)
+        pos += 2 + -(-g[0] // 3) * (-(-g[1] // 3) + 1)
+    enc.assemble(chunk, 0, grids, starts, out)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        enc.assemble(chunk, 0, grids, starts, out)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / reps * 1e3
+    n_img = int((types == vit.TOK_IMAGE).sum())
+    by = n_img * cfg.out_hidden * (4 + 2) + (types.size - n_img) * cfg.out_hidden * 4
+    res["assemble"] = {"positions": int(types.size), "us": us, "gbs": by / (us * 1e-6) / 1e9,
+                       "hbm_frac": by / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
+    return res
+
+
 def attention_traffic():
     """(bytes per launch, note) from the committed counter summary, or (None, reason)."""
     import hashlib
@@ -247,6 +299,7 @@ def main():
                                   "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                   "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
                                   "traffic_unit": "bytes per launch", "traffic_note": note}
+        result["around_the_path"] = around_the_path(enc, cfg, grids, out, args.steps)
         log(json.dumps(kernels, indent=1))
 
     if not args.no_cpu_baseline:

@@ -63,6 +63,12 @@ class _Lib:
         L.orc_round_bf16_array.argtypes = [vp, i64]
         L.orc_gelu_tanh.restype = r
         L.orc_gelu_tanh.argtypes = [r]
+        L.orc_gelu_erf.restype = r
+        L.orc_gelu_erf.argtypes = [r]
+        L.orc_silu.restype = r
+        L.orc_silu.argtypes = [r]
+        L.orc_swiglu.argtypes = [vp, vp, i64, vp]
+        L.orc_rmsnorm.argtypes = [vp, i64, i64, i64, i32, vp, r, vp, i64]
         L.orc_patchify.argtypes = [vp, i32, i32, i32, vp, vp, vp]
         L.orc_linear.restype = i32
         L.orc_linear.argtypes = [vp, i64, i64, i64, i32, vp, vp, i32, i32, i32, vp, i64]
@@ -141,6 +147,14 @@ def gelu_tanh(u: float, prec: str = "f32") -> float:
     return lib(prec).L.orc_gelu_tanh(u)
 
 
+def gelu_erf(u: float, prec: str = "f32") -> float:
+    return lib(prec).L.orc_gelu_erf(u)
+
+
+def silu(u: float, prec: str = "f32") -> float:
+    return lib(prec).L.orc_silu(u)
+
+
 def patchify(img: np.ndarray, gh: int, gw: int, cfg, prec: str = "f32") -> np.ndarray:
     """[Z] "Step 1" items 5-6: one bf16 row per 14x14 patch, (c, y, x) inside the row."""
     L = lib(prec)
@@ -187,6 +201,62 @@ def layernorm(x: np.ndarray, g: np.ndarray, b: np.ndarray, eps: float, prec: str
     _run(lambda r0, r1: L.L.orc_layernorm(_p(x), D, r0, r1, D, _p(g), _p(b), eps, _p(out), D),
          M, workers)
     return out
+
+
+def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float, prec: str = "f32",
+            workers: int = 1) -> np.ndarray:
+    """Official tower norm: bf16(x / sqrt(mean(x^2) + eps) * g) per row."""
+    L = lib(prec)
+    x = np.ascontiguousarray(x, dtype=L.dtype)
+    g = np.ascontiguousarray(g, dtype=L.dtype)
+    M, D = x.shape
+    out = np.empty_like(x)
+    _run(lambda r0, r1: L.L.orc_rmsnorm(_p(x), D, r0, r1, D, _p(g), eps, _p(out), D), M, workers)
+    return out
+
+
+def swiglu(g: np.ndarray, u: np.ndarray, prec: str = "f32") -> np.ndarray:
+    """bf16(silu(g) * u) elementwise on the unrounded gate and up projections."""
+    L = lib(prec)
+    g = np.ascontiguousarray(g, dtype=L.dtype)
+    u = np.ascontiguousarray(u, dtype=L.dtype)
+    assert g.shape == u.shape
+    out = np.empty_like(g)
+    L.L.orc_swiglu(_p(g), _p(u), g.size, _p(out))
+    return out
+
+
+def norm(cfg, x: np.ndarray, W, name: str, **kw) -> np.ndarray:
+    """The configured norm of a block or the final norm: LayerNorm (gamma, beta) or, in the
+    official-layer variant, RMSNorm (gamma only)."""
+    if cfg.norm_kind == 1:
+        return rmsnorm(x, W[name + ".g"], cfg.ln_eps, **kw)
+    return layernorm(x, W[name + ".g"], W[name + ".b"], cfg.ln_eps, **kw)
+
+
+def mlp(cfg, x: np.ndarray, W, l: int, **kw) -> np.ndarray:
+    """The block's MLP: fc2(GELU(fc1 x)) with the configured GELU form, or, in the
+    official-layer variant, down(silu(gate x) * up x) (SwiGLU)."""
+    if cfg.mlp_kind == 1:
+        g = linear(x, None, W[f"l{l}.gate.b"], round_out=False, Wt=W.T(f"l{l}.gate.w"), **kw)
+        u = linear(x, None, W[f"l{l}.up.b"], round_out=False, Wt=W.T(f"l{l}.up.w"), **kw)
+        h = swiglu(g, u, kw.get("prec", "f32"))
+        return linear(h, None, W[f"l{l}.down.b"], Wt=W.T(f"l{l}.down.w"), **kw)
+    act = 2 if cfg.gelu_kind == 1 else 1
+    h = linear(x, None, W[f"l{l}.fc1.b"], act=act, Wt=W.T(f"l{l}.fc1.w"), **kw)
+    return linear(h, None, W[f"l{l}.fc2.b"], Wt=W.T(f"l{l}.fc2.w"), **kw)
+
+
+def aligner(cfg, A: np.ndarray, W, **kw) -> np.ndarray:
+    """Projection of the merged rows (fp32 out).  One linear, or with ``aligner_hidden`` > 0
+    two linears with the configured GELU between them ([Z] "Step 2" boundary table: the
+    aligner output covers two linear projections): the first rounded to bf16 after its GELU,
+    the second kept in fp32."""
+    if cfg.aligner_hidden > 0:
+        act = 2 if cfg.gelu_kind == 1 else 1
+        a1 = linear(A, None, W["proj.b"], act=act, Wt=W.T("proj.w"), **kw)
+        return linear(a1, None, W["proj2.b"], round_out=False, Wt=W.T("proj2.w"), **kw)
+    return linear(A, None, W["proj.b"], round_out=False, Wt=W.T("proj.w"), **kw)
 
 
 def add_round(a: np.ndarray, b: np.ndarray, prec: str = "f32") -> np.ndarray:
@@ -286,9 +356,12 @@ def encode_image(cfg, W: Weights, img: np.ndarray, gh: int, gw: int, prec: str =
       [LN -> QKV (bias) -> 2D RoPE on q,k -> attention -> out-proj -> residual ->
        LN -> fc1 + GELU-tanh -> fc2 -> residual], each output rounded to bf16
       -> final LN (bf16) -> 3x3 merge -> projection (kept in fp32).
+    The official-layer variant (``cfg.norm_kind``, ``cfg.mlp_kind``, ``cfg.gelu_kind``,
+    ``cfg.aligner_hidden``) swaps in RMSNorm, the SwiGLU MLP, erf GELU and the two-linear
+    aligner at the same places (see ``norm``, ``mlp`` and ``aligner``).
     ``dumps``, if given, receives the boundary tensors of [Z] "Step 2".
     """
-    D, H, e = cfg.hidden, cfg.heads, cfg.ln_eps
+    D, H = cfg.hidden, cfg.heads
     nl = cfg.layers if layers is None else layers
     kw = dict(prec=prec, workers=workers)
     P = patchify(img, gh, gw, cfg, prec)
@@ -297,24 +370,23 @@ def encode_image(cfg, W: Weights, img: np.ndarray, gh: int, gw: int, prec: str =
         dumps["patches"] = P
         dumps["embed"] = x
     for l in range(nl):
-        ln = layernorm(x, W[f"l{l}.ln1.g"], W[f"l{l}.ln1.b"], e, **kw)
+        ln = norm(cfg, x, W, f"l{l}.ln1", **kw)
         qkv = linear(ln, None, W[f"l{l}.qkv.b"], Wt=W.T(f"l{l}.qkv.w"), **kw)
         qkv = rope_qk(qkv, gw, D, H, cfg.rope_base, **kw)
         o = attention(qkv, D, H, **kw)
         a = linear(o, None, W[f"l{l}.o.b"], Wt=W.T(f"l{l}.o.w"), **kw)
         x = add_round(x, a, prec)
-        ln2 = layernorm(x, W[f"l{l}.ln2.g"], W[f"l{l}.ln2.b"], e, **kw)
-        h = linear(ln2, None, W[f"l{l}.fc1.b"], act=1, Wt=W.T(f"l{l}.fc1.w"), **kw)
-        f = linear(h, None, W[f"l{l}.fc2.b"], Wt=W.T(f"l{l}.fc2.w"), **kw)
+        ln2 = norm(cfg, x, W, f"l{l}.ln2", **kw)
+        f = mlp(cfg, ln2, W, l, **kw)
         x = add_round(x, f, prec)
         if dumps is not None:
             dumps[f"layer{l}"] = x
             if l == 0:
                 dumps["qkv0"] = qkv
                 dumps["attn0"] = o
-    y = layernorm(x, W["lnf.g"], W["lnf.b"], e, **kw)
+    y = norm(cfg, x, W, "lnf", **kw)
     A = merge(y, gh, gw, cfg.merge, prec)
-    out = linear(A, None, W["proj.b"], round_out=False, Wt=W.T("proj.w"), **kw)
+    out = aligner(cfg, A, W, **kw)
     if dumps is not None:
         dumps["final_norm"] = y
         dumps["merged"] = A

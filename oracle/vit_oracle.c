@@ -96,7 +96,8 @@ void orc_patchify(const uint8_t *img, int gh, int gw, int ps, const float *s, co
  * [Z] "Multimodal basics" (patch projection), "Step 2" boundary table (QKV bias, the
  * aligner's linear projection).  W is passed transposed, Wt[k][j] = W[j][k], so that the
  * k-sum for every output runs in index order while the inner loop walks j contiguously.
- * act: 0 none, 1 GELU with the tanh approximation ([Z] "End-to-end results": tanh GELU).
+ * act: 0 none, 1 GELU with the tanh approximation ([Z] "End-to-end results": tanh GELU),
+ * 2 GELU in the exact erf form (the official path, same section).
  * Rows [r0, r1) of the output are computed.
  * ------------------------------------------------------------------------------------- */
 static real gelu_tanh(real u)
@@ -109,6 +110,35 @@ static real gelu_tanh(real u)
 }
 
 real orc_gelu_tanh(real u) { return gelu_tanh(u); }
+
+/* GELU in its exact form u * Phi(u) = 0.5 u (1 + erf(u / sqrt 2)), the form of the official
+ * vision path ([Z] "End-to-end results": the official path uses erf, zLLM the tanh form). */
+static real gelu_erf(real u)
+{
+    const real r2 = (real)1.4142135623730951;   /* sqrt(2) */
+    return (real)0.5 * u * ((real)1 + (ORC_IS_DOUBLE ? (real)erf((double)(u / r2))
+                                                     : (real)erff((float)(u / r2))));
+}
+
+real orc_gelu_erf(real u) { return gelu_erf(u); }
+
+/* SiLU (swish) u * sigmoid(u) = u / (1 + e^-u), the gate activation of SwiGLU. */
+static real silu(real u)
+{
+    return u / ((real)1 + (ORC_IS_DOUBLE ? (real)exp(-(double)u) : (real)expf(-(float)u)));
+}
+
+real orc_silu(real u) { return silu(u); }
+
+/* SwiGLU gating of the official tower's MLP ([Z] "Comparing the DeepSeek V4.1 Flash and
+ * Qwen3-VL vision towers": the official tower uses RMSNorm and SwiGLU): h = bf16(silu(g) * u) elementwise, where g and u
+ * are the unrounded outputs (bias included) of the gate and up projections of the same
+ * input.  Reading: like the GELU MLP's first linear, projection, activation and gating form
+ * one step with one bf16 rounding at its end. */
+void orc_swiglu(const real *g, const real *u, int64_t n, real *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = R(silu(g[i]) * u[i]);
+}
 
 void orc_transpose(const real *W, int64_t rows, int64_t cols, real *Wt)
 {
@@ -134,6 +164,7 @@ int orc_linear(const real *A, int64_t lda, int64_t r0, int64_t r1, int K, const 
         for (int j = 0; j < N; ++j) {
             real v = acc[j] + (bias ? bias[j] : 0);
             if (act == 1) v = gelu_tanh(v);
+            else if (act == 2) v = gelu_erf(v);
             o[j] = round_out ? R(v) : v;
         }
     }
@@ -162,6 +193,27 @@ void orc_layernorm(const real *x, int64_t ld, int64_t r0, int64_t r1, int D, con
         real den = ORC_IS_DOUBLE ? (real)sqrt((double)(var + eps)) : (real)sqrtf((float)(var + eps));
         real *o = out + i * ldo;
         for (int k = 0; k < D; ++k) o[k] = R((xr[k] - mu) / den * g[k] + b[k]);
+    }
+}
+
+/* ---------------------------------------------------------------------------------------
+ * RMSNorm, rows [r0, r1):  ms = sum x^2 / D,  y = bf16(x / sqrt(ms + eps) * g).  The block
+ * norms and the final norm of the official tower ([Z] "Comparing the DeepSeek V4.1 Flash
+ * and Qwen3-VL vision towers": RMSNorm and SwiGLU; "Step 2" boundary table: RMSNorm semantics at the final-norm
+ * boundary).  No mean is subtracted and there is no additive term.  Reading: the same eps
+ * as the LayerNorm form (1e-6), added to the mean square inside the square root.
+ * ------------------------------------------------------------------------------------- */
+void orc_rmsnorm(const real *x, int64_t ld, int64_t r0, int64_t r1, int D, const real *g,
+                 real eps, real *out, int64_t ldo)
+{
+    for (int64_t i = r0; i < r1; ++i) {
+        const real *xr = x + i * ld;
+        real ss = 0;
+        for (int k = 0; k < D; ++k) ss += xr[k] * xr[k];
+        real ms = ss / (real)D;
+        real den = ORC_IS_DOUBLE ? (real)sqrt((double)(ms + eps)) : (real)sqrtf((float)(ms + eps));
+        real *o = out + i * ldo;
+        for (int k = 0; k < D; ++k) o[k] = R(xr[k] / den * g[k]);
     }
 }
 

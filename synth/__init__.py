@@ -127,6 +127,12 @@ class VitConfig:
     rope_base: float = 10000.0
     pix_mean: tuple = (0.5, 0.5, 0.5)
     pix_std: tuple = (0.5, 0.5, 0.5)
+    # official-layer variant ([Z] "Comparing the DeepSeek V4.1 Flash and Qwen3-VL vision
+    # towers", "Step 2", "End-to-end results"); all zero = the LayerNorm / GELU-tanh tower
+    norm_kind: int = 0        # 0 LayerNorm (gamma, beta), 1 RMSNorm (gamma)
+    mlp_kind: int = 0         # 0 fc1 -> GELU -> fc2, 1 SwiGLU: down(silu(gate) * up)
+    gelu_kind: int = 0        # 0 tanh form, 1 erf form (MLP GELU and the aligner's GELU)
+    aligner_hidden: int = 0   # 0 one projection; > 0 two, with this width between them
 
     @property
     def head_dim(self) -> int:
@@ -139,15 +145,29 @@ class VitConfig:
     def tensor_shapes(self):
         """(name, shape) of every weight tensor in blob order."""
         D, F, P, Dl, m2 = self.hidden, self.mlp, self.patch_dim, self.out_hidden, self.merge ** 2
+        rms = self.norm_kind == 1
+
+        def nrm(name):
+            return [(name + ".g", (D,))] + ([] if rms else [(name + ".b", (D,))])
         out = [("pe.w", (D, P)), ("pe.b", (D,))]
         for l in range(self.layers):
-            out += [(f"l{l}.ln1.g", (D,)), (f"l{l}.ln1.b", (D,)),
-                    (f"l{l}.qkv.w", (3 * D, D)), (f"l{l}.qkv.b", (3 * D,)),
-                    (f"l{l}.o.w", (D, D)), (f"l{l}.o.b", (D,)),
-                    (f"l{l}.ln2.g", (D,)), (f"l{l}.ln2.b", (D,)),
-                    (f"l{l}.fc1.w", (F, D)), (f"l{l}.fc1.b", (F,)),
-                    (f"l{l}.fc2.w", (D, F)), (f"l{l}.fc2.b", (D,))]
-        out += [("lnf.g", (D,)), ("lnf.b", (D,)), ("proj.w", (Dl, m2 * D)), ("proj.b", (Dl,))]
+            out += nrm(f"l{l}.ln1")
+            out += [(f"l{l}.qkv.w", (3 * D, D)), (f"l{l}.qkv.b", (3 * D,)),
+                    (f"l{l}.o.w", (D, D)), (f"l{l}.o.b", (D,))]
+            out += nrm(f"l{l}.ln2")
+            if self.mlp_kind == 1:
+                out += [(f"l{l}.gate.w", (F, D)), (f"l{l}.gate.b", (F,)),
+                        (f"l{l}.up.w", (F, D)), (f"l{l}.up.b", (F,)),
+                        (f"l{l}.down.w", (D, F)), (f"l{l}.down.b", (D,))]
+            else:
+                out += [(f"l{l}.fc1.w", (F, D)), (f"l{l}.fc1.b", (F,)),
+                        (f"l{l}.fc2.w", (D, F)), (f"l{l}.fc2.b", (D,))]
+        out += nrm("lnf")
+        if self.aligner_hidden > 0:
+            Da = self.aligner_hidden
+            out += [("proj.w", (Da, m2 * D)), ("proj.b", (Da,)), ("proj2.w", (Dl, Da)), ("proj2.b", (Dl,))]
+        else:
+            out += [("proj.w", (Dl, m2 * D)), ("proj.b", (Dl,))]
         return out
 
     def blob_elems(self) -> int:
@@ -163,6 +183,11 @@ TINY = VitConfig(layers=2, hidden=64, heads=4, mlp=256, out_hidden=128, max_toke
 V41 = VitConfig()                                   # 32 layers, 1024 wide, projection to 5120
 V41_ONE_LAYER = replace(V41, layers=1)
 V4 = replace(V41, out_hidden=4096, max_tokens_per_image=384)
+# the official-layer variant of the V4.1 tower: RMSNorm, SwiGLU MLP, erf GELU and a two-linear
+# aligner whose inner width is the language hidden size (reading: the pages name the layer
+# kinds, not the inner width)
+V41_OFFICIAL = replace(V41, norm_kind=1, mlp_kind=1, gelu_kind=1, aligner_hidden=5120)
+TINY_OFFICIAL = replace(TINY, norm_kind=1, mlp_kind=1, gelu_kind=1, aligner_hidden=192)
 
 
 @dataclass

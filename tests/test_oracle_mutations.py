@@ -47,6 +47,18 @@ MUTATIONS = [
      lambda: pins.test_linear_vs_numpy_fp64("f64")),
     ("linear skips last k", "for (int k = 0; k < K; ++k) {", "for (int k = 0; k < K - 1; ++k) {",
      lambda: pins.test_linear_vs_numpy_fp64("f64")),
+    ("rmsnorm eps outside sqrt", "sqrt((double)(ms + eps))", "(sqrt((double)ms) + eps)",
+     lambda: pins.test_rmsnorm_vs_torch("f64")),
+    ("rmsnorm divides by D - 1", "real ms = ss / (real)D;", "real ms = ss / (real)(D - 1);",
+     lambda: pins.test_rmsnorm_vs_torch("f64")),
+    ("silu as sigmoid", "return u / ((real)1 + (ORC_IS_DOUBLE ? (real)exp(-(double)u)",
+     "return (real)1 / ((real)1 + (ORC_IS_DOUBLE ? (real)exp(-(double)u)", pins.test_silu_closed_forms),
+    ("swiglu gates the wrong operand", "out[i] = R(silu(g[i]) * u[i]);", "out[i] = R(silu(u[i]) * g[i]);",
+     pins.test_swiglu_gate_and_up_roles),
+    ("gelu erf without the sqrt 2", "(real)erf((double)(u / r2))", "(real)erf((double)u)",
+     pins.test_gelu_erf_vs_torch_and_closed_form),
+    ("linear erf act takes the tanh form", "else if (act == 2) v = gelu_erf(v);",
+     "else if (act == 2) v = gelu_tanh(v);", pins.test_linear_gelu_erf_unrounded_and_rounded),
     ("bf16 truncation", "v.u += 0x7FFFu + ((v.u >> 16) & 1u);", "v.u += 0;",
      pins.test_bf16_rounding_matches_torch),
     ("bf16 ties away", "v.u += 0x7FFFu + ((v.u >> 16) & 1u);", "v.u += 0x8000u;",

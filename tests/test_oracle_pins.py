@@ -525,3 +525,191 @@ def test_packed_batch_is_per_image():
     px_rev = np.concatenate([px[n0:], px[:n0]])
     out_rev = oracle.encode(cfg, blob, px_rev, grids[::-1])
     assert np.array_equal(out, np.concatenate([out_rev[3:], out_rev[:3]]))
+
+
+# ------------------------------------------------------------------------------------------
+# official-layer variant: RMSNorm, SiLU / SwiGLU, erf GELU, two-linear aligner
+# ------------------------------------------------------------------------------------------
+def test_gelu_erf_vs_torch_and_closed_form():
+    """Exact GELU: torch's erf form to fp64 rounding; u Phi(u) at u = +-1 from the standard
+    normal table (Phi(1) = 0.8413447460685429); the odd identity gelu(u) - gelu(-u) = u; and
+    the tanh form stays within the ~1e-3 the first page reports for the two forms."""
+    import torch
+    u = np.linspace(-8, 8, 2001)
+    got = np.array([oracle.gelu_erf(v, "f64") for v in u])
+    want = torch.nn.functional.gelu(torch.from_numpy(u)).numpy()
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-14)
+    got32 = np.array([oracle.gelu_erf(v) for v in u])
+    np.testing.assert_allclose(got32, want, rtol=0, atol=2e-6)
+    assert abs(oracle.gelu_erf(1.0, "f64") - 0.8413447460685429) < 1e-15
+    assert abs(oracle.gelu_erf(-1.0, "f64") + 0.15865525393145707) < 1e-15
+    np.testing.assert_allclose(got - got[::-1], u, atol=1e-12)
+    tanh = np.array([oracle.gelu_tanh(v, "f64") for v in u])
+    assert 1e-4 < np.abs(got - tanh).max() < 1e-3
+
+
+def test_silu_closed_forms():
+    """silu(u) = u sigmoid(u): sigmoid(ln 3) = 3/4 gives silu(+-ln 3) = 0.75 ln 3 and
+    -0.25 ln 3; silu(0) = 0; torch's silu to fp64 rounding on a sweep."""
+    import torch
+    l3 = math.log(3.0)
+    assert abs(oracle.silu(l3, "f64") - 0.75 * l3) < 1e-15
+    assert abs(oracle.silu(-l3, "f64") + 0.25 * l3) < 1e-15
+    assert oracle.silu(0.0, "f64") == 0.0
+    u = np.linspace(-30, 30, 1201)
+    got = np.array([oracle.silu(v, "f64") for v in u])
+    want = torch.nn.functional.silu(torch.from_numpy(u)).numpy()
+    np.testing.assert_allclose(got, want, rtol=1e-15, atol=1e-300)
+
+
+def test_swiglu_gate_and_up_roles():
+    """h = bf16(silu(g) u): the activation acts on the gate operand only.  With u = 1 the
+    result is bf16(silu(g)); with g = 0 it is 0 whatever u is; torch's silu product rounded
+    once to bf16 elsewhere."""
+    import torch
+    rng = np.random.default_rng(21)
+    g = rng.standard_normal(4096) * 3
+    u = rng.standard_normal(4096) * 2
+    got = oracle.swiglu(g, u, "f64")
+    want = (torch.nn.functional.silu(torch.from_numpy(g)) * torch.from_numpy(u)).to(torch.bfloat16)
+    assert np.array_equal(got, want.to(torch.float64).numpy())
+    ones = oracle.swiglu(g, np.ones_like(g), "f64")
+    assert np.array_equal(ones, torch.nn.functional.silu(torch.from_numpy(g)).to(torch.bfloat16)
+                          .to(torch.float64).numpy())
+    assert not np.array_equal(ones, oracle.swiglu(np.ones_like(g), g, "f64"))
+    assert (oracle.swiglu(np.zeros_like(g), u, "f64") == 0).all()
+
+
+@pytest.mark.parametrize("prec", ["f32", "f64"])
+def test_rmsnorm_vs_torch(prec):
+    """torch's rms_norm (mean square over the row, eps inside the square root, weight only),
+    with a row whose mean square is far below eps so that eps placement shows."""
+    import torch
+    rng = np.random.default_rng(22)
+    x = rng.standard_normal((10, 64)) * 3 + 1
+    x[3] = 1e-4 * rng.standard_normal(64)
+    g = 1 + 0.1 * rng.standard_normal(64)
+    dt = np.float32 if prec == "f32" else np.float64
+    x, g = (v.astype(dt).astype(np.float64) for v in (x, g))
+    got = oracle.rmsnorm(x, g, 1e-6, prec)
+    want = torch.nn.functional.rms_norm(torch.from_numpy(x), (64,), torch.from_numpy(g), eps=1e-6).numpy()
+    atol = 1e-6 if prec == "f32" else 1e-9
+    assert np.all(np.abs(got - want) <= 2 ** -8 * np.abs(want) + atol)
+
+
+def test_rmsnorm_closed_forms():
+    """A constant row c gives c / sqrt(c^2 + eps) g (no mean is subtracted: a LayerNorm would
+    give its beta); x = (3, 4) gives x / sqrt(12.5 + eps); rows made of (v, -v) pairs have a
+    mean of exactly 0 in any summation order, where RMSNorm equals LayerNorm with beta = 0
+    bit for bit."""
+    g = np.linspace(0.5, 1.5, 64)
+    x = np.full((1, 64), -2.5)
+    want = oracle.round_bf16(-2.5 / math.sqrt(6.25 + 1e-6) * g, "f64")
+    assert np.array_equal(oracle.rmsnorm(x, g, 1e-6, "f64"), want[None, :])
+    got = oracle.rmsnorm(np.array([[3.0, 4.0]]), np.ones(2), 0.5, "f64")
+    assert np.array_equal(got[0], oracle.round_bf16(np.array([3.0, 4.0]) / math.sqrt(13.0), "f64"))
+    rng = np.random.default_rng(23)
+    v = bf16_torch(rng.standard_normal((5, 32)))
+    xz = np.stack([v, -v], axis=2).reshape(5, 64)
+    gz = 1 + 0.1 * rng.standard_normal(64)
+    for prec in ("f32", "f64"):
+        assert np.array_equal(oracle.rmsnorm(xz, gz, 1e-6, prec),
+                              oracle.layernorm(xz, gz, np.zeros(64), 1e-6, prec))
+
+
+def test_linear_gelu_erf_unrounded_and_rounded():
+    """act = 2 is the erf GELU of the biased product: unrounded it matches torch's gelu of
+    A W^T + b to fp64 rounding; rounded, every element is that value rounded once to bf16."""
+    import torch
+    rng = np.random.default_rng(24)
+    A = rng.standard_normal((6, 8))
+    W = rng.standard_normal((5, 8))
+    b = rng.standard_normal(5)
+    pre = torch.from_numpy(A @ W.T + b)
+    want = torch.nn.functional.gelu(pre).numpy()
+    got = oracle.linear(A, W, b, act=2, round_out=False, prec="f64")
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+    got_r = oracle.linear(A, W, b, act=2, prec="f64")
+    assert np.array_equal(got_r, oracle.round_bf16(got, "f64"))
+
+
+def _variant_weights(cfg, **over):
+    """Weights of `cfg` by name as fp64 arrays, with some tensors replaced."""
+    blob = synth.make_weights(cfg, perturbed=True)
+    W = oracle.Weights(cfg, blob, "f64")
+    for k, v in over.items():
+        W.t[k] = np.asarray(v, np.float64)
+        W.tt[k] = np.ascontiguousarray(np.asarray(v, np.float64).T)
+    return W
+
+
+def test_swiglu_mlp_special_case():
+    """With up = 0 weights and bias 1, and down = identity with bias 0 (F = D), the SwiGLU MLP
+    reduces to bf16(silu(x W_gate^T + b_gate)): torch's silu on the gate projection, rounded
+    once.  Swapping gate and up, or applying the activation after the product, breaks it."""
+    import torch
+    from dataclasses import replace
+    cfg = replace(synth.TINY_OFFICIAL, mlp=64, layers=1)
+    D = cfg.hidden
+    W = _variant_weights(cfg, **{"l0.up.w": np.zeros((D, D)), "l0.up.b": np.ones(D),
+                                 "l0.down.w": np.eye(D), "l0.down.b": np.zeros(D)})
+    rng = np.random.default_rng(25)
+    x = bf16_torch(rng.standard_normal((7, D)))
+    got = oracle.mlp(cfg, x, W, 0, prec="f64")
+    pre = torch.from_numpy(x @ W["l0.gate.w"].T + W["l0.gate.b"])
+    want = torch.nn.functional.silu(pre).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(got, want)
+
+
+def test_two_linear_aligner_special_case():
+    """With the second projection 2 I (inner width = out width) and bias 0, the aligner gives
+    2 bf16(gelu_erf(A W_1^T + b_1)) exactly: the GELU sits between the two projections and the
+    first is rounded after it."""
+    import torch
+    from dataclasses import replace
+    cfg = replace(synth.TINY_OFFICIAL, aligner_hidden=synth.TINY_OFFICIAL.out_hidden, layers=1)
+    Dl = cfg.out_hidden
+    W = _variant_weights(cfg, **{"proj2.w": 2 * np.eye(Dl), "proj2.b": np.zeros(Dl)})
+    rng = np.random.default_rng(26)
+    A = bf16_torch(rng.standard_normal((5, 9 * cfg.hidden)))
+    got = oracle.aligner(cfg, A, W, prec="f64")
+    pre = torch.from_numpy(A @ W["proj.w"].T + W["proj.b"])
+    want = 2 * torch.nn.functional.gelu(pre).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.abs(got - want).max() == 0
+
+
+def test_official_variant_blob_and_twin():
+    """The variant's tensor list (no beta for RMSNorm, gate/up/down, two projections) and its
+    encoder's fp32 oracle against the fp64 twin on the tiny workload."""
+    cfg = synth.TINY_OFFICIAL
+    names = [n for n, _ in cfg.tensor_shapes()]
+    assert not any(n.endswith(".b") and (".ln" in n or n.startswith("lnf")) for n in names)
+    assert {"l0.gate.w", "l0.up.w", "l0.down.w", "proj2.w"} <= set(names)
+    D, F, Da, Dl = cfg.hidden, cfg.mlp, cfg.aligner_hidden, cfg.out_hidden
+    per_layer = D + 3 * D * D + 3 * D + D * D + D + D + 3 * F * D + 2 * F + D
+    assert cfg.blob_elems() == (D * cfg.patch_dim + D + cfg.layers * per_layer + D
+                                + Da * 9 * D + Da + Dl * Da + Dl)
+    grids = [(6, 6), (4, 5)]
+    blob = synth.make_weights(cfg, perturbed=True)
+    px = synth.make_pixels(cfg, grids)
+    a = oracle.encode(cfg, blob, px, grids)
+    b = oracle.encode(cfg, blob, px, grids, prec="f64")
+    rel = np.linalg.norm(a - b) / np.linalg.norm(b)
+    assert rel < 1e-2, rel
+
+
+def test_official_variant_final_norm_is_rms():
+    """At the final-norm boundary the variant's rows are RMSNorm outputs of the last block:
+    with gamma = 1 each row's mean square is 1 up to bf16 rounding, while its mean is not 0."""
+    from dataclasses import replace
+    cfg = replace(synth.TINY_OFFICIAL, layers=1)
+    blob = synth.make_weights(cfg)
+    W = oracle.Weights(cfg, blob, "f64")
+    gh, gw = 6, 6
+    px = synth.make_pixels(cfg, [(gh, gw)])
+    d = {}
+    oracle.encode_image(cfg, W, px, gh, gw, prec="f64", dumps=d)
+    y = d["final_norm"]
+    np.testing.assert_allclose((y * y).mean(1), 1.0, atol=1e-2)
+    assert np.array_equal(y, oracle.rmsnorm(d["layer0"], np.ones(cfg.hidden), cfg.ln_eps, "f64"))
+    assert np.abs(y.mean(1)).max() > 1e-3

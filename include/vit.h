@@ -48,13 +48,29 @@ typedef struct { int32_t gh, gw; } vit_grid;
 /* Encoder dimensions.  [Z] "Step 1": 14x14 patches, hidden 1024, 16 heads, 32 layers, 3x3
  * merge, 5120-wide projection (4096 for V4, [G]); token cap 1024 for V4.1, 384 for V4 ([G]).
  * Supported by this build: hidden % 64 == 0, head_dim = hidden/heads in {16, 32, 64, 128},
- * mlp % 64 == 0, patch 14, merge 3, out_hidden >= 1. */
+ * mlp % 64 == 0, patch 14, merge 3, out_hidden >= 1.
+ *
+ * Layer kinds.  All zero gives the pre-LayerNorm tower with a GELU (tanh form) MLP and one
+ * aligner projection.  The official tower's layers ([Z] "Comparing the DeepSeek V4.1 Flash and
+ * Qwen3-VL vision towers": RMSNorm and SwiGLU; "Step 2" boundary table: RMSNorm semantics at
+ * the final norm, two linear projections in the aligner; "End-to-end results and their
+ * limits": erf GELU in the official path) are selected by:
+ *   norm_kind       0 LayerNorm (gamma, beta), 1 RMSNorm bf16(x / sqrt(mean(x^2) + eps) * g);
+ *   mlp_kind        0 fc2(GELU(fc1 x)), 1 SwiGLU down(bf16(silu(gate x) * up x)), where the
+ *                   gate and up projections, SiLU and the product form one step rounded once;
+ *   gelu_kind       0 tanh form, 1 erf form, wherever a GELU appears (the GELU MLP and the
+ *                   aligner between its projections);
+ *   aligner_hidden  0 one projection 9D -> out_hidden (fp32 out); > 0 (a multiple of 64) two:
+ *                   bf16(GELU(9D -> aligner_hidden)), then aligner_hidden -> out_hidden (fp32).
+ * Readings where the pages name only the layer kind: RMSNorm uses ln_eps; SwiGLU and the
+ * aligner keep biases (a zero bias gives the bias-free form). */
 typedef struct {
     int32_t layers, hidden, heads, mlp, patch, merge, out_hidden, max_tokens_per_image;
-    float ln_eps;        /* LayerNorm epsilon (1e-6) */
+    float ln_eps;        /* LayerNorm / RMSNorm epsilon (1e-6) */
     float rope_base;     /* 2D RoPE frequency base (10000) */
     float pix_mean[3];   /* per-channel pixel normalisation: v = (u8/255 - mean) / std, */
     float pix_std[3];    /* evaluated as fmaf(u8, 1/(255 std), -mean/std) in fp32 */
+    int32_t norm_kind, mlp_kind, gelu_kind, aligner_hidden;   /* layer kinds, see above */
 } vit_config;
 
 /* Weights: one host bf16 blob, tensors back to back, every matrix [out][in] row-major:
@@ -64,6 +80,10 @@ typedef struct {
  *   W_2 [D][F], b_2 [D];
  *   lnf.g [D], lnf.b [D], W_proj [out_hidden][9D] (input column c*9 + k: channel-major 3x3
  *   unfold, [Z] "Step 4"), b_proj [out_hidden].
+ * With norm_kind = 1 every ".b" of a norm (ln1.b, ln2.b, lnf.b) is absent.  With mlp_kind = 1
+ * the per-layer W_1, b_1, W_2, b_2 are replaced by W_gate [F][D], b_gate [F], W_up [F][D],
+ * b_up [F], W_down [D][F], b_down [D].  With aligner_hidden = A > 0 the projector is W_proj
+ * [A][9D], b_proj [A], W_proj2 [out_hidden][A], b_proj2 [out_hidden].
  * blob_elems must equal that total. */
 typedef struct {
     vit_config cfg;

@@ -18,13 +18,21 @@
 extern "C" {
 #endif
 
-enum { VIT_ACT_NONE = 0, VIT_ACT_GELU_TANH = 1 };
+enum { VIT_ACT_NONE = 0, VIT_ACT_GELU_TANH = 1, VIT_ACT_GELU_ERF = 2, VIT_ACT_SWIGLU = 3 };
 
 /* Linear layer on bf16 MFMA with fp32 accumulation ([Z] "Multimodal basics": patch
- * projection and the block's linear layers; "End-to-end results": tanh GELU):
+ * projection and the block's linear layers; "End-to-end results and their limits": tanh GELU
+ * in zLLM, erf GELU in the official path):
  *   out[i][j] = act(sum_k A[i][k] W[j][k] + b[j])
  * A bf16 [M][K] (row stride K), W bf16 [N][K], b bf16 [N] or NULL.  out is bf16 [M][N]
- * rounded once after the activation (out_f32 == 0) or fp32 [M][N] (out_f32 != 0).
+ * rounded once after the activation (out_f32 == 0) or fp32 [M][N] (out_f32 != 0, act must be
+ * VIT_ACT_NONE).
+ * VIT_ACT_SWIGLU is the first step of the official tower's MLP ([Z] "Comparing the DeepSeek
+ * V4.1 Flash and Qwen3-VL vision towers"): W and b hold N = 2F rows, the gate and up
+ * projections interleaved in groups of 8 (rows 16j .. 16j+7 = gate rows 8j .. 8j+7, rows
+ * 16j+8 .. 16j+15 = up rows 8j .. 8j+7), and out is bf16 [M][N/2] with
+ * out[i][f] = bf16(silu(g) * u), g and u the biased fp32 gate and up results of feature f.
+ * vit_create builds this interleaved weight from the blob's W_gate and W_up.  N % 16 == 0.
  * Requires M >= 0, N >= 1, K >= 64 and K % 64 == 0. */
 vit_status vit_op_linear(vit_ctx *ctx, const uint16_t *d_A, int64_t M, int32_t K,
                          const uint16_t *d_W, const uint16_t *d_b, int32_t N, int32_t act,
@@ -37,6 +45,14 @@ vit_status vit_op_linear(vit_ctx *ctx, const uint16_t *d_A, int64_t M, int32_t K
 vit_status vit_op_layernorm(vit_ctx *ctx, const uint16_t *d_x, const uint16_t *d_delta,
                             uint16_t *d_xout, int64_t M, int32_t D, const uint16_t *d_g,
                             const uint16_t *d_b, float eps, uint16_t *d_out, void *stream);
+
+/* Residual add + RMSNorm, the official tower's norm ([Z] "Comparing the DeepSeek V4.1 Flash
+ * and Qwen3-VL vision towers"; "Step 2" boundary table: RMSNorm semantics at the final norm),
+ * same kernel and conventions as vit_op_layernorm with:
+ *   out = bf16(x / sqrt(mean(x^2) + eps) * g)   (no mean subtracted, no beta). */
+vit_status vit_op_rmsnorm(vit_ctx *ctx, const uint16_t *d_x, const uint16_t *d_delta,
+                          uint16_t *d_xout, int64_t M, int32_t D, const uint16_t *d_g,
+                          float eps, uint16_t *d_out, void *stream);
 
 /* Row stride (in elements) of the transposed-V buffer for a batch: the buffer is
  * binary16 [heads][head_dim][stride] and image i owns columns starting at a multiple of 64,
@@ -93,9 +109,11 @@ vit_status vit_op_attention(vit_ctx *ctx, const uint16_t *d_qkv, const uint16_t 
  * cuts every item into n slices.  VIT_E_ARG for other values. */
 vit_status vit_set_attention_split(vit_ctx *ctx, int32_t n);
 
-/* 3x3 merge + projector ([Z] "Step 4": right/bottom zero padding on the 2D grid,
- * channel-major unfold; then the aligner projection): d_y = bf16 [N][D] final-norm rows,
- * d_out = fp32 [M][out_hidden] using the context's projector weights. */
+/* 3x3 merge + aligner ([Z] "Step 4": right/bottom zero padding on the 2D grid,
+ * channel-major unfold; then the aligner projection, or with aligner_hidden > 0 the two
+ * projections with the configured GELU between them, the inner result rounded to bf16 in a
+ * context buffer grown on demand): d_y = bf16 [N][D] final-norm rows, d_out = fp32
+ * [M][out_hidden] using the context's aligner weights. */
 vit_status vit_op_merge_project(vit_ctx *ctx, const uint16_t *d_y, const vit_grid *h_grids,
                                 int32_t n_images, float *d_out, void *stream);
 

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libvit.so")
 VIT_OK, VIT_E_ARG, VIT_E_BUDGET, VIT_E_NOMEM, VIT_E_DEVICE = 0, 1, 2, 3, 4
 TOK_START, TOK_IMAGE, TOK_NEWLINE, TOK_END = 1, 2, 3, 4
 DUMP_PATCHES, DUMP_EMBED, DUMP_QKV, DUMP_ATTN, DUMP_LAYER, DUMP_FINAL_NORM, DUMP_MERGED = range(7)
-ACT_NONE, ACT_GELU_TANH = 0, 1
+ACT_NONE, ACT_GELU_TANH, ACT_GELU_ERF, ACT_SWIGLU = 0, 1, 2, 3
 
 # every entry point declared in include/vit.h and include/vit_ops.h
 EXPORTS = ("vit_blob_elems", "vit_create", "vit_destroy", "vit_reserve", "vit_num_tokens",
@@ -26,7 +26,7 @@ EXPORTS = ("vit_blob_elems", "vit_create", "vit_destroy", "vit_reserve", "vit_nu
            "vit_last_error", "vit_op_linear", "vit_op_layernorm", "vit_vt_stride", "vit_op_rope",
            "vit_op_attention", "vit_op_merge_project", "vit_timing_enable", "vit_timing_read",
            "vit_set_attention_split", "vit_op_qkv_rope", "vit_set_sentinels",
-           "vit_assemble", "vit_plan_image", "vit_preprocess")
+           "vit_assemble", "vit_plan_image", "vit_preprocess", "vit_op_rmsnorm")
 STEP_NAMES = ("patch_embed", "layernorm", "qkv", "rope", "attention", "out_proj", "fc1", "fc2",
               "projector", "overlay")
 
@@ -46,7 +46,9 @@ class Config(ctypes.Structure):
                 ("mlp", ctypes.c_int32), ("patch", ctypes.c_int32), ("merge", ctypes.c_int32),
                 ("out_hidden", ctypes.c_int32), ("max_tokens_per_image", ctypes.c_int32),
                 ("ln_eps", ctypes.c_float), ("rope_base", ctypes.c_float),
-                ("pix_mean", ctypes.c_float * 3), ("pix_std", ctypes.c_float * 3)]
+                ("pix_mean", ctypes.c_float * 3), ("pix_std", ctypes.c_float * 3),
+                ("norm_kind", ctypes.c_int32), ("mlp_kind", ctypes.c_int32),
+                ("gelu_kind", ctypes.c_int32), ("aligner_hidden", ctypes.c_int32)]
 
 
 class Weights(ctypes.Structure):
@@ -96,6 +98,7 @@ def lib():
             "vit_last_error": (ctypes.c_char_p, [vp]),
             "vit_op_linear": (i32, [vp, vp, i64, i32, vp, vp, i32, i32, i32, vp, vp]),
             "vit_op_layernorm": (i32, [vp, vp, vp, vp, i64, i32, vp, vp, ctypes.c_float, vp, vp]),
+            "vit_op_rmsnorm": (i32, [vp, vp, vp, vp, i64, i32, vp, ctypes.c_float, vp, vp]),
             "vit_vt_stride": (i64, [P(Grid), i32]),
             "vit_op_rope": (i32, [vp, vp, vp, P(Grid), i32, vp]),
             "vit_op_qkv_rope": (i32, [vp, vp, vp, vp, P(Grid), i32, vp, vp, i32, vp]),
@@ -128,7 +131,24 @@ def make_config(cfg) -> Config:
     for i in range(3):
         c.pix_mean[i] = float(cfg.pix_mean[i])
         c.pix_std[i] = float(cfg.pix_std[i])
+    for f in ("norm_kind", "mlp_kind", "gelu_kind", "aligner_hidden"):
+        setattr(c, f, int(getattr(cfg, f, 0)))
     return c
+
+
+def swiglu_interleave(gate, up):
+    """The ACT_SWIGLU operand layout from gate and up tensors of F rows each (weights [F][K]
+    or biases [F]): rows 16j .. 16j+7 = gate rows 8j .. 8j+7, rows 16j+8 .. 16j+15 = up rows
+    8j .. 8j+7.  Works on numpy arrays and torch tensors (a pure row permutation)."""
+    F = gate.shape[0]
+    assert up.shape == gate.shape and F % 8 == 0
+    rest = tuple(gate.shape[1:])
+    g = gate.reshape((F // 8, 8) + rest)
+    u = up.reshape((F // 8, 8) + rest)
+    if hasattr(gate, "new_empty"):
+        import torch
+        return torch.stack([g, u], dim=1).reshape((2 * F,) + rest)
+    return np.stack([g, u], axis=1).reshape((2 * F,) + rest)
 
 
 def grid_array(grids):
@@ -281,10 +301,12 @@ class Encoder:
 
     # ---- single steps (include/vit_ops.h) ---------------------------------------------
     def op_linear(self, A, W, b, act=ACT_NONE, out_f32=False, stream=None):
+        """act = ACT_SWIGLU takes W, b in the swiglu_interleave layout and returns [M][N/2]."""
         import torch
         M, K = A.shape
         N = W.shape[0]
-        out = torch.empty((M, N), dtype=torch.float32 if out_f32 else torch.bfloat16, device=A.device)
+        n_out = N // 2 if act == ACT_SWIGLU else N
+        out = torch.empty((M, n_out), dtype=torch.float32 if out_f32 else torch.bfloat16, device=A.device)
         self._check(lib().vit_op_linear(self._ctx, _ptr(A), M, K, _ptr(W), _ptr(b), N, act,
                                         1 if out_f32 else 0, _ptr(out), _stream(stream)))
         return out
@@ -296,6 +318,14 @@ class Encoder:
         self._check(lib().vit_op_layernorm(self._ctx, _ptr(x), _ptr(delta), _ptr(xout), M, D,
                                            _ptr(g), _ptr(b), float(eps), _ptr(out),
                                            _stream(stream)))
+        return out
+
+    def op_rmsnorm(self, x, g, eps, delta=None, xout=None, stream=None):
+        import torch
+        M, D = x.shape
+        out = torch.empty_like(x)
+        self._check(lib().vit_op_rmsnorm(self._ctx, _ptr(x), _ptr(delta), _ptr(xout), M, D,
+                                         _ptr(g), float(eps), _ptr(out), _stream(stream)))
         return out
 
     def op_rope(self, qkv, grids, stream=None):

@@ -82,6 +82,16 @@ __device__ __forceinline__ float gelu_tanh_big(float u)
     return u * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// GELU, exact form: u Phi(u) = 0.5 u (1 + erf(u / sqrt 2)) (the official vision path, [Z]
+// "End-to-end results and their limits": erf there, tanh in zLLM).
+__device__ __forceinline__ float gelu_erf_big(float u) { return 0.5f * u * (1.0f + erff(u * 0.70710678118654752f)); }
+
+// SiLU: u sigmoid(u) = u / (1 + 2^(-u log2 e)); saturates to u and to -0 for large |u|.
+__device__ __forceinline__ float silu_big(float u)
+{
+    return u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(u * -1.4426950408889634f));
+}
+
 // bias (columns n..n+3; columns past N get none) and activation
 template <int ACT>
 __device__ __forceinline__ void bias_act(const bf16_t *bias, int N, int n, const float *v, float *r)
@@ -99,6 +109,9 @@ __device__ __forceinline__ void bias_act(const bf16_t *bias, int N, int n, const
     if (ACT == ACT_GELU_TANH)
 #pragma unroll
         for (int j = 0; j < 4; ++j) r[j] = gelu_tanh_big(r[j]);
+    if (ACT == ACT_GELU_ERF)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r[j] = gelu_erf_big(r[j]);
 }
 
 // bf16 output.  put(): 4 results -> 8 bytes at dst (LDS staging).  store(): 4 results of row
@@ -106,7 +119,7 @@ __device__ __forceinline__ void bias_act(const bf16_t *bias, int N, int n, const
 template <int ACT>
 struct EpiBF16 {
     static constexpr int OUT_BYTES = 2;
-    static constexpr bool CUSTOM = false;
+    static constexpr bool CUSTOM = false, PAIRED = false;
     bf16_t *out;
     const bf16_t *bias;
     int64_t M;
@@ -135,7 +148,7 @@ struct EpiBF16 {
 
 struct EpiF32 {
     static constexpr int OUT_BYTES = 4;
-    static constexpr bool CUSTOM = false;
+    static constexpr bool CUSTOM = false, PAIRED = false;
     float *out;
     const bf16_t *bias;
     int64_t M;
@@ -165,11 +178,38 @@ struct EpiF32 {
 // Raw fp32 partial tile of a K slice (no bias, no activation), [BM][BN] contiguous.
 struct EpiPart {
     static constexpr int OUT_BYTES = 4;
-    static constexpr bool CUSTOM = false;
+    static constexpr bool CUSTOM = false, PAIRED = false;
     float *out;
     __device__ __forceinline__ void put(char *dst, int, const float *v) const
     {
         *reinterpret_cast<float4 *>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+};
+
+// SwiGLU gating of the official tower's MLP ([Z] "Comparing the DeepSeek V4.1 Flash and
+// Qwen3-VL vision towers": RMSNorm and SwiGLU): h = bf16(silu(g) u), g and u the biased fp32
+// results of the gate and up projections, rounded once.  The weight and bias hold the gate
+// and up rows interleaved in groups of 8 (fused rows 16j .. 16j+7 = gate features 8j .. 8j+7,
+// rows 16j+8 .. 16j+15 = up features 8j .. 8j+7).  A lane's accumulator block covers columns
+// 8q + 4g .. 8q + 4g + 3 (q = 0..3) of a 32-column MFMA block, so blocks q = 0, 2 are gate
+// values and q = 1, 3 the up values of the same 4 features: the gating needs no exchange.
+// N is the fused width 2F; out is bf16 [M][N/2].
+struct EpiSwiGLU {
+    static constexpr int OUT_BYTES = 2;
+    static constexpr bool CUSTOM = false, PAIRED = true;
+    bf16_t *out;
+    const bf16_t *bias;
+    int64_t M;
+    int N;
+    // g: fused columns nf..nf+3, u: nf+8..nf+11 -> 4 bf16 outputs (8 bytes) at dst
+    __device__ __forceinline__ void put2(char *dst, int nf, const float *g, const float *u) const
+    {
+        float rg[4], ru[4], h[4];
+        bias_act<ACT_NONE>(bias, N, nf, g, rg);
+        bias_act<ACT_NONE>(bias, N, nf + 8, u, ru);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) h[j] = silu_big(rg[j]) * ru[j];
+        *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
     }
 };
 
@@ -208,7 +248,7 @@ __device__ __forceinline__ uint32_t bf16_to_f16_sat(uint32_t b)
 template <int HD>
 struct EpiQKVRope {
     static constexpr int OUT_BYTES = 2;
-    static constexpr bool CUSTOM = true;
+    static constexpr bool CUSTOM = true, PAIRED = false;
     bf16_t *out;        // [M][3D]
     const bf16_t *bias;
     int64_t M;
@@ -584,10 +624,9 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(SRC src, const bf16_t 
                 }
         __syncthreads();
     };
-    auto staged = [&](const auto &e, int pitch, int ob, char *gout, int64_t gpitch, int rows,
-                      int row_bytes) {
-        stage_tile(e, pitch, ob);
-        const int ch = BN * ob / 16;                        // 16-byte chunks per tile row
+    // whole rows of a staged tile (tile_bytes per row) to global memory
+    auto write_rows = [&](int pitch, int tile_bytes, char *gout, int64_t gpitch, int rows, int row_bytes) {
+        const int ch = tile_bytes / 16;                     // 16-byte chunks per tile row
 #pragma unroll 4
         for (int c = tid; c < BM * ch; c += NT) {
             const int r = c / ch, b = (c % ch) * 16;
@@ -602,13 +641,41 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(SRC src, const bf16_t 
             }
         }
     };
+    auto staged = [&](const auto &e, int pitch, int ob, char *gout, int64_t gpitch, int rows,
+                      int row_bytes) {
+        stage_tile(e, pitch, ob);
+        write_rows(pitch, BN * ob, gout, gpitch, rows, row_bytes);
+    };
     if (item >= 0) {   // K slice: raw fp32 partial tile, every row and column (host: BN = 128)
         if constexpr (PSTAGED)
             staged(EpiPart{}, PPITCH, 4, reinterpret_cast<char *>(sk.part + (int64_t)item * BM * BN),
                    (int64_t)BN * 4, BM, BN * 4);
         return;
     }
-    if constexpr (EP::CUSTOM) {
+    if constexpr (EP::PAIRED) {
+        // gating in registers: output column (wn WN + 32 j) / 2 + 8 p + 4 g of the tile takes
+        // the gate block q = 2p and the up block q = 2p + 1; tile rows of BN/2 bf16
+        constexpr int OPITCH = BN + 16;
+        static_assert(BM * OPITCH <= SMEM, "paired staging exceeds the LDS of the kernel");
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    const float vg[4] = {acc[i][j][8 * p], acc[i][j][8 * p + 1], acc[i][j][8 * p + 2],
+                                         acc[i][j][8 * p + 3]};
+                    const float vu[4] = {acc[i][j][8 * p + 4], acc[i][j][8 * p + 5], acc[i][j][8 * p + 6],
+                                         acc[i][j][8 * p + 7]};
+                    const int r = wm * WM + i * 32 + l32, cb = wn * WN + j * 32;
+                    ep.put2(smem + r * OPITCH + (cb / 2 + 8 * p + 4 * g) * 2, n0 + cb + 16 * p + 4 * g, vg, vu);
+                }
+        __syncthreads();
+        const int rows = (int)(ep.M - m0 < BM ? ep.M - m0 : BM);
+        const int row_bytes = N - n0 < BN ? N - n0 : BN;     // (fused columns / 2) x 2 bytes
+        write_rows(OPITCH, BN, reinterpret_cast<char *>(ep.out) + (m0 * (N / 2) + n0 / 2) * 2, (int64_t)N, rows,
+                   row_bytes);
+    } else if constexpr (EP::CUSTOM) {
         static_assert(STAGED, "custom epilogues need the staged tile");
         const int rows_c = (int)(ep.M - m0 < BM ? ep.M - m0 : BM);
         ep.template prepare<BM, NT>(smem + BM * PITCH, m0, rows_c, tid);
@@ -698,7 +765,7 @@ hipError_t run_big(SRC src, const bf16_t *W, int64_t M, int N, int K, EP ep, con
     if (M <= 0) return hipSuccess;
     const int tiles_m = (int)ceil_div(M, BM), tiles_n = (int)ceil_div(N, BN);
     SplitK sk{0, 1, 0, 0, nullptr};
-    if constexpr (!EP::CUSTOM) {   // custom epilogues need whole tiles
+    if constexpr (!EP::CUSTOM && !EP::PAIRED) {   // custom and paired epilogues need whole tiles
         sk = plan_split(M, N, K, BM, BN, ws != nullptr);
         if (sk.splits > 1 && (size_t)sk.items * BM * BN * 4 > ws->bytes) sk = SplitK{0, 1, 0, 0, nullptr};
         if (sk.splits > 1) {
@@ -726,6 +793,7 @@ SrcPlain rows_from(const SrcPlain &s, int64_t m0) { return SrcPlain{s.A + m0 * s
 template <int ACT>
 EpiBF16<ACT> rows_from(const EpiBF16<ACT> &e, int64_t m0) { return EpiBF16<ACT>{e.out + m0 * e.N, e.bias, e.M - m0, e.N}; }
 EpiF32 rows_from(const EpiF32 &e, int64_t m0) { return EpiF32{e.out + m0 * e.N, e.bias, e.M - m0, e.N}; }
+EpiSwiGLU rows_from(const EpiSwiGLU &e, int64_t m0) { return EpiSwiGLU{e.out + m0 * (e.N / 2), e.bias, e.M - m0, e.N}; }
 
 // Row tail of a multi-round launch (one block per CU): when the tiles of the last, partial
 // round are whole rows of tiles, those rows run afterwards as 128 x 128 tiles, four times as
@@ -774,6 +842,14 @@ hipError_t dispatch(SRC src, const bf16_t *W, int64_t M, int N, int K, const bf1
     }
     if (act == ACT_GELU_TANH) {
         EpiBF16<ACT_GELU_TANH> ep{(bf16_t *)out, bias, M, N};
+        return big ? run_rows<256, 256>(src, W, M, N, K, ep, ws, s) : run_rows<256, 128>(src, W, M, N, K, ep, ws, s);
+    }
+    if (act == ACT_GELU_ERF) {
+        EpiBF16<ACT_GELU_ERF> ep{(bf16_t *)out, bias, M, N};
+        return big ? run_rows<256, 256>(src, W, M, N, K, ep, ws, s) : run_rows<256, 128>(src, W, M, N, K, ep, ws, s);
+    }
+    if (act == ACT_SWIGLU) {
+        EpiSwiGLU ep{(bf16_t *)out, bias, M, N};
         return big ? run_rows<256, 256>(src, W, M, N, K, ep, ws, s) : run_rows<256, 128>(src, W, M, N, K, ep, ws, s);
     }
     EpiBF16<ACT_NONE> ep{(bf16_t *)out, bias, M, N};
@@ -847,9 +923,9 @@ hipError_t launch_vt_tail_zero(uint16_t *vt, int64_t ldv, const ImgDesc *imgs, i
 }
 
 hipError_t launch_merge_project(const bf16_t *y, const ImgDesc *imgs, int n_img, int64_t Mtok,
-                                int D, const bf16_t *Wp, const bf16_t *bias, int Dl, float *out,
-                                const bf16_t *zero, const GemmWorkspace *ws, hipStream_t s)
+                                int D, const bf16_t *Wp, const bf16_t *bias, int Dl, int act, bool out_f32,
+                                void *out, const bf16_t *zero, const GemmWorkspace *ws, hipStream_t s)
 {
-    return dispatch(SrcMerge{y, imgs, n_img, Mtok, D, zero}, Wp, Mtok, Dl, 9 * D, bias, ACT_NONE,
-                    true, out, ws, s);
+    return dispatch(SrcMerge{y, imgs, n_img, Mtok, D, zero}, Wp, Mtok, Dl, 9 * D, bias, act, out_f32, out, ws,
+                    s);
 }

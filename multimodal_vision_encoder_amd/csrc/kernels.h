@@ -15,11 +15,12 @@ struct GemmWorkspace {
 size_t gemm_workspace_bytes(int64_t M, int N, int K);
 size_t gemm_workspace_max_bytes();
 
-// Activation of the linear epilogue.
-enum { ACT_NONE = 0, ACT_GELU_TANH = 1 };
+// Activation of the linear epilogue.  ACT_SWIGLU: W and b hold the gate and up rows
+// interleaved in groups of 8 (N = 2F fused rows), out = bf16 [M][N/2] = bf16(silu(g) u).
+enum { ACT_NONE = 0, ACT_GELU_TANH = 1, ACT_GELU_ERF = 2, ACT_SWIGLU = 3 };
 
-// out = act(A W^T + b) on bf16 MFMA, fp32 accumulation; out bf16 (rounded once) or fp32.
-// A bf16 [M][K], W bf16 [N][K]; K % 64 == 0.
+// out = act(A W^T + b) on bf16 MFMA, fp32 accumulation; out bf16 (rounded once) or fp32
+// (ACT_NONE only).  A bf16 [M][K], W bf16 [N][K]; K % 64 == 0.
 hipError_t launch_linear(const bf16_t *A, int64_t M, int K, const bf16_t *W, const bf16_t *bias,
                          int N, int act, bool out_f32, void *out, const GemmWorkspace *ws,
                          hipStream_t s);
@@ -31,15 +32,15 @@ hipError_t launch_patch_embed(const uint8_t *px, const ImgDesc *imgs, int n_img,
                               int Kp, const bf16_t *bias, int D, bf16_t *patches, bf16_t *out,
                               const GemmWorkspace *ws, hipStream_t s);
 
-// 3x3 merge gather + projector: out fp32 [Mtok][Dl]; Wp position-major [Dl][9D]; `zero`
-// points at >= 16 zero bytes (read for positions in the right/bottom padding).
+// 3x3 merge gather + projector: out [Mtok][Dl], fp32 or bf16 after `act`; Wp position-major
+// [Dl][9D]; `zero` points at >= 16 zero bytes (read for positions in the right/bottom padding).
 hipError_t launch_merge_project(const bf16_t *y, const ImgDesc *imgs, int n_img, int64_t Mtok,
-                                int D, const bf16_t *Wp, const bf16_t *bias, int Dl, float *out,
-                                const bf16_t *zero, const GemmWorkspace *ws, hipStream_t s);
+                                int D, const bf16_t *Wp, const bf16_t *bias, int Dl, int act, bool out_f32,
+                                void *out, const bf16_t *zero, const GemmWorkspace *ws, hipStream_t s);
 
-// Optional residual add + LayerNorm (rows of width D).
+// Optional residual add + LayerNorm, or RMSNorm with `rms` (b unused), rows of width D.
 hipError_t launch_layernorm(const bf16_t *x, const bf16_t *delta, bf16_t *xout, int64_t M, int D,
-                            const bf16_t *g, const bf16_t *b, float eps, bf16_t *out,
+                            const bf16_t *g, const bf16_t *b, float eps, bool rms, bf16_t *out,
                             hipStream_t s);
 
 // 2D RoPE on q,k in place + transposed copy of v; one block per (64-row tile, head).

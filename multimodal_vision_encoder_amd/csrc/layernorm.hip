@@ -1,7 +1,10 @@
-// Residual add + LayerNorm, one wave (64 lanes) per row of width D.
+// Residual add + LayerNorm or RMSNorm, one wave (64 lanes) per row of width D.
 //
 //   x   = bf16(x + delta)          (when delta is given; written back to xout)
 //   out = bf16((x - mean) / sqrt(var + eps) * g + b),  mean and biased variance over the row
+//   or, RMSNorm (the official tower: [Z] "Comparing the DeepSeek V4.1 Flash and Qwen3-VL
+//   vision towers"; "Step 2" boundary table, RMSNorm semantics at the final norm):
+//   out = bf16(x / sqrt(mean(x^2) + eps) * g)
 //
 // Pre-norm blocks and the final norm ([Z] "Step 2" boundary table).  The row stays in
 // registers: each lane holds D/64 elements (16 at D = 1024, loaded as two 16-byte chunks
@@ -56,7 +59,7 @@ __device__ __forceinline__ void store_row(bf16_t *p, int lane, const float *v)
     }
 }
 
-template <int EPL>
+template <int EPL, bool RMS>
 __global__ __launch_bounds__(256) void layernorm_kernel(const bf16_t *__restrict__ x,
                                                         const bf16_t *__restrict__ delta,
                                                         bf16_t *xout, int64_t M,
@@ -78,10 +81,13 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const bf16_t *__restrict
         for (int e = 0; e < EPL; ++e) v[e] = bf16_to_f32(f32_to_bf16(__fadd_rn(v[e], d[e])));
         store_row<EPL>(xout + row * D, lane, v);
     }
-    float s = 0.f;
+    float mu = 0.f;
+    if constexpr (!RMS) {
+        float s = 0.f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) s += v[e];
-    const float mu = wave_sum(s) / (float)D;
+        for (int e = 0; e < EPL; ++e) s += v[e];
+        mu = wave_sum(s) / (float)D;
+    }
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
@@ -91,42 +97,51 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const bf16_t *__restrict
     const float var = wave_sum(ss) / (float)D;
     const float den = sqrtf(var + eps);
     // gamma and beta in the same lane layout as the row (16-byte loads)
-    float gv[EPL], bv[EPL];
+    float gv[EPL], y[EPL];
     load_row<EPL>(g, lane, gv);
-    load_row<EPL>(b, lane, bv);
-    float y[EPL];
+    if constexpr (RMS) {
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
+        for (int e = 0; e < EPL; ++e) y[e] = __fmul_rn(__fdiv_rn(v[e], den), gv[e]);
+    } else {
+        float bv[EPL];
+        load_row<EPL>(b, lane, bv);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
 #pragma clang fp contract(off)
-        y[e] = __fadd_rn(__fmul_rn(__fdiv_rn(v[e] - mu, den), gv[e]), bv[e]);
+            y[e] = __fadd_rn(__fmul_rn(__fdiv_rn(v[e] - mu, den), gv[e]), bv[e]);
+        }
     }
     store_row<EPL>(out + row * D, lane, y);
 }
 
 template <int EPL>
 hipError_t run_ln(const bf16_t *x, const bf16_t *delta, bf16_t *xout, int64_t M, const bf16_t *g,
-                  const bf16_t *b, float eps, bf16_t *out, hipStream_t s)
+                  const bf16_t *b, float eps, bool rms, bf16_t *out, hipStream_t s)
 {
-    hipLaunchKernelGGL(layernorm_kernel<EPL>, dim3((unsigned)ceil_div(M, 4)), dim3(256), 0, s, x,
-                       delta, xout, M, g, b, eps, out);
+    if (rms)
+        hipLaunchKernelGGL((layernorm_kernel<EPL, true>), dim3((unsigned)ceil_div(M, 4)), dim3(256), 0, s, x,
+                           delta, xout, M, g, b, eps, out);
+    else
+        hipLaunchKernelGGL((layernorm_kernel<EPL, false>), dim3((unsigned)ceil_div(M, 4)), dim3(256), 0, s, x,
+                           delta, xout, M, g, b, eps, out);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_layernorm(const bf16_t *x, const bf16_t *delta, bf16_t *xout, int64_t M, int D,
-                            const bf16_t *g, const bf16_t *b, float eps, bf16_t *out,
+                            const bf16_t *g, const bf16_t *b, float eps, bool rms, bf16_t *out,
                             hipStream_t s)
 {
     if (M <= 0) return hipSuccess;
     switch (D) {
-    case 64: return run_ln<1>(x, delta, xout, M, g, b, eps, out, s);
-    case 128: return run_ln<2>(x, delta, xout, M, g, b, eps, out, s);
-    case 256: return run_ln<4>(x, delta, xout, M, g, b, eps, out, s);
-    case 512: return run_ln<8>(x, delta, xout, M, g, b, eps, out, s);
-    case 1024: return run_ln<16>(x, delta, xout, M, g, b, eps, out, s);
-    case 1536: return run_ln<24>(x, delta, xout, M, g, b, eps, out, s);
-    case 2048: return run_ln<32>(x, delta, xout, M, g, b, eps, out, s);
+    case 64: return run_ln<1>(x, delta, xout, M, g, b, eps, rms, out, s);
+    case 128: return run_ln<2>(x, delta, xout, M, g, b, eps, rms, out, s);
+    case 256: return run_ln<4>(x, delta, xout, M, g, b, eps, rms, out, s);
+    case 512: return run_ln<8>(x, delta, xout, M, g, b, eps, rms, out, s);
+    case 1024: return run_ln<16>(x, delta, xout, M, g, b, eps, rms, out, s);
+    case 1536: return run_ln<24>(x, delta, xout, M, g, b, eps, rms, out, s);
+    case 2048: return run_ln<32>(x, delta, xout, M, g, b, eps, rms, out, s);
     default: return hipErrorInvalidValue;
     }
 }

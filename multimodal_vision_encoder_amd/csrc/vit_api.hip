@@ -20,6 +20,9 @@ constexpr int kVtAlign = 64;         // per-image column alignment of the transp
 
 thread_local std::string g_err;
 
+// Per-layer weights.  With the SwiGLU MLP, w1/b1 are the gate and up rows interleaved in
+// groups of 8 (the ACT_SWIGLU layout, 2F rows) and w2/b2 the down projection; with RMSNorm the
+// norms have no beta (ln1b, ln2b NULL).
 struct Layer {
     const bf16_t *ln1g, *ln1b, *wqkv, *bqkv, *wo, *bo, *ln2g, *ln2b, *w1, *b1, *w2, *b2;
 };
@@ -39,6 +42,11 @@ struct vit_ctx {
     float s3[3] = {0, 0, 0}, t3[3] = {0, 0, 0};
 
     bf16_t *d_blob = nullptr, *d_wpe = nullptr, *d_wproj = nullptr;
+    bf16_t *d_gu = nullptr;            // SwiGLU: interleaved gate/up weights and biases of all layers
+    const bf16_t *wproj2 = nullptr, *proj2_b = nullptr;   // second aligner projection
+    int Da = 0;                        // rows of the first aligner projection
+    bf16_t *a1 = nullptr;              // aligner inner activations, bf16 [cap_tokens][Da]
+    int64_t cap_tokens = 0;
     bf16_t *d_zero = nullptr;   // 256 zero bytes: the padding source of the merge gather
     uint16_t *d_sentinels = nullptr;   // learned START, NEWLINE, END rows, bf16 [3][Dl]
     float *d_pre_ws = nullptr;         // preprocessing scratch (horizontal resize pass)
@@ -105,6 +113,10 @@ std::string check_config(const vit_config &c)
     if (c.out_hidden < 1) return "out_hidden must be >= 1";
     if (c.max_tokens_per_image < 1) return "max_tokens_per_image must be >= 1";
     if (!(c.ln_eps > 0.f) || !(c.rope_base > 0.f)) return "ln_eps and rope_base must be > 0";
+    if (c.norm_kind != 0 && c.norm_kind != 1) return "norm_kind must be 0 or 1";
+    if (c.mlp_kind != 0 && c.mlp_kind != 1) return "mlp_kind must be 0 or 1";
+    if (c.gelu_kind != 0 && c.gelu_kind != 1) return "gelu_kind must be 0 or 1";
+    if (c.aligner_hidden < 0 || c.aligner_hidden % 64) return "aligner_hidden must be 0 or a positive multiple of 64";
     for (int i = 0; i < 3; ++i)
         if (!(c.pix_std[i] != 0.f) || !std::isfinite(c.pix_std[i]) || !std::isfinite(c.pix_mean[i]))
             return "pixel std must be non-zero and finite";
@@ -114,11 +126,16 @@ std::string check_config(const vit_config &c)
 size_t blob_elems_of(const vit_config &c)
 {
     const size_t D = c.hidden, F = c.mlp, P = 3 * (size_t)c.patch * c.patch, Dl = c.out_hidden;
+    const size_t nrm = c.norm_kind == 1 ? D : 2 * D;                 // gamma (+ beta)
+    const size_t mlp = c.mlp_kind == 1 ? 3 * F * D + 2 * F + D : 2 * F * D + F + D;
+    const size_t Da = c.aligner_hidden;
     size_t n = D * P + D;
-    n += (size_t)c.layers * (2 * D + 3 * D * D + 3 * D + D * D + D + 2 * D + F * D + F + D * F + D);
-    n += 2 * D + Dl * 9 * D + Dl;
+    n += (size_t)c.layers * (2 * nrm + 3 * D * D + 3 * D + D * D + D + mlp);
+    n += nrm + (Da ? Da * 9 * D + Da + Dl * Da + Dl : Dl * 9 * D + Dl);
     return n;
 }
+
+int gelu_act(const vit_config &c) { return c.gelu_kind == 1 ? ACT_GELU_ERF : ACT_GELU_TANH; }
 
 int64_t tokens_of(int gh, int gw) { return (int64_t)((gh + 2) / 3) * ((gw + 2) / 3); }
 
@@ -355,6 +372,34 @@ void timing_stop(vit_ctx *c, hipStream_t s, int kind, long i)
         timing_stop(ctx, s, kind, t_);                                                        \
     } while (0)
 
+// The aligner: 3x3 merge gather + one projection into fp32 rows, or with a second projection
+// bf16(GELU(first)) into the inner buffer (grown on demand), then the second into fp32.
+vit_status run_aligner(vit_ctx *c, const bf16_t *y, const ImgDesc *imgs, int ni, int64_t M, float *out,
+                       const GemmWorkspace *gws, hipStream_t s)
+{
+    if (!c->wproj2) {
+        LAUNCH(c, launch_merge_project(y, imgs, ni, M, c->D, c->d_wproj, c->proj_b, c->Dl, ACT_NONE, true, out,
+                                       c->d_zero, gws, s));
+        return VIT_OK;
+    }
+    if (M > c->cap_tokens) {
+        HIP_TRY(c, hipDeviceSynchronize());
+        if (c->a1) (void)hipFree(c->a1);
+        c->a1 = nullptr;
+        c->cap_tokens = 0;
+        if (hipMalloc((void **)&c->a1, (size_t)M * c->Da * sizeof(bf16_t)) != hipSuccess) {
+            (void)hipGetLastError();
+            c->a1 = nullptr;
+            return fail(c, VIT_E_NOMEM, "aligner workspace allocation failed");
+        }
+        c->cap_tokens = M;
+    }
+    LAUNCH(c, launch_merge_project(y, imgs, ni, M, c->D, c->d_wproj, c->proj_b, c->Da, gelu_act(c->cfg), false,
+                                   c->a1, c->d_zero, gws, s));
+    LAUNCH(c, launch_linear(c->a1, M, c->Da, c->wproj2, c->proj2_b, c->Dl, ACT_NONE, true, out, gws, s));
+    return VIT_OK;
+}
+
 constexpr int kStopNone = -1;
 
 // One encoder pass; with stop >= 0 it ends at that debug boundary and copies the tensor.
@@ -365,6 +410,7 @@ vit_status encode_impl(vit_ctx *c, const uint8_t *px, const vit_grid *grids, int
     vit_status st = make_plan(c, grids, n, p);
     if (st != VIT_OK) return st;
     const int D = c->D, H = c->H, L = c->L;
+    const bool rms = c->cfg.norm_kind == 1, swiglu = c->cfg.mlp_kind == 1;
     const size_t b2 = sizeof(bf16_t);
     if (stop == kStopNone) {
         if (p.N > 0 && (!px || !out)) return fail(c, VIT_E_ARG, "d_pixels or d_out_rows is NULL");
@@ -411,7 +457,7 @@ vit_status encode_impl(vit_ctx *c, const uint8_t *px, const vit_grid *grids, int
     for (int l = 0; l < L; ++l) {
         const Layer &w = c->layers[l];
         TLAUNCH(c, VIT_STEP_LAYERNORM, s, launch_layernorm(c->x, l ? c->delta : nullptr, c->x, p.N, D, w.ln1g, w.ln1b,
-                                   c->cfg.ln_eps, c->ln, s));
+                                   c->cfg.ln_eps, rms, c->ln, s));
         // QKV projection with RoPE on q, k and the V^T relayout in its epilogue
         TLAUNCH(c, VIT_STEP_QKV, s, launch_qkv_rope(c->ln, p.N, D, H, w.wqkv, w.bqkv, c->qkv, c->vt, p.vt_cols,
                                                     dp.imgs, ni, c->d_cos, c->d_sin,
@@ -422,24 +468,30 @@ vit_status encode_impl(vit_ctx *c, const uint8_t *px, const vit_grid *grids, int
         if (stop == VIT_DUMP_ATTN && arg == l) return copy_out(c->o);
         TLAUNCH(c, VIT_STEP_OUT_PROJ, s, launch_linear(c->o, p.N, D, w.wo, w.bo, D, ACT_NONE, false, c->delta, &gws, s));
         TLAUNCH(c, VIT_STEP_LAYERNORM, s, launch_layernorm(c->x, c->delta, c->x, p.N, D, w.ln2g, w.ln2b, c->cfg.ln_eps,
-                                   c->ln, s));
-        TLAUNCH(c, VIT_STEP_FC1, s, launch_linear(c->ln, p.N, D, w.w1, w.b1, c->F, ACT_GELU_TANH, false, c->h1, &gws, s));
+                                   rms, c->ln, s));
+        // GELU MLP: fc1 + GELU; SwiGLU: gate and up projections + silu(g) u in one launch
+        if (swiglu)
+            TLAUNCH(c, VIT_STEP_FC1, s, launch_linear(c->ln, p.N, D, w.w1, w.b1, 2 * c->F, ACT_SWIGLU, false, c->h1, &gws, s));
+        else
+            TLAUNCH(c, VIT_STEP_FC1, s, launch_linear(c->ln, p.N, D, w.w1, w.b1, c->F, gelu_act(c->cfg), false, c->h1, &gws, s));
         TLAUNCH(c, VIT_STEP_FC2, s, launch_linear(c->h1, p.N, c->F, w.w2, w.b2, D, ACT_NONE, false, c->delta, &gws, s));
         if (stop == VIT_DUMP_LAYER && arg == l) {
             // the residual add is fused into the next LayerNorm; run it to materialise x
             LAUNCH(c, launch_layernorm(c->x, c->delta, c->x, p.N, D, c->lnf_g, c->lnf_b,
-                                       c->cfg.ln_eps, c->ln, s));
+                                       c->cfg.ln_eps, rms, c->ln, s));
             return copy_out(c->x);
         }
     }
     TLAUNCH(c, VIT_STEP_LAYERNORM, s, launch_layernorm(c->x, L ? c->delta : nullptr, c->x, p.N, D, c->lnf_g, c->lnf_b,
-                               c->cfg.ln_eps, c->ln, s));
+                               c->cfg.ln_eps, rms, c->ln, s));
     if (stop == VIT_DUMP_FINAL_NORM) return copy_out(c->ln);
     if (stop == VIT_DUMP_MERGED) {
         LAUNCH(c, launch_dump_merged(c->ln, dp.imgs, ni, p.M, D, (bf16_t *)dst, c->d_zero, s));
         return VIT_OK;
     }
-    TLAUNCH(c, VIT_STEP_PROJECTOR, s, launch_merge_project(c->ln, dp.imgs, ni, p.M, D, c->d_wproj, c->proj_b, c->Dl, out, c->d_zero, &gws, s));
+    const long t_ = timing_start(c, s);
+    if ((st = run_aligner(c, c->ln, dp.imgs, ni, p.M, out, &gws, s)) != VIT_OK) return st;
+    timing_stop(c, s, VIT_STEP_PROJECTOR, t_);
     return VIT_OK;
 }
 
@@ -449,7 +501,7 @@ void destroy(vit_ctx *c)
     (void)hipDeviceSynchronize();
     free_workspace(c);
     void *bufs[] = {c->d_blob, c->d_wpe, c->d_wproj, c->d_cos, c->d_sin, c->d_meta, c->d_zero, c->d_gemm_ws,
-                    c->d_attn_ws, c->d_sentinels, c->d_pre_ws};
+                    c->d_attn_ws, c->d_sentinels, c->d_pre_ws, c->d_gu, c->a1};
     for (void *b : bufs)
         if (b) (void)hipFree(b);
     if (c->h_stage) (void)hipHostFree(c->h_stage);
@@ -522,31 +574,69 @@ vit_status vit_create(const vit_weights *w, vit_ctx **out)
     CREATE_HIP(hipMemcpy(c->d_blob, w->blob, want * sizeof(bf16_t), hipMemcpyHostToDevice));
 
     const size_t D = c->D, F = c->F, Dl = c->Dl;
+    const bool rms = w->cfg.norm_kind == 1, swiglu = w->cfg.mlp_kind == 1;
+    c->Da = w->cfg.aligner_hidden > 0 ? w->cfg.aligner_hidden : c->Dl;
+    const size_t Da = c->Da;
     const uint16_t *hb = w->blob;
     size_t off = 0;
     auto take = [&](size_t n) { const size_t o = off; off += n; return o; };
     const size_t o_wpe = take(D * P), o_bpe = take(D);
     c->pe_b = c->d_blob + o_bpe;
     c->layers.resize(c->L);
+    // SwiGLU: blob offsets of each layer's gate and up tensors, interleaved below
+    std::vector<size_t> o_gate(c->L), o_up(c->L), o_bgate(c->L), o_bup(c->L);
     for (int l = 0; l < c->L; ++l) {
         Layer &y = c->layers[l];
         y.ln1g = c->d_blob + take(D);
-        y.ln1b = c->d_blob + take(D);
+        y.ln1b = rms ? nullptr : c->d_blob + take(D);
         y.wqkv = c->d_blob + take(3 * D * D);
         y.bqkv = c->d_blob + take(3 * D);
         y.wo = c->d_blob + take(D * D);
         y.bo = c->d_blob + take(D);
         y.ln2g = c->d_blob + take(D);
-        y.ln2b = c->d_blob + take(D);
-        y.w1 = c->d_blob + take(F * D);
-        y.b1 = c->d_blob + take(F);
+        y.ln2b = rms ? nullptr : c->d_blob + take(D);
+        if (swiglu) {
+            o_gate[l] = take(F * D);
+            o_bgate[l] = take(F);
+            o_up[l] = take(F * D);
+            o_bup[l] = take(F);
+        } else {
+            y.w1 = c->d_blob + take(F * D);
+            y.b1 = c->d_blob + take(F);
+        }
         y.w2 = c->d_blob + take(D * F);
         y.b2 = c->d_blob + take(D);
     }
     c->lnf_g = c->d_blob + take(D);
-    c->lnf_b = c->d_blob + take(D);
-    const size_t o_wproj = take(Dl * 9 * D);
-    c->proj_b = c->d_blob + take(Dl);
+    c->lnf_b = rms ? nullptr : c->d_blob + take(D);
+    const size_t o_wproj = take(Da * 9 * D);
+    c->proj_b = c->d_blob + take(Da);
+    if (w->cfg.aligner_hidden > 0) {
+        c->wproj2 = c->d_blob + take(Dl * Da);
+        c->proj2_b = c->d_blob + take(Dl);
+    }
+
+    // SwiGLU gate and up rows interleaved in groups of 8 (the ACT_SWIGLU layout): per layer
+    // [2F][D] weights, then the [2F] biases of all layers
+    if (swiglu && c->L > 0) {
+        const size_t per = 2 * F * D;
+        CREATE_HIP(hipMalloc((void **)&c->d_gu, (per + 2 * F) * c->L * sizeof(bf16_t)));
+        std::vector<uint16_t> wl(per), bl(2 * F);
+        for (int l = 0; l < c->L; ++l) {
+            for (size_t f = 0; f < F; ++f) {
+                const size_t r = (f / 8) * 16 + f % 8;
+                std::memcpy(&wl[r * D], hb + o_gate[l] + f * D, D * sizeof(uint16_t));
+                std::memcpy(&wl[(r + 8) * D], hb + o_up[l] + f * D, D * sizeof(uint16_t));
+                bl[r] = hb[o_bgate[l] + f];
+                bl[r + 8] = hb[o_bup[l] + f];
+            }
+            bf16_t *dw = c->d_gu + per * l, *db = c->d_gu + per * c->L + 2 * F * l;
+            CREATE_HIP(hipMemcpy(dw, wl.data(), per * sizeof(bf16_t), hipMemcpyHostToDevice));
+            CREATE_HIP(hipMemcpy(db, bl.data(), 2 * F * sizeof(bf16_t), hipMemcpyHostToDevice));
+            c->layers[l].w1 = dw;
+            c->layers[l].b1 = db;
+        }
+    }
 
     // patch projection weight zero-padded to Kp columns ([Z] "Step 5")
     {
@@ -558,8 +648,8 @@ vit_status vit_create(const vit_weights *w, vit_ctx **out)
     }
     // projector weight permuted from channel-major (c*9 + pos) to position-major (pos*D + c)
     {
-        std::vector<uint16_t> perm(Dl * 9 * D);
-        for (size_t j = 0; j < Dl; ++j) {
+        std::vector<uint16_t> perm(Da * 9 * D);
+        for (size_t j = 0; j < Da; ++j) {
             const uint16_t *src = hb + o_wproj + j * 9 * D;
             uint16_t *dstp = &perm[j * 9 * D];
             for (size_t ch = 0; ch < D; ++ch)
@@ -912,7 +1002,10 @@ vit_status vit_op_linear(vit_ctx *ctx, const uint16_t *d_A, int64_t M, int32_t K
 {
     if (!ctx) return fail(nullptr, VIT_E_ARG, "ctx is NULL");
     if (M < 0 || N < 1 || K < 64 || K % 64) return fail(ctx, VIT_E_ARG, "bad M, N or K");
-    if (act != VIT_ACT_NONE && act != VIT_ACT_GELU_TANH) return fail(ctx, VIT_E_ARG, "bad act");
+    if (act != VIT_ACT_NONE && act != VIT_ACT_GELU_TANH && act != VIT_ACT_GELU_ERF && act != VIT_ACT_SWIGLU)
+        return fail(ctx, VIT_E_ARG, "bad act");
+    if (act != VIT_ACT_NONE && out_f32) return fail(ctx, VIT_E_ARG, "fp32 output takes no activation");
+    if (act == VIT_ACT_SWIGLU && N % 16) return fail(ctx, VIT_E_ARG, "SwiGLU needs N % 16 == 0");
     if (M == 0) return VIT_OK;
     if (!d_A || !d_W || !d_out) return fail(ctx, VIT_E_ARG, "NULL pointer");
     const GemmWorkspace gws = gemm_ws(ctx);
@@ -928,7 +1021,18 @@ vit_status vit_op_layernorm(vit_ctx *ctx, const uint16_t *d_x, const uint16_t *d
     if (M < 0 || !supported_hidden(D)) return fail(ctx, VIT_E_ARG, "bad M or D");
     if (M == 0) return VIT_OK;
     if (!d_x || !d_g || !d_b || !d_out || (d_delta && !d_xout)) return fail(ctx, VIT_E_ARG, "NULL pointer");
-    LAUNCH(ctx, launch_layernorm(d_x, d_delta, d_xout, M, D, d_g, d_b, eps, d_out, (hipStream_t)stream));
+    LAUNCH(ctx, launch_layernorm(d_x, d_delta, d_xout, M, D, d_g, d_b, eps, false, d_out, (hipStream_t)stream));
+    return VIT_OK;
+}
+
+vit_status vit_op_rmsnorm(vit_ctx *ctx, const uint16_t *d_x, const uint16_t *d_delta, uint16_t *d_xout, int64_t M,
+                          int32_t D, const uint16_t *d_g, float eps, uint16_t *d_out, void *stream)
+{
+    if (!ctx) return fail(nullptr, VIT_E_ARG, "ctx is NULL");
+    if (M < 0 || !supported_hidden(D)) return fail(ctx, VIT_E_ARG, "bad M or D");
+    if (M == 0) return VIT_OK;
+    if (!d_x || !d_g || !d_out || (d_delta && !d_xout)) return fail(ctx, VIT_E_ARG, "NULL pointer");
+    LAUNCH(ctx, launch_layernorm(d_x, d_delta, d_xout, M, D, d_g, nullptr, eps, true, d_out, (hipStream_t)stream));
     return VIT_OK;
 }
 
@@ -1015,9 +1119,7 @@ vit_status vit_op_merge_project(vit_ctx *ctx, const uint16_t *d_y, const vit_gri
     DevPlan dp{};
     if ((st = stage_plan(ctx, p, (hipStream_t)stream, dp)) != VIT_OK) return st;
     const GemmWorkspace gws = gemm_ws(ctx);
-    LAUNCH(ctx, launch_merge_project(d_y, dp.imgs, (int)p.imgs.size(), p.M, ctx->D, ctx->d_wproj,
-                                     ctx->proj_b, ctx->Dl, d_out, ctx->d_zero, &gws, (hipStream_t)stream));
-    return VIT_OK;
+    return run_aligner(ctx, d_y, dp.imgs, (int)p.imgs.size(), p.M, d_out, &gws, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -34,9 +34,13 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_blob_size_agrees_with_generator():
-    for cfg in (synth.TINY, synth.V41, synth.V4, synth.V41_ONE_LAYER):
+    for cfg in (synth.TINY, synth.V41, synth.V4, synth.V41_ONE_LAYER, synth.V41_OFFICIAL,
+                synth.TINY_OFFICIAL, replace(synth.TINY, norm_kind=1), replace(synth.TINY, mlp_kind=1),
+                replace(synth.TINY, aligner_hidden=64), replace(synth.TINY, gelu_kind=1)):
         assert vit.lib().vit_blob_elems(vit.make_config(cfg)) == cfg.blob_elems()
-    assert vit.lib().vit_blob_elems(vit.make_config(replace(synth.TINY, hidden=100))) == 0
+    for bad in (dict(hidden=100), dict(norm_kind=2), dict(mlp_kind=-1), dict(gelu_kind=3),
+                dict(aligner_hidden=100), dict(aligner_hidden=-64)):
+        assert vit.lib().vit_blob_elems(vit.make_config(replace(synth.TINY, **bad))) == 0, bad
 
 
 @pytest.mark.parametrize("grids", [[(96, 96)], [(54, 63)], [(6, 6), (5, 7), (1, 1), (10, 4)],

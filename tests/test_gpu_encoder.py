@@ -157,6 +157,36 @@ def test_one_layer_end_to_end(perturbed):
     assert_projector_gate(got, want, "one layer")
 
 
+@pytest.mark.parametrize("perturbed", [False, True])
+def test_official_variant_tiny_end_to_end(perturbed):
+    """RMSNorm blocks and final norm, SwiGLU MLP, erf GELU, two-linear aligner; ragged images."""
+    cfg = synth.TINY_OFFICIAL
+    grids = [(6, 6), (5, 7), (1, 1)]
+    blob = synth.make_weights(cfg, perturbed=perturbed)
+    enc, px, got = run(cfg, blob, grids)
+    want = oracle.encode(cfg, blob, px, grids)
+    assert got.shape == (4 + 6 + 1, cfg.out_hidden)
+    assert_projector_gate(got, want, "official tiny")
+
+
+def test_official_variant_one_layer_end_to_end():
+    """One full-width official-variant layer (336x336 image, F = 4096 SwiGLU, 9216 -> 5120 ->
+    5120 aligner) with the boundary tensors compared on the way."""
+    torch = require_gpu()
+    cfg = replace(synth.V41_OFFICIAL, layers=1)
+    grids = [(24, 24)]
+    blob = synth.make_weights(cfg, perturbed=True)
+    enc, px, got = run(cfg, blob, grids)
+    W = oracle.Weights(cfg, blob)
+    dumps = {}
+    want = oracle.encode_image(cfg, W, px, 24, 24, workers=8, dumps=dumps)
+    d_px = torch.from_numpy(px).cuda()
+    for name, b, arg in (("layer0", vit.DUMP_LAYER, 0), ("final_norm", vit.DUMP_FINAL_NORM, 0)):
+        g = from_dev_bf16(enc.dump(b, d_px, grids, arg=arg))
+        assert rel_l2(g, dumps[name]) < 1e-2, name
+    assert_projector_gate(got, want, "official one layer")
+
+
 def test_uniform_gray_image_rows_agree():
     """A flat RGB-127 canvas: all patches equal, v equal at every position, so every visual
     row is the same vector up to rounding (positions enter only through q and k)."""

@@ -172,3 +172,33 @@ def test_packed16_assemble_in_chunks():
         got[a:b] = d.view(torch.int16).cpu().numpy().view(np.uint16)
     assert np.array_equal(got, want)
 
+
+
+def test_official_variant_first_block_full_length():
+    """The official-layer variant at the 1024-token image (96 x 96 = 9216 patches, one block):
+    the residual stream after the first block on sampled rows against the oracle, which
+    computes q, k, v for every patch and the rest of the block for the sampled rows only
+    (attention rows are independent of one another; the other steps act row by row)."""
+    from dataclasses import replace
+    torch = require_gpu()
+    cfg = replace(synth.V41_OFFICIAL, layers=1)
+    gh = gw = 96
+    blob = synth.make_weights(cfg, perturbed=True)
+    px = synth.make_pixels(cfg, [(gh, gw)])
+    enc = vit.Encoder(cfg, blob)
+    x1 = enc.dump(vit.DUMP_LAYER, torch.from_numpy(px).cuda(), [(gh, gw)], 0)
+    torch.cuda.synchronize()
+    rows = np.r_[0:2, 95:98, 4600:4602, 9214:9216]
+    got = from_dev_bf16(x1)[rows]
+    W = oracle.Weights(cfg, blob)
+    kw = dict(workers=16)
+    D, H = cfg.hidden, cfg.heads
+    x0 = oracle.linear(oracle.patchify(px, gh, gw, cfg), None, W["pe.b"], Wt=W.T("pe.w"), **kw)
+    ln = oracle.norm(cfg, x0, W, "l0.ln1", **kw)
+    qkv = oracle.rope_qk(oracle.linear(ln, None, W["l0.qkv.b"], Wt=W.T("l0.qkv.w"), **kw), gw, D, H,
+                         cfg.rope_base, **kw)
+    o = np.stack([oracle.attention(qkv, D, H, rows=(r, r + 1))[r] for r in rows])
+    a = oracle.linear(o, None, W["l0.o.b"], Wt=W.T("l0.o.w"))
+    x = oracle.add_round(x0[rows], a)
+    want = oracle.add_round(x, oracle.mlp(cfg, oracle.norm(cfg, x, W, "l0.ln2"), W, 0))
+    assert_projector_gate(got, want, "official first block")

@@ -162,6 +162,160 @@ def test_layernorm(M, D, residual):
 
 
 # ------------------------------------------------------------------------------------------
+# official-layer variant: RMSNorm, erf GELU, SwiGLU, two-linear aligner
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("M,D,residual", [(37, 64, False), (1000, 1024, True), (9216, 1024, True),
+                                          (5, 256, True), (3, 2048, False)])
+def test_rmsnorm(M, D, residual):
+    torch = require_gpu()
+    enc, _, _ = encoder()
+    x = seeded_bf16((M, D), 120, 0, std=2.0, mean=0.5)
+    x[0, :] = 0                                   # an all-zero row: eps alone in the root
+    dl = seeded_bf16((M, D), 120, 1, std=1.0)
+    g = seeded_bf16((D,), 120, 2, std=0.1, mean=1.0)
+    dx = to_dev_bf16(x)
+    out = enc.op_rmsnorm(dx, to_dev_bf16(g), 1e-6, delta=to_dev_bf16(dl) if residual else None,
+                         xout=dx if residual else None)
+    torch.cuda.synchronize()
+    xr = oracle.add_round(f32(x), f32(dl)) if residual else f32(x)
+    if residual:
+        assert np.array_equal(from_dev_bf16(dx), xr), "residual add must be exact"
+    want = oracle.rmsnorm(xr, f32(g), 1e-6)
+    assert_bf16_close(from_dev_bf16(out), want, atol=1e-6, what="rmsnorm")
+
+
+def _swiglu_want(A, Wg, bg, Wu, bu, workers=1):
+    """Oracle SwiGLU step and its slack: the gate and up sums (fp32, another order) move h by
+    at most |silu'(g)| |u| dg + |silu(g)| du, with |silu'| <= 1.1 and |silu(g)| <= |g|."""
+    g = oracle.linear(f32(A), f32(Wg), f32(bg), round_out=False, workers=workers)
+    u = oracle.linear(f32(A), f32(Wu), f32(bu), round_out=False, workers=workers)
+    h = oracle.swiglu(g, u)
+    slack = 1.1 * np.abs(u) * sum_bound(A, Wg) + np.abs(g) * sum_bound(A, Wu) + 1e-6 * np.abs(h)
+    return h, slack
+
+
+@pytest.mark.parametrize("M,K,F", [(300, 128, 200), (1, 64, 8), (257, 192, 64), (129, 256, 520)])
+def test_linear_swiglu_small(M, K, F):
+    """Gate and up projections with silu(g) u in the epilogue, weights interleaved in groups
+    of 8 rows; ragged M and F (F = 200, 520: the last 256-wide fused tile is partial)."""
+    torch = require_gpu()
+    enc, _, _ = encoder()
+    A = seeded_bf16((M, K), 121, 0)
+    Wg = seeded_bf16((F, K), 121, 1, std=0.05)
+    Wu = seeded_bf16((F, K), 121, 2, std=0.05)
+    bg = seeded_bf16((F,), 121, 3, std=0.1)
+    bu = seeded_bf16((F,), 121, 4, std=0.1)
+    W = vit.swiglu_interleave(Wg, Wu)
+    b = vit.swiglu_interleave(bg, bu)
+    got = enc.op_linear(to_dev_bf16(A), to_dev_bf16(W), to_dev_bf16(b), vit.ACT_SWIGLU)
+    torch.cuda.synchronize()
+    assert tuple(got.shape) == (M, F)
+    want, slack = _swiglu_want(A, Wg, bg, Wu, bu)
+    assert_bf16_close(from_dev_bf16(got), want, atol=slack, what="swiglu")
+
+
+def test_linear_swiglu_gate_up_roles_exact():
+    """Gate weights 0 with bias b_g and up weights one-hot: h = bf16(silu(b_g) a_sel), a single
+    product per output, so the only rounding is the final one -- checked bit for bit against
+    the oracle with the same operands (silu on the GPU uses exp2 and a reciprocal: values
+    within 2 ulps of fp32, compared at bf16 with one-ulp slack)."""
+    torch = require_gpu()
+    enc, _, _ = encoder()
+    M, K, F = 200, 128, 96
+    A = seeded_bf16((M, K), 122)
+    sel = np.random.default_rng(1).permutation(K)[:F]
+    Wu = np.zeros((F, K), np.uint16)
+    Wu[np.arange(F), sel] = 0x3F80
+    Wg = np.zeros((F, K), np.uint16)
+    bg = seeded_bf16((F,), 122, 1, std=2.0)
+    bu = np.zeros(F, np.uint16)
+    got = from_dev_bf16(enc.op_linear(to_dev_bf16(A), to_dev_bf16(vit.swiglu_interleave(Wg, Wu)),
+                                      to_dev_bf16(vit.swiglu_interleave(bg, bu)), vit.ACT_SWIGLU))
+    torch.cuda.synchronize()
+    want = oracle.swiglu(np.broadcast_to(f32(bg), (M, F)), f32(A)[:, sel])
+    assert_bf16_close(got, want, what="swiglu roles")
+    # swapped roles would give bf16(silu(a_sel) b_g): make sure that differs on this input
+    assert not np.array_equal(want, oracle.swiglu(f32(A)[:, sel], np.broadcast_to(f32(bg), (M, F))))
+
+
+@pytest.mark.parametrize("M", [9216, 8492], ids=["one_image", "row_tail"])
+def test_linear_swiglu_full_size_sampled(M):
+    """The official MLP's first step at the 1024-token image's shape (K = 1024, F = 4096, 8192
+    fused rows), and at a row count whose last round runs as the 128 x 128 row tail."""
+    torch = require_gpu()
+    enc, _, _ = encoder()
+    K, F = 1024, 4096
+    A = seeded_bf16((M, K), 123, 0)
+    Wg = seeded_bf16((F, K), 123, 1, std=0.02)
+    Wu = seeded_bf16((F, K), 123, 2, std=0.02)
+    bg = seeded_bf16((F,), 123, 3, std=0.02)
+    bu = seeded_bf16((F,), 123, 4, std=0.02)
+    got = from_dev_bf16(enc.op_linear(to_dev_bf16(A), to_dev_bf16(vit.swiglu_interleave(Wg, Wu)),
+                                      to_dev_bf16(vit.swiglu_interleave(bg, bu)), vit.ACT_SWIGLU))
+    torch.cuda.synchronize()
+    rows = np.r_[0:3, 127:130, 4000:4003, 8188:8196, M - 5:M]
+    want, slack = _swiglu_want(A[rows], Wg, bg, Wu, bu, workers=8)
+    assert_bf16_close(got[rows], want, atol=slack, what="swiglu full size")
+
+
+@pytest.mark.parametrize("M,K,N", [(257, 192, 130), (1024, 9216, 5120)], ids=["small", "aligner"])
+def test_linear_gelu_erf(M, K, N):
+    torch = require_gpu()
+    enc, _, _ = encoder()
+    A = seeded_bf16((M, K), 124, 0)
+    W = seeded_bf16((N, K), 124, 1, std=0.02)
+    b = seeded_bf16((N,), 124, 2, std=0.1)
+    got = from_dev_bf16(enc.op_linear(to_dev_bf16(A), to_dev_bf16(W), to_dev_bf16(b), vit.ACT_GELU_ERF))
+    torch.cuda.synchronize()
+    rows = np.arange(M) if M < 1000 else np.r_[0:3, 500:503, M - 4:M]
+    want = oracle.linear(f32(A[rows]), f32(W), f32(b), act=2)
+    assert_bf16_close(got[rows], want, atol=1.2 * sum_bound(A[rows], W) + 1e-6, what="gelu erf")
+
+
+def test_linear_rejects_activation_with_fp32_output():
+    require_gpu()
+    enc, _, _ = encoder()
+    A = to_dev_bf16(seeded_bf16((8, 64), 125))
+    W = to_dev_bf16(seeded_bf16((16, 64), 125, 1))
+    with pytest.raises(vit.VitError):
+        enc.op_linear(A, W, None, vit.ACT_GELU_ERF, out_f32=True)
+    with pytest.raises(vit.VitError):
+        enc.op_linear(A, to_dev_bf16(seeded_bf16((24, 64), 125, 2)), None, vit.ACT_SWIGLU)
+
+
+_official = {}
+
+
+def official_encoder():
+    if "tiny" not in _official:
+        require_gpu()
+        cfg = synth.TINY_OFFICIAL
+        blob = synth.make_weights(cfg, perturbed=True)
+        _official["tiny"] = (vit.Encoder(cfg, blob), cfg, blob)
+    return _official["tiny"]
+
+
+@pytest.mark.parametrize("grids", [[(6, 6)], [(5, 7), (3, 9), (1, 1), (4, 8)]])
+def test_two_linear_aligner(grids):
+    """Merge gather + first projection + erf GELU (bf16), then the second projection (fp32)."""
+    torch = require_gpu()
+    enc, cfg, blob = official_encoder()
+    N = sum(a * b for a, b in grids)
+    y = seeded_bf16((N, cfg.hidden), 126)
+    got = enc.op_merge_project(to_dev_bf16(y), grids).cpu().numpy()
+    torch.cuda.synchronize()
+    W = oracle.Weights(cfg, blob)
+    off, want = 0, []
+    for gh, gw in grids:
+        A = oracle.merge(f32(y[off:off + gh * gw]), gh, gw)
+        want.append(oracle.aligner(cfg, A, W))
+        off += gh * gw
+    want = np.concatenate(want)
+    assert got.shape == want.shape
+    assert rel_l2(got, want) < 1e-3 and np.abs(got - want).max() <= 1e-2 * np.abs(want).max()
+
+
+# ------------------------------------------------------------------------------------------
 # RoPE + attention
 # ------------------------------------------------------------------------------------------
 def _qkv_for(grids, D, seed, std=1.0):

@@ -7,7 +7,10 @@ and vit_overlay of the visual rows into a prompt embedding matrix.  Inputs are r
 HBM before the timed region starts.  Prints one JSON line on stdout; progress on stderr.
 
 Default workload: one 1344x1344 image (96x96 = 9216 patches, 32 layers of width 1024 with
-16 heads and MLP 4096, 1024 merged tokens projected to 5120).
+16 heads and MLP 4096, 1024 merged tokens projected to 5120).  Besides the headline line's
+figures, the JSON carries per-kernel times, the steps around the path (preprocessing, chunk
+assembly) and the same images through the official-layer variant of the tower (RMSNorm,
+SwiGLU, erf GELU, two-linear aligner).
 """
 import argparse
 import json
@@ -34,8 +37,12 @@ def log(*a):
 
 def flops_per_pass(cfg, grids):
     """Algorithmic MFMA FLOPs: patch projection at K = 588, per layer QKV + out-proj + MLP +
-    attention (QK^T and PV over each image's own patches only), projector at K = 9D."""
+    attention (QK^T and PV over each image's own patches only), projector at K = 9D.  The
+    official-layer variant's SwiGLU step computes two F-wide projections (gate and up), and
+    its aligner adds the second projection."""
     D, F, L, Dl = cfg.hidden, cfg.mlp, cfg.layers, cfg.out_hidden
+    Da = cfg.aligner_hidden or Dl
+    nf1 = 2 if cfg.mlp_kind == 1 else 1
     tot = {"patch_embed": 0, "qkv": 0, "attention": 0, "out_proj": 0, "fc1": 0, "fc2": 0,
            "projector": 0}
     for gh, gw in grids:
@@ -44,9 +51,9 @@ def flops_per_pass(cfg, grids):
         tot["qkv"] += L * 6 * n * D * D
         tot["attention"] += L * 4 * n * n * D
         tot["out_proj"] += L * 2 * n * D * D
-        tot["fc1"] += L * 2 * n * D * F
+        tot["fc1"] += L * 2 * n * D * F * nf1
         tot["fc2"] += L * 2 * n * F * D
-        tot["projector"] += 2 * m * 9 * D * Dl
+        tot["projector"] += 2 * m * 9 * D * Da + (2 * m * Da * Dl if cfg.aligner_hidden else 0)
     return tot
 
 
@@ -145,6 +152,56 @@ def around_the_path(enc, cfg, grids, out, reps):
     by = n_img * cfg.out_hidden * (4 + 2) + (types.size - n_img) * cfg.out_hidden * 4
     res["assemble"] = {"positions": int(types.size), "us": us, "gbs": by / (us * 1e-6) / 1e9,
                        "hbm_frac": by / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
+    return res
+
+
+def official_variant(cfg, grids, steps, warmup):
+    """The official-layer variant of the same tower (RMSNorm, SwiGLU MLP, erf GELU, two-linear
+    aligner with inner width out_hidden) on the same images: encoder throughput and per-step
+    kernel times.  Random N(0, 0.02) weights, gamma 1, biases 0."""
+    import dataclasses
+    import torch
+    import multimodal_vision_encoder_amd as vit
+    import synth
+    vc = dataclasses.replace(cfg, norm_kind=1, mlp_kind=1, gelu_kind=1, aligner_hidden=cfg.out_hidden)
+    blob = synth.make_weights(vc)
+    px = torch.from_numpy(synth.make_pixels(vc, grids)).cuda()
+    M = sum(vc.tokens(gh, gw) for gh, gw in grids)
+    enc = vit.Encoder(vc, blob)
+    del blob
+    out = torch.empty((M, vc.out_hidden), dtype=torch.float32, device="cuda")
+    for _ in range(warmup):
+        enc.encode(px, grids, out=out)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        enc.encode(px, grids, out=out)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    ms = el / steps * 1e3
+    fl = flops_per_pass(vc, grids)
+    res = {"layers": "RMSNorm, SwiGLU MLP, erf GELU, two-linear aligner",
+           "aligner_hidden": vc.aligner_hidden, "visual_tokens_per_s": M * steps / el, "ms_per_step": ms,
+           "images_per_s": len(grids) * steps / el, "tflops": sum(fl.values()) / (ms * 1e-3) / 1e12}
+    res["mfma_frac"] = res["tflops"] / PEAK_BF16_TFLOPS
+    enc.timing(True)
+    for _ in range(steps):
+        enc.encode(px, grids, out=out)
+    torch.cuda.synchronize()
+    tm = enc.timing_read()
+    enc.timing(False)
+    kern = {}
+    for k, (t_ms, n) in tm.items():
+        if n == 0:
+            continue
+        e = {"ms_per_step": t_ms / steps, "avg_launch_us": t_ms / n * 1e3}
+        if k in fl:
+            e["tflops"] = fl[k] / (t_ms / steps * 1e-3) / 1e12
+            e["mfma_frac"] = e["tflops"] / PEAK_BF16_TFLOPS
+        kern[k] = e
+    res["kernels"] = kern
+    enc.close()
+    log(f"official-layer variant: {ms:.3f} ms/step, {res['visual_tokens_per_s']:.0f} tokens/s")
     return res
 
 
@@ -301,6 +358,8 @@ def main():
                                   "traffic_unit": "bytes per launch", "traffic_note": note}
         result["around_the_path"] = around_the_path(enc, cfg, grids, out, args.steps)
         log(json.dumps(kernels, indent=1))
+        if args.workload in ("v4_384", "v41_1024", "packed16"):
+            result["official_layer_variant"] = official_variant(cfg, grids, args.steps, args.warmup)
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")

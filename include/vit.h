@@ -102,9 +102,9 @@ vit_status vit_create(const vit_weights *w, vit_ctx **out);
 /* Release everything the context owns.  Waits for the device first.  NULL is a no-op. */
 void vit_destroy(vit_ctx *ctx);
 
-/* Optional: pre-size the workspace for up to max_patches patches in one call, and cap it
- * there (a later vit_encode needing more returns VIT_E_NOMEM).  max_patches <= 0 removes
- * the cap.  Synchronous. */
+/* Optional: pre-size the workspace for up to max_patches patches in one call (including the
+ * aligner's inner rows when aligner_hidden > 0), and cap it there (a later vit_encode needing
+ * more returns VIT_E_NOMEM).  max_patches <= 0 removes the cap.  Synchronous. */
 vit_status vit_reserve(vit_ctx *ctx, int64_t max_patches);
 
 /* Merged visual tokens of a batch: sum over images of ceil(gh/3) * ceil(gw/3)

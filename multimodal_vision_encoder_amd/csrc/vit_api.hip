@@ -372,6 +372,28 @@ void timing_stop(vit_ctx *c, hipStream_t s, int kind, long i)
         timing_stop(ctx, s, kind, t_);                                                        \
     } while (0)
 
+// Inner rows of the two-projection aligner: bf16 [M][Da], grown on demand; after vit_reserve
+// it holds as many rows as the reserved patches (a batch never has more merged tokens than
+// patches), so reserved calls do not allocate.
+vit_status ensure_tokens(vit_ctx *c, int64_t M)
+{
+    if (!c->wproj2 || M <= c->cap_tokens) return VIT_OK;
+    if (c->reserve_cap > 0 && M > c->reserve_cap)
+        return fail(c, VIT_E_NOMEM, "batch of " + std::to_string(M) + " tokens exceeds the reserved workspace");
+    HIP_TRY(c, hipDeviceSynchronize());
+    if (c->a1) (void)hipFree(c->a1);
+    c->a1 = nullptr;
+    c->cap_tokens = 0;
+    const int64_t cap = std::max<int64_t>(M, 64);
+    if (hipMalloc((void **)&c->a1, (size_t)cap * c->Da * sizeof(bf16_t)) != hipSuccess) {
+        (void)hipGetLastError();
+        c->a1 = nullptr;
+        return fail(c, VIT_E_NOMEM, "aligner workspace allocation failed");
+    }
+    c->cap_tokens = cap;
+    return VIT_OK;
+}
+
 // The aligner: 3x3 merge gather + one projection into fp32 rows, or with a second projection
 // bf16(GELU(first)) into the inner buffer (grown on demand), then the second into fp32.
 vit_status run_aligner(vit_ctx *c, const bf16_t *y, const ImgDesc *imgs, int ni, int64_t M, float *out,
@@ -382,18 +404,8 @@ vit_status run_aligner(vit_ctx *c, const bf16_t *y, const ImgDesc *imgs, int ni,
                                        c->d_zero, gws, s));
         return VIT_OK;
     }
-    if (M > c->cap_tokens) {
-        HIP_TRY(c, hipDeviceSynchronize());
-        if (c->a1) (void)hipFree(c->a1);
-        c->a1 = nullptr;
-        c->cap_tokens = 0;
-        if (hipMalloc((void **)&c->a1, (size_t)M * c->Da * sizeof(bf16_t)) != hipSuccess) {
-            (void)hipGetLastError();
-            c->a1 = nullptr;
-            return fail(c, VIT_E_NOMEM, "aligner workspace allocation failed");
-        }
-        c->cap_tokens = M;
-    }
+    vit_status st = ensure_tokens(c, M);
+    if (st != VIT_OK) return st;
     LAUNCH(c, launch_merge_project(y, imgs, ni, M, c->D, c->d_wproj, c->proj_b, c->Da, gelu_act(c->cfg), false,
                                    c->a1, c->d_zero, gws, s));
     LAUNCH(c, launch_linear(c->a1, M, c->Da, c->wproj2, c->proj2_b, c->Dl, ACT_NONE, true, out, gws, s));
@@ -693,6 +705,7 @@ vit_status vit_reserve(vit_ctx *ctx, int64_t max_patches)
     // is sized here for 64 images and may still grow for batches with more images
     vit_status st = ensure_workspace(ctx, max_patches, max_patches + (int64_t)kVtAlign * 64);
     if (st != VIT_OK) return st;
+    if ((st = ensure_tokens(ctx, max_patches)) != VIT_OK) return st;
     ctx->reserve_cap = max_patches;
     return VIT_OK;
 }

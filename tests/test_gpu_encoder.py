@@ -187,6 +187,36 @@ def test_official_variant_one_layer_end_to_end():
     assert_projector_gate(got, want, "official one layer")
 
 
+def test_official_variant_reserve():
+    """After vit_reserve the two-projection aligner's inner rows are sized for the reserved
+    patches: a batch of 1x1 images (one merged token per patch, the most tokens a batch can
+    have) encodes within the cap, bitwise as an unreserved context does; a batch larger than
+    the reserved workspace (at least 64 patches) is refused with VIT_E_NOMEM and writes
+    nothing."""
+    torch = require_gpu()
+    cfg = synth.TINY_OFFICIAL
+    blob = synth.make_weights(cfg, perturbed=True)
+    grids = [(1, 1)] * 12 + [(6, 6)]
+    n = 12 + 36
+    px = torch.from_numpy(synth.make_pixels(cfg, grids)).cuda()
+    free = vit.Encoder(cfg, blob)
+    want = free.encode(px, grids).cpu().numpy()
+    enc = vit.Encoder(cfg, blob)
+    enc.reserve(n)
+    got = enc.encode(px, grids).cpu().numpy()
+    assert got.shape == (16, cfg.out_hidden) and np.array_equal(got, want)
+    big = grids + [(6, 6)]          # 84 patches: beyond the workspace the reserve allocated
+    px2 = torch.from_numpy(synth.make_pixels(cfg, big)).cuda()
+    out = torch.full((20, cfg.out_hidden), 7.0, device="cuda")
+    with pytest.raises(vit.VitError) as e:
+        enc.encode(px2, big, out=out)
+    assert e.value.status == vit.VIT_E_NOMEM
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())
+    free.close()
+    enc.close()
+
+
 def test_uniform_gray_image_rows_agree():
     """A flat RGB-127 canvas: all patches equal, v equal at every position, so every visual
     row is the same vector up to rounding (positions enter only through q and k)."""

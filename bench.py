@@ -243,6 +243,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="v41_1024",
                     choices=["tiny", "one_layer", "v4_384", "v41_1024", "packed16"])
+    ap.add_argument("--tower", default="base", choices=["base", "official"],
+                    help="official: time the official-layer variant (RMSNorm, SwiGLU, erf GELU, "
+                         "two-linear aligner) as the step instead of the LayerNorm/GELU tower")
+    ap.add_argument("--no-variant", action="store_true",
+                    help="skip the extra official-layer variant measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel timing loop")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -267,6 +272,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     wl = synth.workload(args.workload)
     cfg, grids = wl.cfg, wl.grids
+    if args.tower == "official":
+        import dataclasses
+        cfg = dataclasses.replace(cfg, norm_kind=1, mlp_kind=1, gelu_kind=1, aligner_hidden=cfg.out_hidden)
     N, M = wl.n_patches, wl.n_tokens
     log(f"workload {args.workload}: {len(grids)} image(s), {N} patches, {M} tokens")
     t = time.perf_counter()
@@ -310,7 +318,7 @@ def main():
         "value": M * args.steps / elapsed, "unit": "visual tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": args.workload, "images": len(grids),
+        "config": {"workload": args.workload, "tower": args.tower, "images": len(grids),
                    "grids": grids if len(grids) <= 4 else f"{len(grids)} seeded grids",
                    "patches": N, "tokens": M, "layers": cfg.layers, "hidden": cfg.hidden,
                    "heads": cfg.heads, "mlp": cfg.mlp, "out_hidden": cfg.out_hidden,
@@ -358,7 +366,7 @@ def main():
                                   "traffic_unit": "bytes per launch", "traffic_note": note}
         result["around_the_path"] = around_the_path(enc, cfg, grids, out, args.steps)
         log(json.dumps(kernels, indent=1))
-        if args.workload in ("v4_384", "v41_1024", "packed16"):
+        if args.workload in ("v4_384", "v41_1024", "packed16") and args.tower == "base" and not args.no_variant:
             result["official_layer_variant"] = official_variant(cfg, grids, args.steps, args.warmup)
 
     if not args.no_cpu_baseline:

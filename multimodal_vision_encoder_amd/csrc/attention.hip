@@ -328,14 +328,16 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(
     // S^T of one tile (accumulator started from -m, so the scores come out shifted) and
     // O^T += V^T P^T of an earlier tile; P^T is already in the B-operand layout of the S^T
     // accumulator (the key order inside each 16-key chunk is permuted identically on both
-    // operands).  The two products form four independent accumulation chains.
+    // operands).  The two products form four independent accumulation chains: S^T over the
+    // KS 16-wide slices of the head dim, P.V over the 4 16-key slices of the tile.
     auto mfmas = [&](f32x16_t *sn, const uint32_t (*pk)[4], bool with_pv) {
+        constexpr int NI = KS > 4 ? KS : 4;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < NI; ++i) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
                 if (i < KS) sn[kb] = mfma32_f16(kf[i][kb], qf[i], i == 0 ? cm : sn[kb]);
-            if (with_pv) {
+            if (with_pv && i < 4) {
                 const f16x8_t pf = as_f16x8(make_uint4(pk[i][0], pk[i][1], pk[i][2], pk[i][3]));
 #pragma unroll
                 for (int b = 0; b < DB; ++b) oacc[b] = mfma32_f16(vf[i][b], pf, oacc[b]);

@@ -187,6 +187,34 @@ def test_official_variant_one_layer_end_to_end():
     assert_projector_gate(got, want, "official one layer")
 
 
+@pytest.mark.parametrize("hidden,heads,official", [(128, 4, False), (256, 2, False), (512, 16, True),
+                                                    (1536, 12, False), (2048, 16, True), (128, 8, True)],
+                         ids=["d128_hd32", "d256_hd128", "d512_hd32_official", "d1536_hd128",
+                              "d2048_hd128_official", "d128_hd16_official"])
+def test_widths_and_head_dims_end_to_end(hidden, heads, official):
+    """The other widths (128 .. 2048) and head dims (16, 32, 128) the build supports, both
+    layer kinds, two layers, on a ragged batch (6x6, 5x7, 1x1, 9x12) against the oracle.
+    Gate: rel-L2 <= 1e-2, and max-abs within 5e-2 or, for the wide aligners whose outputs sum
+    up to 9 x 2048 products, within 1.5 x the gap between the fp32 oracle and its fp64 twin on
+    the same rows (an exact implementation can be no closer to the fp32 oracle)."""
+    cfg = replace(synth.TINY, hidden=hidden, heads=heads, mlp=4 * hidden, layers=2, out_hidden=192,
+                  pix_mean=synth.V41.pix_mean, pix_std=synth.V41.pix_std)
+    if official:
+        cfg = replace(cfg, norm_kind=1, mlp_kind=1, gelu_kind=1, aligner_hidden=256)
+    grids = [(6, 6), (5, 7), (1, 1), (9, 12)]
+    blob = synth.make_weights(cfg, perturbed=True)
+    enc, px, got = run(cfg, blob, grids)
+    want = oracle.encode(cfg, blob, px, grids, workers=8)
+    assert got.shape == (4 + 6 + 1 + 12, cfg.out_hidden)
+    r, m = rel_l2(got, want), float(np.abs(got - want).max())
+    bound = 5e-2
+    if m > bound:
+        w64 = oracle.encode(cfg, blob, px, grids, prec="f64", workers=8)
+        bound = max(bound, 1.5 * float(np.abs(w64 - want).max()))
+    assert r <= 1e-2 and m <= bound, (hidden, heads, r, m, bound)
+    enc.close()
+
+
 def test_official_variant_reserve():
     """After vit_reserve the two-projection aligner's inner rows are sized for the reserved
     patches: a batch of 1x1 images (one merged token per patch, the most tokens a batch can

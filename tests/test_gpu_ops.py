@@ -459,6 +459,33 @@ def test_attention_small(name, grids):
                      rows_per_image=lambda n: list(range(min(n, 20))) + [n - 1, n // 2])
 
 
+@pytest.mark.parametrize("hidden,heads", [(128, 8), (128, 4), (1024, 16), (256, 2), (1024, 8)],
+                         ids=["hd16", "hd32", "hd64", "hd128_h2", "hd128_h8"])
+def test_attention_head_dims(hidden, heads):
+    """Every supported head dim with unit-variance q and k, so the softmax is far from
+    uniform and every head dimension moves the scores; ragged images and one spanning several
+    query tiles and key slices."""
+    from dataclasses import replace
+    torch = require_gpu()
+    cfg = replace(synth.TINY, hidden=hidden, heads=heads, mlp=256, layers=0, out_hidden=16)
+    key = ("hd", hidden, heads)
+    if key not in _encs:
+        _encs[key] = (vit.Encoder(cfg, synth.make_weights(cfg)), cfg, None)
+    enc = _encs[key][0]
+    grids = [(5, 7), (1, 1), (20, 21), (2, 3)]
+    qkv = _qkv_for(grids, hidden, 127)
+    d = to_dev_bf16(qkv)
+    vt = enc.op_rope(d, grids)
+    for split in (0, 3):
+        enc.set_attention_split(split)
+        o = enc.op_attention(d, vt, grids)
+        torch.cuda.synchronize()
+        rot = _oracle_rope(f32(qkv), grids, cfg)
+        _attention_check(from_dev_bf16(o), rot, grids, cfg,
+                         rows_per_image=lambda n: list(range(min(n, 12))) + [n - 1, n // 2, 200 % n])
+    enc.set_attention_split(0)
+
+
 def test_attention_single_patch_image_is_v():
     """A 1-patch image attends only to itself: output = v exactly."""
     torch = require_gpu()

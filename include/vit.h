@@ -47,8 +47,9 @@ typedef struct { int32_t gh, gw; } vit_grid;
 
 /* Encoder dimensions.  [Z] "Step 1": 14x14 patches, hidden 1024, 16 heads, 32 layers, 3x3
  * merge, 5120-wide projection (4096 for V4, [G]); token cap 1024 for V4.1, 384 for V4 ([G]).
- * Supported by this build: hidden % 64 == 0, head_dim = hidden/heads in {16, 32, 64, 128},
- * mlp % 64 == 0, patch 14, merge 3, out_hidden >= 1.
+ * Supported by this build: hidden in {64, 128, 256, 512, 1024, 1536, 2048}, head_dim =
+ * hidden/heads in {16, 32, 64, 128}, mlp % 64 == 0, patch in [1, 64] (14 for the V4 / V4.1
+ * towers), merge 3, out_hidden >= 1.
  *
  * Layer kinds.  All zero gives the pre-LayerNorm tower with a GELU (tanh form) MLP and one
  * aligner projection.  The official tower's layers ([Z] "Comparing the DeepSeek V4.1 Flash and

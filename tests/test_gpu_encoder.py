@@ -27,7 +27,12 @@ def run(cfg, blob, grids, pixels=None):
 # bit-exact parts: patchify, the K padding of the patch projection, merge gather, overlay
 # ------------------------------------------------------------------------------------------
 @pytest.mark.parametrize("cfg,grids", [(synth.TINY, [(6, 6)]), (synth.V41, [(5, 7), (2, 9), (1, 1)]),
-                                       (synth.V41, [(24, 24)])], ids=["tiny", "ragged", "one_layer"])
+                                       (synth.V41, [(24, 24)]),
+                                       (replace(synth.TINY, patch=16), [(5, 7), (1, 1), (3, 6)]),
+                                       (replace(synth.TINY, patch=8), [(6, 5), (2, 2)]),
+                                       (replace(synth.TINY, patch=1), [(9, 7)]),
+                                       (replace(synth.TINY, patch=32), [(3, 4)])],
+                         ids=["tiny", "ragged", "one_layer", "patch16", "patch8", "patch1", "patch32"])
 def test_patchify_bit_exact(cfg, grids):
     torch = require_gpu()
     c1 = replace(cfg, layers=0, out_hidden=16)
@@ -37,7 +42,7 @@ def test_patchify_bit_exact(cfg, grids):
     torch.cuda.synchronize()
     off, pix = 0, 0
     for gh, gw in grids:
-        n, npx = gh * gw, 14 * gh * 14 * gw * 3
+        n, npx = gh * gw, c1.patch * gh * c1.patch * gw * 3
         assert np.array_equal(got[off:off + n], oracle.patchify(px[pix:pix + npx], gh, gw, c1))
         off += n
         pix += npx
@@ -122,6 +127,17 @@ def test_tiny_end_to_end(perturbed):
     want = oracle.encode(wl.cfg, blob, px, wl.grids)
     assert got.shape == (4, 128)
     assert_projector_gate(got, want, "tiny")
+
+
+@pytest.mark.parametrize("patch", [16, 8])
+def test_other_patch_sizes_end_to_end(patch):
+    """Patch sides other than 14 (K = 3 p^2 = 768 and 192, zero-padded to multiples of 64)."""
+    cfg = replace(synth.TINY, patch=patch)
+    grids = [(6, 6), (5, 7), (1, 1)]
+    blob = synth.make_weights(cfg, perturbed=True)
+    enc, px, got = run(cfg, blob, grids)
+    want = oracle.encode(cfg, blob, px, grids)
+    assert_projector_gate(got, want, f"patch {patch}")
 
 
 def test_tiny_ragged_multi_image():

@@ -190,7 +190,14 @@ def test_official_variant_first_block_full_length():
     torch.cuda.synchronize()
     rows = np.r_[0:2, 95:98, 4600:4602, 9214:9216]
     got = from_dev_bf16(x1)[rows]
-    W = oracle.Weights(cfg, blob)
+    want = first_block_rows(cfg, oracle.Weights(cfg, blob), px, gh, gw, rows)
+    assert_projector_gate(got, want, "official first block")
+
+
+def first_block_rows(cfg, W, px, gh, gw, rows):
+    """Residual stream after the first block for some rows of one image, from the oracle: q, k,
+    v for every patch, the rest of the block for those rows only (attention rows are
+    independent of one another; the other steps act row by row)."""
     kw = dict(workers=16)
     D, H = cfg.hidden, cfg.heads
     x0 = oracle.linear(oracle.patchify(px, gh, gw, cfg), None, W["pe.b"], Wt=W.T("pe.w"), **kw)
@@ -200,5 +207,29 @@ def test_official_variant_first_block_full_length():
     o = np.stack([oracle.attention(qkv, D, H, rows=(r, r + 1))[r] for r in rows])
     a = oracle.linear(o, None, W["l0.o.b"], Wt=W.T("l0.o.w"))
     x = oracle.add_round(x0[rows], a)
-    want = oracle.add_round(x, oracle.mlp(cfg, oracle.norm(cfg, x, W, "l0.ln2"), W, 0))
-    assert_projector_gate(got, want, "official first block")
+    return oracle.add_round(x, oracle.mlp(cfg, oracle.norm(cfg, x, W, "l0.ln2"), W, 0))
+
+
+def test_extreme_aspect_images_first_block():
+    """The longest grids the token cap allows: 3 x 3072 and 3072 x 3 patches (1024 merged tokens
+    each, RoPE positions up to 3071 on one axis), packed in one batch; the residual stream
+    after the first block on rows at both ends and in the middle of each image."""
+    from dataclasses import replace
+    torch = require_gpu()
+    cfg = replace(synth.V41, layers=1)
+    grids = [(3, 3072), (3072, 3)]
+    blob = synth.make_weights(cfg, perturbed=True)
+    px = synth.make_pixels(cfg, grids)
+    enc = vit.Encoder(cfg, blob)
+    x1 = from_dev_bf16(enc.dump(vit.DUMP_LAYER, torch.from_numpy(px).cuda(), grids, 0))
+    torch.cuda.synchronize()
+    W = oracle.Weights(cfg, blob)
+    n = 9216
+    rows = np.r_[0:2, 3070:3074, 6143:6145, n - 2:n]
+    split = 14 * 3 * 14 * 3072 * 3
+    for i, (gh, gw) in enumerate(grids):
+        want = first_block_rows(cfg, W, px[i * split:(i + 1) * split], gh, gw, rows)
+        assert_projector_gate(x1[i * n + rows], want, f"grid {gh}x{gw} first block")
+    out = enc.encode(torch.from_numpy(px).cuda(), grids)
+    torch.cuda.synchronize()
+    assert tuple(out.shape) == (2048, cfg.out_hidden) and bool(torch.isfinite(out).all())

@@ -231,6 +231,20 @@ def test_widths_and_head_dims_end_to_end(hidden, heads, official):
     enc.close()
 
 
+def test_many_small_images():
+    """300 seeded grids from 1x1 to 12x12 in one call (13,557 patches, 1,992 tokens): the
+    per-image metadata, the 64-aligned transposed-V columns of each image, the attention work
+    list and the merge gather all at many images, against the oracle image by image."""
+    cfg = synth.TINY
+    rng = np.random.default_rng(31)
+    grids = [(int(a), int(b)) for a, b in rng.integers(1, 13, size=(300, 2))]
+    blob = synth.make_weights(cfg, perturbed=True)
+    enc, px, got = run(cfg, blob, grids)
+    want = oracle.encode(cfg, blob, px, grids)
+    assert got.shape == want.shape
+    assert_projector_gate(got, want, "300 small images")
+
+
 def test_official_variant_reserve():
     """After vit_reserve the two-projection aligner's inner rows are sized for the reserved
     patches: a batch of 1x1 images (one merged token per patch, the most tokens a batch can

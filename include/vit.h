@@ -2,8 +2,9 @@
  * vit.h -- C ABI of the MI355X (gfx950) vision encoder for DeepSeek V4 / V4.1 Flash.
  *
  * The encoder turns images into visual rows for the language model in five stages:
- * 14x14 RGB patchify, patch projection, a stack of pre-LayerNorm ViT blocks with 2D RoPE,
- * a 3x3 spatial merge, and a projection to the language hidden width.
+ * 14x14 RGB patchify, patch projection, a stack of pre-norm ViT blocks with 2D RoPE
+ * (LayerNorm + GELU MLP, or the official RMSNorm + SwiGLU layers, see vit_config), a 3x3
+ * spatial merge, and the aligner projection(s) to the language hidden width.
  * Sources (web pages, cited by title and section):
  *   [Z] "DeepSeek V4.1 Flash Engineering, Part 3: Integrating Vision" (zhuai.tech)
  *   [G] ds4-learning "glossary/vision": V4 Flash Vision-Exp and V4.1 Flash vision rows
@@ -218,7 +219,7 @@ vit_status vit_assemble(vit_ctx *ctx, uint16_t *d_embeds, int64_t chunk_lo, int6
  *                                              columns hold binary16 (as vit_op_rope)
  *   VIT_DUMP_ATTN        bf16 [N][D]           attention output of layer `arg`
  *   VIT_DUMP_LAYER       bf16 [N][D]           residual stream after layer `arg`
- *   VIT_DUMP_FINAL_NORM  bf16 [N][D]           final LayerNorm output
+ *   VIT_DUMP_FINAL_NORM  bf16 [N][D]           final norm output (LayerNorm or RMSNorm)
  *   VIT_DUMP_MERGED      bf16 [M][9D]          merged projector input, channel-major
  *                                              (same gather as the projector GEMM)
  * N = patches, M = merged tokens of the batch. */
@@ -234,7 +235,10 @@ vit_status vit_dump(vit_ctx *ctx, int32_t boundary, int32_t arg, const uint8_t *
  * HIP event pair around every kernel launch on the caller's stream (no synchronisation);
  * vit_timing_read waits for the last recorded event, writes the summed milliseconds and the
  * launch count of each step kind into ms[VIT_STEP_COUNT] / launches[VIT_STEP_COUNT] (either
- * may be NULL) and starts a new accumulation.  Disabled by default. */
+ * may be NULL) and starts a new accumulation.  Disabled by default.  VIT_STEP_LAYERNORM also
+ * counts the RMSNorm of the official layers, VIT_STEP_FC1 their SwiGLU step (gate and up
+ * projections in one launch), VIT_STEP_FC2 the down projection, and VIT_STEP_PROJECTOR the
+ * whole aligner (both projections when there are two). */
 enum {
     VIT_STEP_PATCH_EMBED = 0, VIT_STEP_LAYERNORM = 1, VIT_STEP_QKV = 2, VIT_STEP_ROPE = 3,
     VIT_STEP_ATTENTION = 4, VIT_STEP_OUT_PROJ = 5, VIT_STEP_FC1 = 6, VIT_STEP_FC2 = 7,

@@ -119,26 +119,41 @@ __device__ __forceinline__ float silu_big(float u)
     return u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(u * -1.4426950408889634f));
 }
 
-// bias (columns n..n+3; columns past N get none) and activation
-template <int ACT>
-__device__ __forceinline__ void bias_act(const bf16_t *bias, int N, int n, const float *v, float *r)
+// Bias of columns n..n+3 as four bf16 in a uint2 (zero without a bias and past N).  With
+// N % 4 == 0, as in every encoder GEMM, it is one 8-byte load from a valid address (columns
+// past N read the last four, and are never stored), with no branch on the column, so that
+// an epilogue can issue the loads of all its columns before it waits for any of them.
+__device__ __forceinline__ uint2 bias4(const bf16_t *bias, int N, int n)
 {
-    if (bias && n + 3 < N) {
-        const uint2 b = *reinterpret_cast<const uint2 *>(bias + n);
-        r[0] = v[0] + __uint_as_float(b.x << 16);
-        r[1] = v[1] + __uint_as_float(b.x & 0xFFFF0000u);
-        r[2] = v[2] + __uint_as_float(b.y << 16);
-        r[3] = v[3] + __uint_as_float(b.y & 0xFFFF0000u);
-    } else {
+    if (!bias) return make_uint2(0u, 0u);
+    if ((N & 3) == 0) return *reinterpret_cast<const uint2 *>(bias + (n < N ? n : N - 4));
+    uint32_t e[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) r[j] = (bias && n + j < N) ? v[j] + bf16_to_f32(bias[n + j]) : v[j];
-    }
+    for (int j = 0; j < 4; ++j) e[j] = n + j < N ? (uint32_t)bias[n + j] : 0u;
+    return make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
+}
+
+// r = v + bias (four bf16 in b), then the activation
+template <int ACT>
+__device__ __forceinline__ void add_act(uint2 b, const float *v, float *r)
+{
+    r[0] = v[0] + __uint_as_float(b.x << 16);
+    r[1] = v[1] + __uint_as_float(b.x & 0xFFFF0000u);
+    r[2] = v[2] + __uint_as_float(b.y << 16);
+    r[3] = v[3] + __uint_as_float(b.y & 0xFFFF0000u);
     if (ACT == ACT_GELU_TANH)
 #pragma unroll
         for (int j = 0; j < 4; ++j) r[j] = gelu_tanh_big(r[j]);
     if (ACT == ACT_GELU_ERF)
 #pragma unroll
         for (int j = 0; j < 4; ++j) r[j] = gelu_erf_big(r[j]);
+}
+
+// bias (columns n..n+3; columns past N get none) and activation
+template <int ACT>
+__device__ __forceinline__ void bias_act(const bf16_t *bias, int N, int n, const float *v, float *r)
+{
+    add_act<ACT>(bias4(bias, N, n), v, r);
 }
 
 // bf16 output.  put(): 4 results -> 8 bytes at dst (LDS staging).  store(): 4 results of row
@@ -151,10 +166,12 @@ struct EpiBF16 {
     const bf16_t *bias;
     int64_t M;
     int N;
-    __device__ __forceinline__ void put(char *dst, int n, const float *v) const
+    __device__ __forceinline__ const bf16_t *bias_ptr() const { return bias; }
+    __device__ __forceinline__ int ncols() const { return N; }
+    __device__ __forceinline__ void put(char *dst, const float *v, uint2 b) const
     {
         float r[4];
-        bias_act<ACT>(bias, N, n, v, r);
+        add_act<ACT>(b, v, r);
         *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]));
     }
     __device__ __forceinline__ void store(int64_t m, int n, const float *v) const
@@ -180,10 +197,12 @@ struct EpiF32 {
     const bf16_t *bias;
     int64_t M;
     int N;
-    __device__ __forceinline__ void put(char *dst, int n, const float *v) const
+    __device__ __forceinline__ const bf16_t *bias_ptr() const { return bias; }
+    __device__ __forceinline__ int ncols() const { return N; }
+    __device__ __forceinline__ void put(char *dst, const float *v, uint2 b) const
     {
         float r[4];
-        bias_act<ACT_NONE>(bias, N, n, v, r);
+        add_act<ACT_NONE>(b, v, r);
         *reinterpret_cast<float4 *>(dst) = make_float4(r[0], r[1], r[2], r[3]);
     }
     __device__ __forceinline__ void store(int64_t m, int n, const float *v) const
@@ -207,7 +226,9 @@ struct EpiPart {
     static constexpr int OUT_BYTES = 4;
     static constexpr bool CUSTOM = false, PAIRED = false;
     float *out;
-    __device__ __forceinline__ void put(char *dst, int, const float *v) const
+    __device__ __forceinline__ const bf16_t *bias_ptr() const { return nullptr; }
+    __device__ __forceinline__ int ncols() const { return 4; }
+    __device__ __forceinline__ void put(char *dst, const float *v, uint2) const
     {
         *reinterpret_cast<float4 *>(dst) = make_float4(v[0], v[1], v[2], v[3]);
     }
@@ -228,12 +249,14 @@ struct EpiSwiGLU {
     const bf16_t *bias;
     int64_t M;
     int N;
-    // g: fused columns nf..nf+3, u: nf+8..nf+11 -> 4 bf16 outputs (8 bytes) at dst
-    __device__ __forceinline__ void put2(char *dst, int nf, const float *g, const float *u) const
+    __device__ __forceinline__ const bf16_t *bias_ptr() const { return bias; }
+    __device__ __forceinline__ int ncols() const { return N; }
+    // g, u: 4 gate and the matching 4 up results, bg, bu their biases -> 4 bf16 outputs at dst
+    __device__ __forceinline__ void put2(char *dst, const float *g, const float *u, uint2 bg, uint2 bu) const
     {
         float rg[4], ru[4], h[4];
-        bias_act<ACT_NONE>(bias, N, nf, g, rg);
-        bias_act<ACT_NONE>(bias, N, nf + 8, u, ru);
+        add_act<ACT_NONE>(bg, g, rg);
+        add_act<ACT_NONE>(bu, u, ru);
 #pragma unroll
         for (int j = 0; j < 4; ++j) h[j] = silu_big(rg[j]) * ru[j];
         *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
@@ -287,10 +310,12 @@ struct EpiQKVRope {
     int n_img;
     const float *cos_t, *sin_t;
     int store_v;
-    __device__ __forceinline__ void put(char *dst, int n, const float *v) const
+    __device__ __forceinline__ const bf16_t *bias_ptr() const { return bias; }
+    __device__ __forceinline__ int ncols() const { return N; }
+    __device__ __forceinline__ void put(char *dst, const float *v, uint2 b) const
     {
         float r[4];
-        bias_act<ACT_NONE>(bias, N, n, v, r);
+        add_act<ACT_NONE>(b, v, r);
         *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]));
     }
     // Bytes of LDS past the staged tile that the epilogue uses: (row, column) on the image's
@@ -630,8 +655,31 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(SRC src, const bf16_t 
     sync();
 
     // acc[i][j][r]: output row l32 of the 32-block, column 8*(r/4) + 4*g + r%4.
+    // The bias of this lane's columns (the same for all its rows), loaded all at once: with a
+    // bias and N % 4 == 0 (a uniform branch) as unconditional 8-byte loads with no wait between
+    // them; otherwise column by column.
+    auto bias_cols = [&](const auto &e, uint2 (*bpre)[4]) {
+        const bf16_t *bp = e.bias_ptr();
+        const int nc = e.ncols();
+        if (bp && (nc & 3) == 0) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int n = n0 + wn * WN + j * 32 + 8 * q + 4 * g;
+                    bpre[j][q] = *reinterpret_cast<const uint2 *>(bp + (n < nc ? n : nc - 4));
+                }
+        } else {
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) bpre[j][q] = bias4(bp, nc, n0 + wn * WN + j * 32 + 8 * q + 4 * g);
+        }
+    };
     // Stage rows of `pitch` bytes in LDS via put(), then write whole rows of the tile.
     auto stage_tile = [&](const auto &e, int pitch, int ob) {
+        uint2 bpre[TN][4];
+        bias_cols(e, bpre);
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -641,7 +689,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(SRC src, const bf16_t 
                     const float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                                         acc[i][j][4 * q + 3]};
                     const int r = wm * WM + i * 32 + l32, c = wn * WN + j * 32 + 8 * q + 4 * g;
-                    e.put(smem + r * pitch + c * ob, n0 + c, v);
+                    e.put(smem + r * pitch + c * ob, v, bpre[j][q]);
                 }
         __syncthreads();
     };
@@ -678,6 +726,8 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(SRC src, const bf16_t 
         // the gate block q = 2p and the up block q = 2p + 1; tile rows of BN/2 bf16
         constexpr int OPITCH = BN + 16;
         static_assert(BM * OPITCH <= SMEM, "paired staging exceeds the LDS of the kernel");
+        uint2 bpre[TN][4];
+        bias_cols(ep, bpre);
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -689,7 +739,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(SRC src, const bf16_t 
                     const float vu[4] = {acc[i][j][8 * p + 4], acc[i][j][8 * p + 5], acc[i][j][8 * p + 6],
                                          acc[i][j][8 * p + 7]};
                     const int r = wm * WM + i * 32 + l32, cb = wn * WN + j * 32;
-                    ep.put2(smem + r * OPITCH + (cb / 2 + 8 * p + 4 * g) * 2, n0 + cb + 16 * p + 4 * g, vg, vu);
+                    ep.put2(smem + r * OPITCH + (cb / 2 + 8 * p + 4 * g) * 2, vg, vu, bpre[j][2 * p], bpre[j][2 * p + 1]);
                 }
         __syncthreads();
         const int rows = (int)(ep.M - m0 < BM ? ep.M - m0 : BM);

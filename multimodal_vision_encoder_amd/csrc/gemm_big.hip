@@ -694,8 +694,26 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(SRC src, const bf16_t 
         __syncthreads();
     };
     // whole rows of a staged tile (tile_bytes per row) to global memory
-    auto write_rows = [&](int pitch, int tile_bytes, char *gout, int64_t gpitch, int rows, int row_bytes) {
-        const int ch = tile_bytes / 16;                     // 16-byte chunks per tile row
+    // A whole tile (every row, full width) reads all its chunks from LDS before it stores any,
+    // so one wait covers the LDS latency of all of them; a partial tile goes chunk by chunk.
+    auto write_rows = [&](auto tbc, int pitch, char *gout, int64_t gpitch, int rows, int row_bytes) {
+        constexpr int TB = decltype(tbc)::value, CH = TB / 16, IT = BM * CH / NT;
+        static_assert(BM * CH % NT == 0, "tile chunks must divide among the threads");
+        if (rows == BM && row_bytes == TB) {
+            uint4 val[IT];
+#pragma unroll
+            for (int it = 0; it < IT; ++it) {
+                const int c = tid + it * NT, r = c / CH, b = (c % CH) * 16;
+                val[it] = *reinterpret_cast<const uint4 *>(smem + r * pitch + b);
+            }
+#pragma unroll
+            for (int it = 0; it < IT; ++it) {
+                const int c = tid + it * NT, r = c / CH, b = (c % CH) * 16;
+                *reinterpret_cast<uint4 *>(gout + r * gpitch + b) = val[it];
+            }
+            return;
+        }
+        const int ch = CH;                                   // 16-byte chunks per tile row
 #pragma unroll 4
         for (int c = tid; c < BM * ch; c += NT) {
             const int r = c / ch, b = (c % ch) * 16;
@@ -713,7 +731,8 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(SRC src, const bf16_t 
     auto staged = [&](const auto &e, int pitch, int ob, char *gout, int64_t gpitch, int rows,
                       int row_bytes) {
         stage_tile(e, pitch, ob);
-        write_rows(pitch, BN * ob, gout, gpitch, rows, row_bytes);
+        write_rows(std::integral_constant<int, BN * std::decay_t<decltype(e)>::OUT_BYTES>{}, pitch, gout, gpitch,
+                   rows, row_bytes);
     };
     if (item >= 0) {   // K slice: raw fp32 partial tile, every row and column (host: BN = 128)
         if constexpr (PSTAGED)
@@ -744,8 +763,8 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(SRC src, const bf16_t 
         __syncthreads();
         const int rows = (int)(ep.M - m0 < BM ? ep.M - m0 : BM);
         const int row_bytes = N - n0 < BN ? N - n0 : BN;     // (fused columns / 2) x 2 bytes
-        write_rows(OPITCH, BN, reinterpret_cast<char *>(ep.out) + (m0 * (N / 2) + n0 / 2) * 2, (int64_t)N, rows,
-                   row_bytes);
+        write_rows(std::integral_constant<int, BN>{}, OPITCH, reinterpret_cast<char *>(ep.out) + (m0 * (N / 2) + n0 / 2) * 2,
+                   (int64_t)N, rows, row_bytes);
     } else if constexpr (EP::CUSTOM) {
         static_assert(STAGED, "custom epilogues need the staged tile");
         const int rows_c = (int)(ep.M - m0 < BM ? ep.M - m0 : BM);

@@ -318,7 +318,8 @@ def workload(name: str) -> Workload:
     one_layer: 336x336 (24x24 -> 64 tokens), one full-width layer, 5120 projection.
     v4_384: 756x882 (54x63 -> 378 tokens), 32 layers, 4096 projection, 2048-row overlay.
     v41_1024: 1344x1344 (96x96 -> 1024 tokens), 32 layers, 5120 projection.
-    packed16: 16 seeded grids (~8k tokens, >70k patches), 32 layers, 5120 projection."""
+    packed16: 16 seeded grids (~8k tokens, >70k patches), 32 layers, 5120 projection.
+    v41_official: the 1024-token image through the official-layer variant of the V4.1 tower."""
     if name == "tiny":
         return Workload(name, TINY, [(6, 6)])
     if name == "one_layer":
@@ -329,7 +330,9 @@ def workload(name: str) -> Workload:
         return Workload(name, V41, [(96, 96)])
     if name == "packed16":
         return Workload(name, V41, packed_grids_batch())
+    if name == "v41_official":
+        return Workload(name, V41_OFFICIAL, [(96, 96)])
     raise KeyError(name)
 
 
-WORKLOADS = ("tiny", "one_layer", "v4_384", "v41_1024", "packed16")
+WORKLOADS = ("tiny", "one_layer", "v4_384", "v41_1024", "packed16", "v41_official")

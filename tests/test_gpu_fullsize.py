@@ -1,6 +1,7 @@
-"""Full-size end-to-end parity: the 32-layer workloads on the GPU against rows written by the
-CPU oracle (``tests/golden/make_golden.py``, which calls only the oracle and the seeded
-generator), plus the overlay of those workloads into prompt embedding matrices.
+"""Full-size end-to-end parity: the 32-layer workloads (and the 1024-token image through the
+official-layer variant of the tower) on the GPU against rows written by the CPU oracle
+(``tests/golden/make_golden.py``, which calls only the oracle and the seeded generator), plus
+the overlay of those workloads into prompt embedding matrices.
 
 Two gates:
 
@@ -53,7 +54,7 @@ def encoded(name):
     return _runs[name]
 
 
-@pytest.mark.parametrize("name", ["v4_384", "v41_1024", "packed16"])
+@pytest.mark.parametrize("name", ["v4_384", "v41_1024", "packed16", "v41_official"])
 def test_full_size_rows_match_oracle(name):
     torch = require_gpu()
     g = golden(name)
@@ -72,7 +73,7 @@ def test_full_size_rows_match_oracle(name):
         (name, err_rel, floor_rel, err_max, floor_max)
 
 
-@pytest.mark.parametrize("name", ["v4_384", "v41_1024", "packed16"])
+@pytest.mark.parametrize("name", ["v4_384", "v41_1024", "packed16", "v41_official"])
 def test_full_size_first_block_matches_oracle(name):
     """Residual stream after the first block, every image at full length, on sampled rows."""
     torch = require_gpu()

@@ -89,6 +89,9 @@ def test_null_context_is_rejected():
     assert L.vit_set_sentinels(None, None, 128) == vit.VIT_E_ARG
     assert L.vit_assemble(None, None, 0, 8, 128, g, 1, None, None, None) == vit.VIT_E_ARG
     assert L.vit_op_qkv_rope(None, None, None, None, g, 1, None, None, 0, None) == vit.VIT_E_ARG
+    assert L.vit_op_rmsnorm(None, None, None, None, 4, 64, None, 1e-6, None, None) == vit.VIT_E_ARG
+    assert L.vit_op_linear(None, None, 4, 64, None, None, 32, vit.ACT_SWIGLU, 0, None, None) == vit.VIT_E_ARG
+    assert L.vit_op_merge_project(None, None, g, 1, None, None) == vit.VIT_E_ARG
 
 
 def test_plan_image_matches_oracle():

@@ -123,6 +123,10 @@ int64_t vit_num_patches(const vit_ctx *ctx, const vit_grid *h_grids, int32_t n_i
  *   d_out_rows: fp32 [vit_num_tokens][out_hidden], image-major, merged tokens row-major
  *              inside each image ([G] V4.1: plain row-major stream).
  * Attention is bidirectional inside each image and never crosses images ([L] DS4V).
+ * Results are bitwise reproducible for the same batch.  The work split (K slices of the
+ * GEMMs, key slices of the attention) is chosen from the size of the whole batch, so the
+ * rows of one image encoded in different batches can differ in summation order, within the
+ * same error bounds.
  * Returns without synchronising the stream. */
 vit_status vit_encode(vit_ctx *ctx, const uint8_t *d_pixels, const vit_grid *h_grids,
                       int32_t n_images, float *d_out_rows, void *stream);

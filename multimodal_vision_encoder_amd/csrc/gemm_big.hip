@@ -816,9 +816,9 @@ __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(EP ep, int tiles
 }
 
 // Split plan of a BM x BN launch (one block per CU).  With T tiles and P CUs, a last round of
-// r = T mod P tiles leaves P - r CUs idle for a whole tile time; cutting those r tiles into s
-// K slices shortens that round to about 1/s of a tile time, at the cost of writing and
-// reading back r*s fp32 partial tiles.  Costs are modelled with the measured time of one
+// r = T mod P tiles (all T tiles when T < P) leaves P - r CUs idle for a whole tile time;
+// cutting those r tiles into s K slices shortens that round to about 1/s of a tile time, at
+// the cost of writing and reading back r*s fp32 partial tiles.  Costs are modelled with the measured time of one
 // 32-wide k-step of a 256 x 128 tile (about 0.5 us) and 4 TB/s for the partial traffic; the
 // split is used when it saves at least 5 us.  Only 256 x 128 tiles with bf16 or fp32 output
 // and N % 4 == 0 are split.
@@ -827,7 +827,7 @@ SplitK plan_split(int64_t M, int N, int K, int BM, int BN, bool allowed)
     SplitK sk{0, 1, 0, 0, nullptr};
     const int64_t tiles = ceil_div(M, BM) * ceil_div(N, BN);
     const int P = cu_count();
-    if (!allowed || BN != 128 || (N & 3) != 0 || P % 8 != 0 || tiles < P) return sk;
+    if (!allowed || BN != 128 || (N & 3) != 0 || P % 8 != 0) return sk;
     const int64_t full = tiles / P * P, left = tiles - full;
     if (left == 0) return sk;
     const int nk = K / BK;

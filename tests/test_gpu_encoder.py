@@ -324,8 +324,11 @@ def test_errors_publish_nothing():
 
 
 def test_deterministic_and_isolated():
-    """Two runs are bitwise identical, and an image's rows do not depend on the other images
-    of the packed batch."""
+    """Two runs of a batch are bitwise identical.  An image's rows do not depend on the other
+    images of the packed batch beyond summation order (the GEMM K split is chosen from the
+    batch size: here the lone image's patch projection is cut into K slices, the pair's is
+    not): encoded alone or next to another image, they meet the parity gate against the
+    oracle and against each other."""
     torch = require_gpu()
     cfg = synth.V41_ONE_LAYER
     blob = synth.make_weights(cfg, perturbed=True)
@@ -339,7 +342,10 @@ def test_deterministic_and_isolated():
     alone = enc.encode(torch.from_numpy(px[n0:]).cuda(), grids[1:]).cpu().numpy()
     torch.cuda.synchronize()
     assert np.array_equal(a, b)
-    assert np.array_equal(a[4 * 5:], alone)
+    want = oracle.encode(cfg, blob, px[n0:], grids[1:], workers=8)
+    assert_projector_gate(a[4 * 5:], want, "in the batch")
+    assert_projector_gate(alone, want, "alone")
+    assert_projector_gate(a[4 * 5:], alone, "in the batch against alone")
 
 
 # ------------------------------------------------------------------------------------------

@@ -138,6 +138,28 @@ def test_linear_split_k_tail(act, out_f32):
         assert_bf16_close(from_dev_bf16(got)[rows], want, atol=sum_bound(A[rows], W), what="split-K tail")
 
 
+@pytest.mark.parametrize("M,K,N,out_f32", [(378, 9216, 4096, True), (3402, 4096, 1024, False)],
+                         ids=["projector_v4", "fc2_v4"])
+def test_linear_split_k_under_one_round(M, K, N, out_f32):
+    """Launches with fewer tiles than compute units (the 384-token image's projector, 64 tiles
+    of 256 x 128, and its fc2, 112 tiles): every tile is cut into K slices whose fp32 partials a
+    second kernel sums in slice order.  Rows in every tile row are checked."""
+    torch = require_gpu()
+    enc, _, _ = encoder()
+    A = seeded_bf16((M, K), 128, 0)
+    W = seeded_bf16((N, K), 128, 1, std=0.02)
+    b = seeded_bf16((N,), 128, 2, std=0.02)
+    got = enc.op_linear(to_dev_bf16(A), to_dev_bf16(W), to_dev_bf16(b), vit.ACT_NONE, out_f32)
+    torch.cuda.synchronize()
+    rows = np.unique(np.r_[0:2, 255:258, np.arange(0, M, 211), M - 3:M])
+    want = oracle.linear(f32(A[rows]), f32(W), f32(b), round_out=not out_f32, workers=8)
+    if out_f32:
+        g = got.cpu().numpy()[rows]
+        assert np.all(np.abs(g - want) <= sum_bound(A[rows], W) + 1e-6 * np.abs(want))
+    else:
+        assert_bf16_close(from_dev_bf16(got)[rows], want, atol=sum_bound(A[rows], W), what="split-K under one round")
+
+
 # ------------------------------------------------------------------------------------------
 # LayerNorm (+ residual)
 # ------------------------------------------------------------------------------------------

@@ -921,29 +921,29 @@ hipError_t run_rows(SrcMerge src, const bf16_t *W, int64_t M, int N, int K, EP e
     return run_big<BM, BN>(src, W, M, N, K, ep, ws, s);
 }
 
+// Tile shape of a launch: 256 x 256 when those tiles give at least one full round of blocks;
+// 128 x 128 when 256 x 128 tiles would occupy at most half of the compute units and K is
+// short (twice the blocks for the same work; with a long K the K split of 256 x 128 tiles
+// does better); 256 x 128 otherwise.
+template <class SRC, class EP>
+hipError_t run_shaped(SRC src, const bf16_t *W, int64_t M, int N, int K, EP ep, const GemmWorkspace *ws,
+                      hipStream_t s)
+{
+    if (use_big_tiles(M, N)) return run_rows<256, 256>(src, W, M, N, K, ep, ws, s);
+    if (K <= 2048 && ceil_div(M, 256) * ceil_div(N, 128) * 2 <= cu_count())
+        return run_rows<128, 128>(src, W, M, N, K, ep, ws, s);
+    return run_rows<256, 128>(src, W, M, N, K, ep, ws, s);
+}
+
 template <class SRC>
 hipError_t dispatch(SRC src, const bf16_t *W, int64_t M, int N, int K, const bf16_t *bias, int act,
                     bool out_f32, void *out, const GemmWorkspace *ws, hipStream_t s)
 {
-    const bool big = use_big_tiles(M, N);
-    if (out_f32) {
-        EpiF32 ep{(float *)out, bias, M, N};
-        return big ? run_rows<256, 256>(src, W, M, N, K, ep, ws, s) : run_rows<256, 128>(src, W, M, N, K, ep, ws, s);
-    }
-    if (act == ACT_GELU_TANH) {
-        EpiBF16<ACT_GELU_TANH> ep{(bf16_t *)out, bias, M, N};
-        return big ? run_rows<256, 256>(src, W, M, N, K, ep, ws, s) : run_rows<256, 128>(src, W, M, N, K, ep, ws, s);
-    }
-    if (act == ACT_GELU_ERF) {
-        EpiBF16<ACT_GELU_ERF> ep{(bf16_t *)out, bias, M, N};
-        return big ? run_rows<256, 256>(src, W, M, N, K, ep, ws, s) : run_rows<256, 128>(src, W, M, N, K, ep, ws, s);
-    }
-    if (act == ACT_SWIGLU) {
-        EpiSwiGLU ep{(bf16_t *)out, bias, M, N};
-        return big ? run_rows<256, 256>(src, W, M, N, K, ep, ws, s) : run_rows<256, 128>(src, W, M, N, K, ep, ws, s);
-    }
-    EpiBF16<ACT_NONE> ep{(bf16_t *)out, bias, M, N};
-    return big ? run_rows<256, 256>(src, W, M, N, K, ep, ws, s) : run_rows<256, 128>(src, W, M, N, K, ep, ws, s);
+    if (out_f32) return run_shaped(src, W, M, N, K, EpiF32{(float *)out, bias, M, N}, ws, s);
+    if (act == ACT_GELU_TANH) return run_shaped(src, W, M, N, K, EpiBF16<ACT_GELU_TANH>{(bf16_t *)out, bias, M, N}, ws, s);
+    if (act == ACT_GELU_ERF) return run_shaped(src, W, M, N, K, EpiBF16<ACT_GELU_ERF>{(bf16_t *)out, bias, M, N}, ws, s);
+    if (act == ACT_SWIGLU) return run_shaped(src, W, M, N, K, EpiSwiGLU{(bf16_t *)out, bias, M, N}, ws, s);
+    return run_shaped(src, W, M, N, K, EpiBF16<ACT_NONE>{(bf16_t *)out, bias, M, N}, ws, s);
 }
 
 }  // namespace
@@ -965,12 +965,6 @@ int cu_count()
 
 size_t gemm_workspace_max_bytes() { return (size_t)cu_count() * 256 * 128 * 4; }
 
-size_t gemm_workspace_bytes(int64_t M, int N, int K)
-{
-    if (use_big_tiles(M, N)) return 0;
-    const SplitK sk = plan_split(M, N, K, 256, 128, true);
-    return sk.splits > 1 ? (size_t)sk.items * 256 * 128 * 4 : 0;
-}
 
 hipError_t launch_linear(const bf16_t *A, int64_t M, int K, const bf16_t *W, const bf16_t *bias,
                          int N, int act, bool out_f32, void *out, const GemmWorkspace *ws, hipStream_t s)

@@ -10,9 +10,8 @@ struct GemmWorkspace {
     size_t bytes;
 };
 
-// Bytes of GemmWorkspace a linear of this shape uses (0: it runs without one), and the most
-// any shape uses on this device.
-size_t gemm_workspace_bytes(int64_t M, int N, int K);
+// Bytes of GemmWorkspace the largest split of any shape uses on this device (at most one
+// fp32 256 x 128 partial tile per compute unit).
 size_t gemm_workspace_max_bytes();
 
 // Activation of the linear epilogue.  ACT_SWIGLU: W and b hold the gate and up rows

@@ -1,8 +1,9 @@
 // Large-tile bf16 "NT" GEMM on gfx950 MFMA:  C[m][n] = epilogue(sum_k A[m][k] W[n][k]).
 //
-// Block tile BM x BN (256 x 256 or 256 x 128), k-tiles of 32, 8 waves.  Each wave owns a
-// 64 x (BN/2) tile of v_mfma_f32_32x32x16_bf16 blocks, issued with the W fragment first so
-// each lane holds 4 consecutive output columns of one row.
+// Block tile BM x BN (256 x 256, 256 x 128 or 128 x 128, chosen from the launch's size), k-tiles
+// of 32, 8 waves.  Each wave owns a (BM/4) x (BN/2) tile of v_mfma_f32_32x32x16_bf16 blocks,
+// issued with the W fragment first so each lane holds 4 consecutive output columns of one row.
+// Tiles are dealt to the 8 XCDs in contiguous ranges, in groups of 4 tile rows.
 //
 // Copies: A and W k-tiles move global -> LDS with global_load_lds_dwordx4 (no register
 // staging) into a 4-stage ring.  They are inline assembly so that the compiler's wait-count
@@ -18,11 +19,12 @@
 // matrix core busy while the other reads LDS and issues copies.  Group 0 copies the A tile,
 // group 1 the W tile.
 //
-// Epilogue: bias and activation are applied in registers, the tile is staged in LDS (rows
-// padded by 16 bytes) and written out as whole rows, 16 bytes per lane.
+// Epilogue: each lane loads the bias of its columns once, bias and activation are applied in
+// registers, the tile is staged in LDS (rows padded by 16 bytes) and written out as whole
+// rows, 16 bytes per lane.  The SwiGLU epilogue pairs gate and up columns in registers.
 //
-// Split-K tail: when the tile count leaves a last partial round of blocks, the leftover tiles
-// can be split along K so that the last round fills the chip.  Each slice writes its fp32
+// Split-K tail: when the tile count leaves a last partial round of blocks (or is below one
+// round), the leftover tiles can be split along K so that the last round fills the chip.  Each slice writes its fp32
 // partial tile to a workspace; a second kernel sums the slices in slice order (so results do
 // not depend on timing) and applies the epilogue.  The host enables it only where the time
 // saved exceeds the cost of the partial traffic.

@@ -584,7 +584,7 @@ size_t attention_plan_bytes(const AttnSplit &sp, int D, int H)
     const int64_t tail = sp.per_xcd - sp.full;
     if (sp.slices <= 1 || tail <= 0) return 0;
     const int hd = D / H;
-    return (size_t)8 * tail * sp.slices * 128 * ((size_t)hd * sizeof(uint16_t) + sizeof(float2));
+    return (size_t)8 * tail * sp.slices * attention_q_tile() * ((size_t)hd * sizeof(uint16_t) + sizeof(float2));
 }
 
 // Work split of a batch.  The blocks of one XCD fill its block slots (CUs x resident blocks)

@@ -80,6 +80,25 @@ def test_create_rejects_bad_weights_without_touching_the_device():
     assert L.vit_create(None, ctypes.byref(ctx)) == vit.VIT_E_ARG
 
 
+def test_create_rejects_mismatched_layer_kinds():
+    """A blob laid out for the official layers is refused under the LayerNorm/GELU config and
+    the other way round (their sizes differ), and invalid layer kinds are refused, all before
+    any device work."""
+    L = vit.lib()
+    ctx = ctypes.c_void_p()
+    base, off = synth.TINY, synth.TINY_OFFICIAL
+    for cfg, blob_cfg in ((base, off), (off, base), (replace(off, norm_kind=3), off),
+                          (replace(off, aligner_hidden=100), off)):
+        blob = synth.make_weights(blob_cfg)
+        w = vit.Weights()
+        w.cfg = vit.make_config(cfg)
+        w.blob = blob.ctypes.data
+        w.blob_elems = blob.size
+        assert L.vit_create(ctypes.byref(w), ctypes.byref(ctx)) == vit.VIT_E_ARG
+        assert not ctx.value
+        assert L.vit_last_error(None)
+
+
 def test_null_context_is_rejected():
     L = vit.lib()
     g = vit.grid_array([(6, 6)])

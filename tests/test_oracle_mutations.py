@@ -82,3 +82,78 @@ def test_pin_catches_mutation(name, old, new, pin, tmp_path, monkeypatch):
     monkeypatch.setattr(oracle, "_libs", {})
     with pytest.raises(AssertionError):
         pin()
+
+
+# ------------------------------------------------------------------------------------------
+# mistakes in the oracle's Python layer: the order of the steps and the pixel constants
+# ------------------------------------------------------------------------------------------
+import types
+
+import tests.test_oracle_composition as comp
+
+PY_SRC = os.path.join(os.path.dirname(oracle.__file__), "__init__.py")
+_LN_CASE = lambda: comp.test_encoder_equals_bruteforce_composition(*comp.CASES[0])
+_PAD_CASE = lambda: comp.test_encoder_equals_bruteforce_composition(*comp.CASES[1])
+_OFFICIAL_CASE = lambda: comp.test_encoder_equals_bruteforce_composition(*comp.CASES[2])
+_ALIGNER_CASE = lambda: comp.test_encoder_equals_bruteforce_composition(*comp.CASES[3])
+
+PY_MUTATIONS = [
+    ("residual after attention kept unrounded", "x = add_round(x, a, prec)", "x = x + a",
+     comp.test_constant_values_block_closed_form),
+    ("residual after the MLP kept unrounded", "x = add_round(x, f, prec)", "x = x + f",
+     comp.test_uniform_image_block_closed_form),
+    ("block without LN1", 'ln = norm(cfg, x, W, f"l{l}.ln1", **kw)', "ln = x",
+     comp.test_uniform_image_block_closed_form),
+    ("block without LN2", 'ln2 = norm(cfg, x, W, f"l{l}.ln2", **kw)', "ln2 = x",
+     comp.test_constant_values_block_closed_form),
+    ("post-norm block", "x = add_round(x, a, prec)",
+     'x = norm(cfg, add_round(x, a, prec), W, f"l{l}.ln1", **kw)', _LN_CASE),
+    ("sublayer output replaces the residual", "x = add_round(x, f, prec)", "x = f",
+     comp.test_zero_output_projections_keep_the_patch_embedding),
+    ("no final norm", 'y = norm(cfg, x, W, "lnf", **kw)', "y = x",
+     comp.test_zero_output_projections_keep_the_patch_embedding),
+    ("RoPE skipped", "qkv = rope_qk(qkv, gw, D, H, cfg.rope_base, **kw)", "qkv = qkv", _LN_CASE),
+    ("RoPE given the grid height as the row length", "qkv = rope_qk(qkv, gw, D, H",
+     "qkv = rope_qk(qkv, gh, D, H", _LN_CASE),
+    ("merge of the transposed grid", "A = merge(y, gh, gw, cfg.merge, prec)",
+     "A = merge(y, gw, gh, cfg.merge, prec)", _PAD_CASE),
+    ("SwiGLU gate and up exchanged", 'h = swiglu(g, u, kw.get("prec", "f32"))',
+     'h = swiglu(u, g, kw.get("prec", "f32"))', _OFFICIAL_CASE),
+    ("aligner inner layer left unrounded", 'a1 = linear(A, None, W["proj.b"], act=act, Wt=W.T("proj.w"), **kw)',
+     'a1 = linear(A, None, W["proj.b"], act=act, round_out=False, Wt=W.T("proj.w"), **kw)', _ALIGNER_CASE),
+    ("pixel map with mean and std exchanged",
+     "m32 = [float(np.float32(m)) for m in mean]\n    s32 = [float(np.float32(sd)) for sd in std]",
+     "m32 = [float(np.float32(m)) for m in std]\n    s32 = [float(np.float32(sd)) for sd in mean]",
+     comp.test_clip_pixel_map_endpoints_by_hand),
+    ("pixel map without the 1/255", "s = np.array([1.0 / (255.0 * sd) for sd in s32], dtype=np.float32)",
+     "s = np.array([1.0 / sd for sd in s32], dtype=np.float32)", comp.test_clip_pixel_map_endpoints_by_hand),
+]
+
+
+@pytest.mark.parametrize("name,old,new,pin", PY_MUTATIONS, ids=[m[0] for m in PY_MUTATIONS])
+def test_pin_catches_python_mutation(name, old, new, pin, monkeypatch):
+    """The oracle's Python module with one mistake planted is executed as a private module,
+    and its functions replace the real module's for the duration of the named pin."""
+    src = open(PY_SRC).read()
+    assert src.count(old) == 1, f"mutation anchor not found once: {old}"
+    mod = types.ModuleType("oracle_mutant")
+    mod.__file__ = PY_SRC
+    exec(compile(src.replace(old, new), PY_SRC + " (mutant)", "exec"), mod.__dict__)
+    for k, v in vars(mod).items():
+        if isinstance(v, (types.FunctionType, type)) and getattr(v, "__module__", None) == "oracle_mutant":
+            monkeypatch.setattr(oracle, k, v)
+    with pytest.raises(AssertionError):
+        pin()
+
+
+@pytest.mark.parametrize("pin", sorted({m[3] for m in PY_MUTATIONS}, key=id), ids=lambda p: getattr(p, "__name__", "case"))
+def test_python_mutation_harness_control(pin, monkeypatch):
+    """Control: the same harness with no mistake planted leaves every pin passing."""
+    src = open(PY_SRC).read()
+    mod = types.ModuleType("oracle_mutant")
+    mod.__file__ = PY_SRC
+    exec(compile(src, PY_SRC + " (copy)", "exec"), mod.__dict__)
+    for k, v in vars(mod).items():
+        if isinstance(v, (types.FunctionType, type)) and getattr(v, "__module__", None) == "oracle_mutant":
+            monkeypatch.setattr(oracle, k, v)
+    pin()

@@ -60,7 +60,12 @@ def test_patchify_closed_form(cfg):
     gh, gw = 4, 5
     img = _closed_form_image(gh, gw)
     P = oracle.patchify(img.reshape(-1), gh, gw, cfg)
-    s, t = oracle.pixel_affine(cfg.pix_mean, cfg.pix_std)
+    # the constants from their definition (fp32 of 1/(255 std_c) and -mean_c/std_c), not from
+    # the oracle's own helper
+    mean = np.float32(cfg.pix_mean).astype(np.float64)
+    std = np.float32(cfg.pix_std).astype(np.float64)
+    s = (1.0 / (255.0 * std)).astype(np.float32)
+    t = (-mean / std).astype(np.float32)
     # reference order by reshaping the image: (gy, y, gx, x, c) -> (gy, gx, c, y, x)
     blocks = img.reshape(gh, 14, gw, 14, 3).transpose(0, 2, 4, 1, 3).reshape(gh * gw, 588)
     chan = np.repeat(np.arange(3), 196)

@@ -118,11 +118,20 @@ int64_t vit_num_patches(const vit_ctx *ctx, const vit_grid *h_grids, int32_t n_i
 
 /* Encode a packed batch of images into visual rows.
  *   d_pixels:  uint8 RGB, each image HWC [patch*gh][patch*gw][3], images back to back.
- *   h_grids:   n_images patch grids (host).  Each gh, gw >= 1 and each image's merged token
- *              count <= max_tokens_per_image (else VIT_E_BUDGET).
+ *   h_grids:   n_images patch grids (host), 0 <= n_images <= 4096.  Each side in [1, 4096]
+ *              (else VIT_E_ARG: the rotary tables cover 4096 positions per axis) and each
+ *              image's merged token count <= max_tokens_per_image (else VIT_E_BUDGET).
  *   d_out_rows: fp32 [vit_num_tokens][out_hidden], image-major, merged tokens row-major
  *              inside each image ([G] V4.1: plain row-major stream).
  * Attention is bidirectional inside each image and never crosses images ([L] DS4V).
+ * Operand precision inside attention: the tensors between steps are bf16 ([G] V4 Flash row:
+ * intermediates rounded to BF16), but the attention contraction runs on IEEE binary16 MFMA
+ * operands.  Rotated k and v are converted from bf16 to binary16 (round to nearest even:
+ * exact for magnitudes 2^-14 .. 65504, subnormal below, saturating to +-65504 above);
+ * q is scaled by log2(e)/sqrt(head_dim) and rounded once to binary16 (relative error
+ * <= 2^-11, same saturation); the softmax weights enter the value product as binary16
+ * (relative error < 2^-10).  With the encoder's LayerNorm inputs these values stay far
+ * inside the range; k or v entries beyond 65504 in magnitude would be clamped.
  * Results are bitwise reproducible for the same batch.  The work split (K slices of the
  * GEMMs, key slices of the attention) is chosen from the size of the whole batch, so the
  * rows of one image encoded in different batches can differ in summation order, within the

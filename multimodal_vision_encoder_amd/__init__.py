@@ -182,6 +182,51 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def check_tensor(t, name, dtype, shape=None, numel=None, optional=False, gpu=True):
+    """Refuse a tensor the kernels would read or write out of bounds: wrong dtype, not
+    contiguous, wrong shape or element count, or (with gpu) not on a GPU (ValueError).  The
+    checks run in that order, so the host-side ones can be exercised without a GPU."""
+    import torch
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is None")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor, got {type(t).__name__}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(int(v) for v in shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if numel is not None and t.numel() != int(numel):
+        raise ValueError(f"{name} must hold {int(numel)} elements, got {t.numel()}")
+    if gpu:
+        on_gpu(**{name: t})
+
+
+def on_gpu(**tensors):
+    """ValueError unless every given tensor (None entries skipped) lives on a GPU."""
+    for name, t in tensors.items():
+        if t is not None and t.device.type != "cuda":
+            raise ValueError(f"{name} must be on a GPU, got {t.device}")
+
+
+def batch_sizes(grids, patch: int, merge: int = 3):
+    """(patches, merged tokens, pixel bytes) of a batch of (gh, gw) grids: sum of gh*gw, of
+    ceil(gh/merge)*ceil(gw/merge) and of 3*(patch*gh)*(patch*gw).  ValueError on a grid side
+    below 1 (the library validates the rest)."""
+    n = m = px = 0
+    for gh, gw in grids:
+        gh, gw = int(gh), int(gw)
+        if gh < 1 or gw < 1:
+            raise ValueError(f"grid {gh}x{gw}: sides must be >= 1")
+        n += gh * gw
+        m += -(-gh // merge) * -(-gw // merge)
+        px += 3 * patch * gh * patch * gw
+    return n, m, px
+
+
 def _stream(stream=None):
     import torch
     s = torch.cuda.current_stream() if stream is None else stream
@@ -245,17 +290,21 @@ class Encoder:
     def encode(self, pixels, grids, out=None, stream=None):
         """pixels: uint8 CUDA tensor (packed HWC images); returns fp32 [tokens][out_hidden]."""
         import torch
-        M = self.num_tokens(grids)
+        _, M, npx = batch_sizes(grids, int(self.cfg.patch), int(self.cfg.merge))
+        check_tensor(pixels, "pixels", torch.uint8, numel=npx, gpu=False)
         if out is None:
-            out = torch.empty((max(M, 0), self.out_hidden), dtype=torch.float32, device=pixels.device)
+            out = torch.empty((M, self.out_hidden), dtype=torch.float32, device=pixels.device)
+        check_tensor(out, "out", torch.float32, shape=(M, self.out_hidden), gpu=False)
+        on_gpu(pixels=pixels, out=out)
         self._check(lib().vit_encode(self._ctx, _ptr(pixels), grid_array(grids), len(grids),
                                      _ptr(out), _stream(stream)))
         return out
 
     def dump(self, boundary: int, pixels, grids, arg: int = 0, stream=None):
         import torch
-        N, M = self.num_patches(grids), self.num_tokens(grids)
         D, ps = int(self.cfg.hidden), int(self.cfg.patch)
+        N, M, npx = batch_sizes(grids, ps, int(self.cfg.merge))
+        check_tensor(pixels, "pixels", torch.uint8, numel=npx)
         shape = {DUMP_PATCHES: (N, 3 * ps * ps), DUMP_EMBED: (N, D), DUMP_QKV: (N, 3 * D),
                  DUMP_ATTN: (N, D), DUMP_LAYER: (N, D), DUMP_FINAL_NORM: (N, D),
                  DUMP_MERGED: (M, 9 * D)}[boundary]
@@ -267,7 +316,13 @@ class Encoder:
     def overlay(self, embeds, rows, visual_rows, stream=None):
         """embeds: bf16 CUDA tensor [R][out_hidden] (modified in place); rows: host ints
         (negative = skip); visual_rows: fp32 CUDA tensor [len(rows)][out_hidden]."""
-        r = np.ascontiguousarray(np.asarray(rows, dtype=np.int32))
+        import torch
+        r = np.ascontiguousarray(np.asarray(rows, dtype=np.int32).reshape(-1))
+        if embeds is None or embeds.dim() != 2:
+            raise ValueError("embeds must be a 2-D tensor [rows][out_hidden]")
+        check_tensor(embeds, "embeds", torch.bfloat16, shape=(embeds.shape[0], self.out_hidden), gpu=False)
+        check_tensor(visual_rows, "visual_rows", torch.float32, shape=(r.size, self.out_hidden), gpu=False)
+        on_gpu(embeds=embeds, visual_rows=visual_rows)
         self._check(lib().vit_overlay(self._ctx, _ptr(embeds), embeds.shape[0], r.ctypes.data,
                                       _ptr(visual_rows), r.size, int(embeds.shape[1]),
                                       _stream(stream)))
@@ -277,6 +332,7 @@ class Encoder:
         """The gray canvas of `plan` (uint8 CUDA tensor [canvas_h][canvas_w][3]) from src (uint8
         CUDA tensor, HWC height x width x 3)."""
         import torch
+        check_tensor(src, "src", torch.uint8, numel=int(height) * int(width) * 3)
         p = ImagePlan(**plan)
         canvas = torch.empty((plan["canvas_h"], plan["canvas_w"], 3), dtype=torch.uint8, device=src.device)
         self._check(lib().vit_preprocess(self._ctx, _ptr(src), int(height), int(width), ctypes.byref(p),
@@ -292,7 +348,16 @@ class Encoder:
     def assemble(self, chunk, chunk_lo, grids, span_start, visual_rows, stream=None):
         """Write the span positions inside [chunk_lo, chunk_lo + len(chunk)) into chunk (bf16
         CUDA tensor [rows][out_hidden], row j = prompt position chunk_lo + j)."""
-        st = np.ascontiguousarray(np.asarray(span_start, dtype=np.int64))
+        import torch
+        st = np.ascontiguousarray(np.asarray(span_start, dtype=np.int64).reshape(-1))
+        if len(st) != len(grids):
+            raise ValueError("span_start needs one entry per image")
+        _, M, _ = batch_sizes(grids, int(self.cfg.patch), int(self.cfg.merge))
+        if chunk is None or chunk.dim() != 2:
+            raise ValueError("chunk must be a 2-D tensor [rows][out_hidden]")
+        check_tensor(chunk, "chunk", torch.bfloat16, shape=(chunk.shape[0], self.out_hidden), gpu=False)
+        check_tensor(visual_rows, "visual_rows", torch.float32, shape=(M, self.out_hidden), gpu=False)
+        on_gpu(chunk=chunk, visual_rows=visual_rows)
         self._check(lib().vit_assemble(self._ctx, _ptr(chunk), int(chunk_lo),
                                        int(chunk_lo) + int(chunk.shape[0]), int(chunk.shape[1]),
                                        grid_array(grids), len(grids), st.ctypes.data,
@@ -303,8 +368,14 @@ class Encoder:
     def op_linear(self, A, W, b, act=ACT_NONE, out_f32=False, stream=None):
         """act = ACT_SWIGLU takes W, b in the swiglu_interleave layout and returns [M][N/2]."""
         import torch
+        if A is None or A.dim() != 2 or W is None or W.dim() != 2:
+            raise ValueError("A and W must be 2-D tensors")
         M, K = A.shape
         N = W.shape[0]
+        check_tensor(A, "A", torch.bfloat16, shape=(M, K), gpu=False)
+        check_tensor(W, "W", torch.bfloat16, shape=(N, K), gpu=False)
+        check_tensor(b, "b", torch.bfloat16, shape=(N,), optional=True, gpu=False)
+        on_gpu(A=A, W=W, b=b)
         n_out = N // 2 if act == ACT_SWIGLU else N
         out = torch.empty((M, n_out), dtype=torch.float32 if out_f32 else torch.bfloat16, device=A.device)
         self._check(lib().vit_op_linear(self._ctx, _ptr(A), M, K, _ptr(W), _ptr(b), N, act,
@@ -313,16 +384,31 @@ class Encoder:
 
     def op_layernorm(self, x, g, b, eps, delta=None, xout=None, stream=None):
         import torch
-        M, D = x.shape
+        M, D = self._check_rows(x, delta, xout)
+        check_tensor(g, "g", torch.bfloat16, shape=(D,), gpu=False)
+        check_tensor(b, "b", torch.bfloat16, shape=(D,), gpu=False)
+        on_gpu(x=x, delta=delta, xout=xout, g=g, b=b)
         out = torch.empty_like(x)
         self._check(lib().vit_op_layernorm(self._ctx, _ptr(x), _ptr(delta), _ptr(xout), M, D,
                                            _ptr(g), _ptr(b), float(eps), _ptr(out),
                                            _stream(stream)))
         return out
 
+    @staticmethod
+    def _check_rows(x, delta, xout):
+        import torch
+        if x is None or x.dim() != 2:
+            raise ValueError("x must be a 2-D tensor [rows][D]")
+        check_tensor(x, "x", torch.bfloat16, shape=x.shape, gpu=False)
+        check_tensor(delta, "delta", torch.bfloat16, shape=x.shape, optional=True, gpu=False)
+        check_tensor(xout, "xout", torch.bfloat16, shape=x.shape, optional=delta is None, gpu=False)
+        return x.shape
+
     def op_rmsnorm(self, x, g, eps, delta=None, xout=None, stream=None):
         import torch
-        M, D = x.shape
+        M, D = self._check_rows(x, delta, xout)
+        check_tensor(g, "g", torch.bfloat16, shape=(D,), gpu=False)
+        on_gpu(x=x, delta=delta, xout=xout, g=g)
         out = torch.empty_like(x)
         self._check(lib().vit_op_rmsnorm(self._ctx, _ptr(x), _ptr(delta), _ptr(xout), M, D,
                                          _ptr(g), float(eps), _ptr(out), _stream(stream)))
@@ -333,6 +419,8 @@ class Encoder:
         (torch.float16)."""
         import torch
         H, D = int(self.cfg.heads), int(self.cfg.hidden)
+        N, _, _ = batch_sizes(grids, int(self.cfg.patch), int(self.cfg.merge))
+        check_tensor(qkv, "qkv", torch.bfloat16, shape=(N, 3 * D))
         vt = torch.empty((H, D // H, vt_stride(grids)), dtype=torch.float16, device=qkv.device)
         self._check(lib().vit_op_rope(self._ctx, _ptr(qkv), _ptr(vt), grid_array(grids),
                                       len(grids), _stream(stream)))
@@ -343,6 +431,11 @@ class Encoder:
         binary16 bits and v only with store_v, vt torch.float16 [H][hd][vt_stride])."""
         import torch
         H, D = int(self.cfg.heads), int(self.cfg.hidden)
+        N, _, _ = batch_sizes(grids, int(self.cfg.patch), int(self.cfg.merge))
+        check_tensor(x, "x", torch.bfloat16, shape=(N, D), gpu=False)
+        check_tensor(W, "W", torch.bfloat16, shape=(3 * D, D), gpu=False)
+        check_tensor(b, "b", torch.bfloat16, shape=(3 * D,), optional=True, gpu=False)
+        on_gpu(x=x, W=W, b=b)
         qkv = torch.zeros((x.shape[0], 3 * D), dtype=torch.bfloat16, device=x.device)
         vt = torch.empty((H, D // H, vt_stride(grids)), dtype=torch.float16, device=x.device)
         self._check(lib().vit_op_qkv_rope(self._ctx, _ptr(x), _ptr(W), _ptr(b), grid_array(grids),
@@ -356,6 +449,11 @@ class Encoder:
 
     def op_attention(self, qkv, vt, grids, stream=None):
         import torch
+        H, D = int(self.cfg.heads), int(self.cfg.hidden)
+        N, _, _ = batch_sizes(grids, int(self.cfg.patch), int(self.cfg.merge))
+        check_tensor(qkv, "qkv", torch.bfloat16, shape=(N, 3 * D), gpu=False)
+        check_tensor(vt, "vt", torch.float16, shape=(H, D // H, vt_stride(grids)), gpu=False)
+        on_gpu(qkv=qkv, vt=vt)
         o = torch.empty((qkv.shape[0], int(self.cfg.hidden)), dtype=torch.bfloat16, device=qkv.device)
         self._check(lib().vit_op_attention(self._ctx, _ptr(qkv), _ptr(vt), grid_array(grids),
                                            len(grids), _ptr(o), _stream(stream)))
@@ -363,8 +461,9 @@ class Encoder:
 
     def op_merge_project(self, y, grids, stream=None):
         import torch
-        out = torch.empty((self.num_tokens(grids), self.out_hidden), dtype=torch.float32,
-                          device=y.device)
+        N, M, _ = batch_sizes(grids, int(self.cfg.patch), int(self.cfg.merge))
+        check_tensor(y, "y", torch.bfloat16, shape=(N, int(self.cfg.hidden)))
+        out = torch.empty((M, self.out_hidden), dtype=torch.float32, device=y.device)
         self._check(lib().vit_op_merge_project(self._ctx, _ptr(y), grid_array(grids), len(grids),
                                                _ptr(out), _stream(stream)))
         return out

@@ -7,10 +7,10 @@
 // One block = 4 waves x 32 queries of one head of one image.  Keys come in tiles of 64.
 //
 // Data movement: K and V^T tiles go global -> LDS with global_load_lds_dwordx4 (no register
-// staging) into two rings of 3 stages each (48 KB per block).  K of a tile is read one
+// staging) into two rings of 4 stages each (64 KB per block).  K of a tile is read one
 // iteration before its V^T, so iteration t issues K of tile t+3 and V^T of tile t+2 and,
-// before its closing barrier, waits only for the copies of the previous iteration: every copy
-// has two iterations to land.  The copies are written as inline assembly (scalar base,
+// before its closing barrier, waits only for its copies up to K of tile t+2: every copy has
+// at least one whole iteration to land.  The copies are written as inline assembly (scalar base,
 // 32-bit per-lane offset, fixed for all tiles) so the compiler neither inserts its
 // conservative wait-for-all-copies before LDS reads nor recomputes addresses per tile; the
 // barrier is a bare s_barrier for the same reason (the fence in __syncthreads waits for every

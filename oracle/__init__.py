@@ -347,6 +347,29 @@ class Weights:
         return self.tt[k]
 
 
+def block(cfg, W: Weights, x: np.ndarray, gh: int, gw: int, l: int, prec: str = "f32",
+          workers: int = 1, dumps: dict | None = None) -> np.ndarray:
+    """Pre-norm block l on the residual stream x (bf16 values, [gh*gw][D]) of one image:
+    LN -> QKV (bias) -> 2D RoPE on q, k -> attention -> out-proj -> residual (bf16) ->
+    LN -> MLP -> residual (bf16).  ``dumps`` receives the rotated qkv and the attention
+    output ([Z] "Step 2" boundary table)."""
+    D, H = cfg.hidden, cfg.heads
+    kw = dict(prec=prec, workers=workers)
+    ln = norm(cfg, x, W, f"l{l}.ln1", **kw)
+    qkv = linear(ln, None, W[f"l{l}.qkv.b"], Wt=W.T(f"l{l}.qkv.w"), **kw)
+    qkv = rope_qk(qkv, gw, D, H, cfg.rope_base, **kw)
+    o = attention(qkv, D, H, **kw)
+    a = linear(o, None, W[f"l{l}.o.b"], Wt=W.T(f"l{l}.o.w"), **kw)
+    x = add_round(x, a, prec)
+    ln2 = norm(cfg, x, W, f"l{l}.ln2", **kw)
+    f = mlp(cfg, ln2, W, l, **kw)
+    x = add_round(x, f, prec)
+    if dumps is not None:
+        dumps["qkv"] = qkv
+        dumps["attn"] = o
+    return x
+
+
 def encode_image(cfg, W: Weights, img: np.ndarray, gh: int, gw: int, prec: str = "f32",
                  workers: int = 1, dumps: dict | None = None, layers: int | None = None):
     """Visual rows (fp32, [mh*mw][out_hidden]) of one image.
@@ -361,7 +384,6 @@ def encode_image(cfg, W: Weights, img: np.ndarray, gh: int, gw: int, prec: str =
     aligner at the same places (see ``norm``, ``mlp`` and ``aligner``).
     ``dumps``, if given, receives the boundary tensors of [Z] "Step 2".
     """
-    D, H = cfg.hidden, cfg.heads
     nl = cfg.layers if layers is None else layers
     kw = dict(prec=prec, workers=workers)
     P = patchify(img, gh, gw, cfg, prec)
@@ -370,20 +392,13 @@ def encode_image(cfg, W: Weights, img: np.ndarray, gh: int, gw: int, prec: str =
         dumps["patches"] = P
         dumps["embed"] = x
     for l in range(nl):
-        ln = norm(cfg, x, W, f"l{l}.ln1", **kw)
-        qkv = linear(ln, None, W[f"l{l}.qkv.b"], Wt=W.T(f"l{l}.qkv.w"), **kw)
-        qkv = rope_qk(qkv, gw, D, H, cfg.rope_base, **kw)
-        o = attention(qkv, D, H, **kw)
-        a = linear(o, None, W[f"l{l}.o.b"], Wt=W.T(f"l{l}.o.w"), **kw)
-        x = add_round(x, a, prec)
-        ln2 = norm(cfg, x, W, f"l{l}.ln2", **kw)
-        f = mlp(cfg, ln2, W, l, **kw)
-        x = add_round(x, f, prec)
+        inner = {} if dumps is not None and l == 0 else None
+        x = block(cfg, W, x, gh, gw, l, dumps=inner, **kw)
         if dumps is not None:
             dumps[f"layer{l}"] = x
             if l == 0:
-                dumps["qkv0"] = qkv
-                dumps["attn0"] = o
+                dumps["qkv0"] = inner["qkv"]
+                dumps["attn0"] = inner["attn"]
     y = norm(cfg, x, W, "lnf", **kw)
     A = merge(y, gh, gw, cfg.merge, prec)
     out = aligner(cfg, A, W, **kw)

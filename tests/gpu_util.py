@@ -10,6 +10,17 @@ def require_gpu():
     return torch
 
 
+def raw_encode(enc, pixels, grids, out) -> int:
+    """vit_encode straight through the C ABI, bypassing the binding's own tensor checks, so
+    that the library's validation of grids and budgets is what is tested; returns the status."""
+    import ctypes
+    import torch
+    import multimodal_vision_encoder_amd as vit
+    return vit.lib().vit_encode(enc._ctx, ctypes.c_void_p(pixels.data_ptr()), vit.grid_array(grids),
+                                len(grids), ctypes.c_void_p(out.data_ptr()),
+                                ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+
+
 def to_dev_bf16(bits: np.ndarray):
     """uint16 bf16 bits (numpy) -> torch.bfloat16 CUDA tensor."""
     import torch

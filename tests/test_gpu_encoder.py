@@ -8,7 +8,7 @@ import pytest
 import multimodal_vision_encoder_amd as vit
 import oracle
 import synth
-from tests.gpu_util import (assert_bf16_close, assert_projector_gate, from_dev_bf16,
+from tests.gpu_util import (assert_bf16_close, assert_projector_gate, from_dev_bf16, raw_encode,
                             qkv_after_rope, rel_l2, require_gpu)
 
 pytestmark = pytest.mark.gpu
@@ -69,19 +69,22 @@ def test_identity_patch_projection_bit_exact():
     assert not x0[:, 588:].any()
 
 
-def test_merge_gather_one_hot_projector_bit_exact():
-    """W_proj row j = e_sigma(j) over all 9D columns (out_hidden = 9D), b = 0: the projector
-    output is the merged input permuted by sigma, exactly; the merged input comes from the
-    oracle's merge of the same seeded rows.  A 5x7 grid exercises the right/bottom padding."""
+@pytest.mark.parametrize("base,grids", [(synth.TINY, [(5, 7), (6, 6), (1, 2)]),
+                                        (synth.V41, [(5, 7), (96, 96), (4, 9), (1, 2)])],
+                         ids=["d64", "d1024_96x96"])
+def test_merge_gather_one_hot_projector_bit_exact(base, grids):
+    """W_proj row j = e_sigma(j) over all 9D columns (out_hidden = 9D: 9,216 columns at full
+    width), b = 0: the projector output is the merged input permuted by sigma, exactly; the
+    merged input comes from the oracle's merge of the same seeded rows ([Z] "Step 4": channel-
+    major 3x3 unfold with right/bottom padding, which the 5x7 and 4x9 grids exercise)."""
     torch = require_gpu()
-    cfg = replace(synth.TINY, out_hidden=9 * synth.TINY.hidden)
+    cfg = replace(base, layers=0, out_hidden=9 * base.hidden)
     blob = synth.make_weights(cfg)
     W = synth.split_weights(cfg, blob)
     sigma = np.random.default_rng(7).permutation(9 * cfg.hidden)
     W["proj.w"][:] = 0
     W["proj.w"][np.arange(9 * cfg.hidden), sigma] = 0x3F80
     enc = vit.Encoder(cfg, blob)
-    grids = [(5, 7), (6, 6), (1, 2)]
     N = sum(a * b for a, b in grids)
     y = synth.normal_bf16(201, 0, N * cfg.hidden).reshape(N, cfg.hidden)
     from tests.gpu_util import to_dev_bf16
@@ -95,13 +98,14 @@ def test_merge_gather_one_hot_projector_bit_exact():
     assert np.array_equal(got, np.concatenate(want))
 
 
-def test_merged_dump_is_the_channel_major_unfold_of_the_final_norm():
+@pytest.mark.parametrize("cfg,grids", [(synth.TINY, [(5, 7), (6, 9)]),
+                                       (replace(synth.V41, layers=0), [(5, 7), (96, 96), (4, 9)])],
+                         ids=["d64", "d1024_96x96"])
+def test_merged_dump_is_the_channel_major_unfold_of_the_final_norm(cfg, grids):
     """vit_dump(MERGED) (the projector's own gather) equals the unfold of vit_dump(FINAL_NORM)
-    with right/bottom zero padding, element for element."""
+    with right/bottom zero padding, element for element, at width 64 and at full width."""
     torch = require_gpu()
-    cfg = synth.TINY
     enc = vit.Encoder(cfg, synth.make_weights(cfg))
-    grids = [(5, 7), (6, 9)]
     px = torch.from_numpy(synth.make_pixels(cfg, grids)).cuda()
     y = enc.dump(vit.DUMP_FINAL_NORM, px, grids).float()
     A = from_dev_bf16(enc.dump(vit.DUMP_MERGED, px, grids))
@@ -303,16 +307,25 @@ def test_errors_publish_nothing():
     with pytest.raises(vit.VitError) as e:
         enc_small.encode(px, grids_ok, out=out)
     assert e.value.status == vit.VIT_E_BUDGET
-    with pytest.raises(vit.VitError) as e:
-        enc.encode(px, [(6, 6), (0, 3)], out=out)
-    assert e.value.status == vit.VIT_E_ARG
-    with pytest.raises(vit.VitError) as e:
-        enc.encode(px, [(6, 6), (6000, 1)], out=out)
-    assert e.value.status == vit.VIT_E_ARG
+    # the library's own checks, through the C ABI (the binding refuses these grids itself)
+    assert raw_encode(enc, px, [(6, 6), (0, 3)], out) == vit.VIT_E_ARG
+    assert raw_encode(enc, px, [(6, 6), (6000, 1)], out) == vit.VIT_E_ARG
     torch.cuda.synchronize()
     assert bool((out == 7.0).all()), "a rejected call must not write any output"
     # an empty batch is valid and writes nothing
-    assert enc.encode(px, [], out=out).shape == out.shape
+    assert raw_encode(enc, px, [], out) == vit.VIT_OK
+    assert enc.encode(px[:0], []).shape == (0, cfg.out_hidden)
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())
+    # the binding refuses tensors the kernels would overrun
+    with pytest.raises(ValueError):
+        enc.encode(px[:-1], grids_ok, out=out)
+    with pytest.raises(ValueError):
+        enc.encode(px, [(6, 6), (0, 3)], out=out)
+    with pytest.raises(ValueError):
+        enc.encode(px, grids_ok, out=out[:3])
+    with pytest.raises(ValueError):
+        enc.encode(px, grids_ok, out=out.to(torch.bfloat16))
     with pytest.raises(vit.VitError):
         enc.overlay(torch.zeros((8, cfg.out_hidden), dtype=torch.bfloat16, device="cuda"),
                     [1, 1], torch.zeros((2, cfg.out_hidden), device="cuda"))

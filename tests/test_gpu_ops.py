@@ -508,6 +508,48 @@ def test_attention_head_dims(hidden, heads):
     enc.set_attention_split(0)
 
 
+def _bf16_bits_rne(x):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("big", ["q", "k", "v"])
+def test_attention_binary16_operand_range(big):
+    """The attention's binary16 operands near the top of their range: one of q, k, v drawn with
+    standard deviation 2^11 .. 2^13 and entries of magnitude 2^15 planted in every head (after
+    the rotation up to 2^15 * sqrt(2) = 46,341 < 65,504), the others scaled so that the scores
+    stay those of an ordinary softmax.  Checked against the oracle at the attention bound on
+    every query row."""
+    torch = require_gpu()
+    enc, cfg, _ = encoder("v41_1layer")
+    D, H = cfg.hidden, cfg.heads
+    grids = [(5, 7), (12, 11)]
+    N = sum(a * b for a, b in grids)
+    scale = {"q": (2.0 ** 11, 2.0 ** -9, 1.0), "k": (2.0 ** -9, 2.0 ** 11, 1.0),
+             "v": (1.0, 1.0, 2.0 ** 13)}[big]
+    x = synth.normal_f32(131, "qkv".index(big), N * 3 * D).reshape(N, 3, D)
+    x = x * np.array(scale, np.float32)[None, :, None]
+    j = "qkv".index(big)
+    rng = np.random.default_rng(131)
+    for h in range(H):
+        rows = rng.choice(N, 3, replace=False)
+        cols = h * (D // H) + rng.choice(D // H, 3, replace=False)
+        x[rows, j, cols] = np.float32(2.0 ** 15) * np.sign(rng.standard_normal(3)).astype(np.float32)
+    x = np.clip(x, -2.0 ** 15, 2.0 ** 15).reshape(N, 3 * D)
+    qkv = _bf16_bits_rne(x)
+    assert np.abs(f32(qkv)).max() == 2.0 ** 15
+    d = to_dev_bf16(qkv)
+    vt = enc.op_rope(d, grids)
+    o = enc.op_attention(d, vt, grids)
+    torch.cuda.synchronize()
+    got = from_dev_bf16(o)
+    assert np.isfinite(got).all()
+    rot = _oracle_rope(f32(qkv), grids, cfg)
+    assert np.abs(rot[:, :2 * D]).max() < 65504
+    _attention_check(got, rot, grids, cfg)
+
+
 def test_attention_single_patch_image_is_v():
     """A 1-patch image attends only to itself: output = v exactly."""
     torch = require_gpu()
@@ -688,9 +730,13 @@ def test_assemble_chunks_exact():
             torch.cuda.synchronize()
             parts.append(d.view(torch.int16).cpu().numpy().view(np.uint16).reshape(b - a, Dl))
         assert np.array_equal(np.concatenate(parts), want)
+    m1 = cfg.tokens(*grids[0])
+    m2 = m1 + cfg.tokens(*grids[1])
     with pytest.raises(vit.VitError):   # overlapping spans
-        enc.assemble(to_dev_bf16(emb), 0, grids[:2], [starts[0], starts[0] + 3], d_rows)
+        enc.assemble(to_dev_bf16(emb), 0, grids[:2], [starts[0], starts[0] + 3], d_rows[:m2])
     with pytest.raises(vit.VitError):   # negative span start
-        enc.assemble(to_dev_bf16(emb), 0, grids[:1], [-1], d_rows)
+        enc.assemble(to_dev_bf16(emb), 0, grids[:1], [-1], d_rows[:m1])
+    with pytest.raises(ValueError):     # visual rows of another batch
+        enc.assemble(to_dev_bf16(emb), 0, grids[:1], [0], d_rows)
     enc.close()
 

@@ -9,7 +9,9 @@ for a test, so this script runs it once and stores, in ``tests/golden/oracle_<wo
                       rounding points, fp64 arithmetic between them): the spread between the
                       two is the method's own sensitivity to summation order at full depth;
   layer0_rows/values  sampled patch rows of the residual stream after the first block (fp32
-                      oracle), for a one-block end-to-end check at full size.
+                      oracle), for a one-block end-to-end check at full size;
+  spread_all_rel/max  rel-L2 and max-abs between the fp64 twin and the fp32 oracle over ALL
+                      visual rows of the stored images (the gate of an all-rows comparison).
 
 It calls only ``oracle`` and the seeded input generator ``synth``; the GPU tests regenerate
 the same inputs from the same seeds.
@@ -58,6 +60,7 @@ def run(name: str, workers: int):
     patch_offs = np.cumsum([0] + [gh * gw for gh, gw in grids])
     out = {"images": np.array(images, np.int64)}
     all_rows, all_vals, all_vals64, l0_rows, l0_vals = [], [], [], [], []
+    every32, every64 = [], []
     for i in images:
         gh, gw = grids[i]
         img = px[offs[i]:offs[i + 1]]
@@ -74,6 +77,8 @@ def run(name: str, workers: int):
         del dumps
         rows64 = oracle.encode_image(cfg, W, img, gh, gw, prec="f64", workers=workers)
         all_vals64.append(rows64[sel])
+        every32.append(np.asarray(rows, np.float64))
+        every64.append(np.asarray(rows64, np.float64))
         print(f"{name} image {i} ({gh}x{gw}): {time.time() - t:.0f} s", flush=True)
     out["rows"] = np.concatenate(all_rows)
     out["values"] = np.concatenate(all_vals).astype(np.float32)
@@ -81,6 +86,11 @@ def run(name: str, workers: int):
     out["layer0_rows"] = np.concatenate(l0_rows)
     out["layer0_values"] = np.concatenate(l0_vals).astype(np.float32)
     out["grids"] = np.array(grids, np.int64)
+    e32, e64 = np.concatenate(every32), np.concatenate(every64)
+    out["spread_all_rel"] = np.float64(np.linalg.norm(e64 - e32) / np.linalg.norm(e64))
+    out["spread_all_max"] = np.float64(np.abs(e64 - e32).max())
+    print(f"{name}: fp64 vs fp32 over all {e32.shape[0]} rows: rel_l2={float(out['spread_all_rel']):.3e} "
+          f"max_abs={float(out['spread_all_max']):.3e}", flush=True)
     path = os.path.join(HERE, f"oracle_{name}.npz")
     np.savez_compressed(path, **out)
     print("wrote", path, out["values"].shape, flush=True)
@@ -88,7 +98,7 @@ def run(name: str, workers: int):
 
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
-    ap.add_argument("workloads", nargs="*", default=["v4_384", "v41_1024", "packed16"])
+    ap.add_argument("workloads", nargs="*", default=["v4_384", "v41_1024", "packed16", "v41_official"])
     ap.add_argument("--workers", type=int, default=os.cpu_count() or 1)
     a = ap.parse_args()
     for w in a.workloads:

@@ -38,6 +38,21 @@ vit_status vit_op_linear(vit_ctx *ctx, const uint16_t *d_A, int64_t M, int32_t K
                          const uint16_t *d_W, const uint16_t *d_b, int32_t N, int32_t act,
                          int32_t out_f32, void *d_out, void *stream);
 
+/* vit_op_linear for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same arguments, kernels and
+ * results (bitwise) as vit_op_linear, but the fp32 split-K partial tiles live in a fixed
+ * device scratch of 32 MiB that the library holds on every GPU it runs on until the process
+ * ends, instead of the context's workspace; the call allocates nothing (no hipMalloc, no
+ * hipFree, no allocating library routine).  All calls on one GPU share that scratch: calls
+ * that overlap in time on one GPU (different streams or threads) race and must be
+ * serialised by the caller.  Nothing in the scratch needs to start at zero (each launch
+ * writes every partial it reads).  VIT_E_ARG as vit_op_linear, and also when the K split
+ * chosen for these sizes would need more than the 32 MiB (not on a 256-CU MI355X, where one
+ * split round holds at most one 256 x 128 fp32 tile per compute unit). */
+vit_status vit_op_linear_noalloc(vit_ctx *ctx, const uint16_t *d_A, int64_t M, int32_t K,
+                                 const uint16_t *d_W, const uint16_t *d_b, int32_t N, int32_t act,
+                                 int32_t out_f32, void *d_out, void *stream);
+
 /* Residual add + LayerNorm over rows of width D (D in {64, 128, 256, 512, 1024, 1536, 2048}):
  *   if d_delta != NULL:  x = bf16(x + delta), written to d_xout (may alias d_x);
  *   out = bf16((x - mean) / sqrt(var + eps) * g + b), mean/var over the row (biased).

@@ -26,7 +26,8 @@ EXPORTS = ("vit_blob_elems", "vit_create", "vit_destroy", "vit_reserve", "vit_nu
            "vit_last_error", "vit_op_linear", "vit_op_layernorm", "vit_vt_stride", "vit_op_rope",
            "vit_op_attention", "vit_op_merge_project", "vit_timing_enable", "vit_timing_read",
            "vit_set_attention_split", "vit_op_qkv_rope", "vit_set_sentinels",
-           "vit_assemble", "vit_plan_image", "vit_preprocess", "vit_op_rmsnorm")
+           "vit_assemble", "vit_plan_image", "vit_preprocess", "vit_op_rmsnorm",
+           "vit_op_linear_noalloc")
 STEP_NAMES = ("patch_embed", "layernorm", "qkv", "rope", "attention", "out_proj", "fc1", "fc2",
               "projector", "overlay")
 
@@ -97,6 +98,7 @@ def lib():
             "vit_dump": (i32, [vp, i32, i32, vp, P(Grid), i32, vp, sz, vp]),
             "vit_last_error": (ctypes.c_char_p, [vp]),
             "vit_op_linear": (i32, [vp, vp, i64, i32, vp, vp, i32, i32, i32, vp, vp]),
+            "vit_op_linear_noalloc": (i32, [vp, vp, i64, i32, vp, vp, i32, i32, i32, vp, vp]),
             "vit_op_layernorm": (i32, [vp, vp, vp, vp, i64, i32, vp, vp, ctypes.c_float, vp, vp]),
             "vit_op_rmsnorm": (i32, [vp, vp, vp, vp, i64, i32, vp, ctypes.c_float, vp, vp]),
             "vit_vt_stride": (i64, [P(Grid), i32]),

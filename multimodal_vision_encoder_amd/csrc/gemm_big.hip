@@ -927,14 +927,24 @@ hipError_t run_rows(SrcMerge src, const bf16_t *W, int64_t M, int N, int K, EP e
 // 128 x 128 when 256 x 128 tiles would occupy at most half of the compute units and K is
 // short (twice the blocks for the same work; with a long K the K split of 256 x 128 tiles
 // does better); 256 x 128 otherwise.
+enum TileKind { TILES_256x256, TILES_128x128, TILES_256x128 };
+
+TileKind tile_kind(int64_t M, int N, int K)
+{
+    if (use_big_tiles(M, N)) return TILES_256x256;
+    if (K <= 2048 && ceil_div(M, 256) * ceil_div(N, 128) * 2 <= cu_count()) return TILES_128x128;
+    return TILES_256x128;
+}
+
 template <class SRC, class EP>
 hipError_t run_shaped(SRC src, const bf16_t *W, int64_t M, int N, int K, EP ep, const GemmWorkspace *ws,
                       hipStream_t s)
 {
-    if (use_big_tiles(M, N)) return run_rows<256, 256>(src, W, M, N, K, ep, ws, s);
-    if (K <= 2048 && ceil_div(M, 256) * ceil_div(N, 128) * 2 <= cu_count())
-        return run_rows<128, 128>(src, W, M, N, K, ep, ws, s);
-    return run_rows<256, 128>(src, W, M, N, K, ep, ws, s);
+    switch (tile_kind(M, N, K)) {
+    case TILES_256x256: return run_rows<256, 256>(src, W, M, N, K, ep, ws, s);
+    case TILES_128x128: return run_rows<128, 128>(src, W, M, N, K, ep, ws, s);
+    default: return run_rows<256, 128>(src, W, M, N, K, ep, ws, s);
+    }
 }
 
 template <class SRC>
@@ -966,6 +976,19 @@ int cu_count()
 
 
 size_t gemm_workspace_max_bytes() { return (size_t)cu_count() * 256 * 128 * 4; }
+
+size_t linear_workspace_bytes(int64_t M, int K, int N, int act, bool out_f32)
+{
+    if (M <= 0 || (act == ACT_SWIGLU && !out_f32)) return 0;   // the paired epilogue never splits
+    int BM = 256, BN = 128;
+    switch (tile_kind(M, N, K)) {
+    case TILES_256x256: return 0;                              // only BN = 128 tiles split
+    case TILES_128x128: BM = 128; break;
+    default: break;
+    }
+    const SplitK sk = plan_split(M, N, K, BM, BN, true);
+    return sk.splits > 1 ? (size_t)sk.items * BM * BN * 4 : 0;
+}
 
 
 hipError_t launch_linear(const bf16_t *A, int64_t M, int K, const bf16_t *W, const bf16_t *bias,

@@ -14,6 +14,10 @@ struct GemmWorkspace {
 // fp32 256 x 128 partial tile per compute unit).
 size_t gemm_workspace_max_bytes();
 
+// Bytes of GemmWorkspace that launch_linear with these arguments uses (0: no K split), given
+// a workspace of gemm_workspace_max_bytes().
+size_t linear_workspace_bytes(int64_t M, int K, int N, int act, bool out_f32);
+
 // Activation of the linear epilogue.  ACT_SWIGLU: W and b hold the gate and up rows
 // interleaved in groups of 8 (N = 2F fused rows), out = bf16 [M][N/2] = bf16(silu(g) u).
 enum { ACT_NONE = 0, ACT_GELU_TANH = 1, ACT_GELU_ERF = 2, ACT_SWIGLU = 3 };

@@ -5,12 +5,16 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
 #include "kernels.h"
 #include "vit.h"
 #include "vit_ops.h"
+
+constexpr size_t kNoAllocScratchBytes = (size_t)256 * 256 * 128 * sizeof(float);   // 32 MiB
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
 
 namespace {
 
@@ -19,6 +23,37 @@ constexpr int kMaxImages = 4096;     // images per call
 constexpr int kVtAlign = 64;         // per-image column alignment of the transposed-V buffer
 
 thread_local std::string g_err;
+
+// Fixed device scratch of vit_op_linear_noalloc: the fp32 split-K partial tiles of one GEMM
+// launch (at most one 256 x 128 tile per compute unit of a 256-CU GPU).  Every GPU the library
+// runs on holds its own copy until the process ends.  In host code `scratch` names a host-side
+// stand-in, never the device memory: its device address is resolved per device with
+// hipGetSymbolAddress (scratch_on_device) and only that address is passed to kernels.
+constexpr int kMaxDevices = 64;
+float *g_scratch_ptr[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on device `dev` (resolved once per device, with that device
+// current); NULL with *err set if it cannot be resolved.
+float *scratch_on_device(int dev, hipError_t *err)
+{
+    *err = hipSuccess;
+    if (dev < 0 || dev >= kMaxDevices) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = (float *)p;
+    }
+    return g_scratch_ptr[dev];
+}
 
 // Per-layer weights.  With the SwiGLU MLP, w1/b1 are the gate and up rows interleaved in
 // groups of 8 (the ACT_SWIGLU layout, 2F rows) and w2/b2 the down projection; with RMSNorm the
@@ -579,6 +614,13 @@ vit_status vit_create(const vit_weights *w, vit_ctx **out)
     } while (0)
 
     CREATE_HIP(hipGetDevice(&c->device));
+    {   // the no-allocation entry point's scratch on this device, resolved at set-up
+        hipError_t e_ = hipSuccess;
+        if (!scratch_on_device(c->device, &e_)) {
+            (void)hipGetLastError();
+            return bad(VIT_E_DEVICE, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e_));
+        }
+    }
     CREATE_HIP(hipEventCreateWithFlags(&c->stage_ev, hipEventDisableTiming));
     CREATE_HIP(hipMalloc((void **)&c->d_zero, 256));
     CREATE_HIP(hipMemset(c->d_zero, 0, 256));
@@ -1022,6 +1064,33 @@ vit_status vit_op_linear(vit_ctx *ctx, const uint16_t *d_A, int64_t M, int32_t K
     if (M == 0) return VIT_OK;
     if (!d_A || !d_W || !d_out) return fail(ctx, VIT_E_ARG, "NULL pointer");
     const GemmWorkspace gws = gemm_ws(ctx);
+    LAUNCH(ctx, launch_linear(d_A, M, K, d_W, d_b, N, act, out_f32 != 0, d_out, &gws, (hipStream_t)stream));
+    return VIT_OK;
+}
+
+vit_status vit_op_linear_noalloc(vit_ctx *ctx, const uint16_t *d_A, int64_t M, int32_t K,
+                                 const uint16_t *d_W, const uint16_t *d_b, int32_t N, int32_t act,
+                                 int32_t out_f32, void *d_out, void *stream)
+{
+    if (!ctx) return fail(nullptr, VIT_E_ARG, "ctx is NULL");
+    if (M < 0 || N < 1 || K < 64 || K % 64) return fail(ctx, VIT_E_ARG, "bad M, N or K");
+    if (act != VIT_ACT_NONE && act != VIT_ACT_GELU_TANH && act != VIT_ACT_GELU_ERF && act != VIT_ACT_SWIGLU)
+        return fail(ctx, VIT_E_ARG, "bad act");
+    if (act != VIT_ACT_NONE && out_f32) return fail(ctx, VIT_E_ARG, "fp32 output takes no activation");
+    if (act == VIT_ACT_SWIGLU && N % 16) return fail(ctx, VIT_E_ARG, "SwiGLU needs N % 16 == 0");
+    if (M == 0) return VIT_OK;
+    if (!d_A || !d_W || !d_out) return fail(ctx, VIT_E_ARG, "NULL pointer");
+    const size_t need = linear_workspace_bytes(M, K, N, act, out_f32 != 0);
+    if (need > kNoAllocScratchBytes)
+        return fail(ctx, VIT_E_ARG, "this GEMM's split-K partials need " + std::to_string(need) +
+                                        " bytes, more than the " + std::to_string(kNoAllocScratchBytes) +
+                                        "-byte fixed scratch of the no-allocation entry point");
+    int dev = 0;
+    HIP_TRY(ctx, hipGetDevice(&dev));
+    hipError_t e = hipSuccess;
+    float *part = scratch_on_device(dev, &e);   // first call on a device resolves it here
+    if (!part) return fail(ctx, VIT_E_DEVICE, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    const GemmWorkspace gws{part, kNoAllocScratchBytes};
     LAUNCH(ctx, launch_linear(d_A, M, K, d_W, d_b, N, act, out_f32 != 0, d_out, &gws, (hipStream_t)stream));
     return VIT_OK;
 }

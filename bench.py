@@ -205,6 +205,180 @@ def official_variant(cfg, grids, steps, warmup):
     return res
 
 
+def pass_distribution(step, n):
+    """Per-pass milliseconds of n passes, each bracketed by its own HIP event pair on the
+    current stream (the stream the library launches on): median, p10, p90."""
+    import numpy as np
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in evs:
+        a.record()
+        step()
+        b.record()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in evs])
+    return {"passes": n, "median_ms": float(np.median(t)), "p10_ms": float(np.percentile(t, 10)),
+            "p90_ms": float(np.percentile(t, 90)), "min_ms": float(t.min()), "max_ms": float(t.max())}
+
+
+class ClockSampler:
+    """Samples the GPU core clock (the active level of the driver's sclk table in sysfs) every
+    50 ms while running; None where the table is not readable."""
+
+    def __init__(self):
+        import glob
+        self.files = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.samples = []
+
+    def _read(self):
+        for f in self.files:
+            try:
+                for line in open(f):
+                    if line.rstrip().endswith("*"):
+                        mhz = float(line.split(":")[1].strip().rstrip("*").strip().lower().replace("mhz", ""))
+                        if mhz > 0:
+                            return mhz
+            except (OSError, ValueError, IndexError):
+                continue
+        return None
+
+    def __enter__(self):
+        import threading
+        self._stop = threading.Event()
+
+        def run():
+            while not self._stop.is_set():
+                v = self._read()
+                if v is not None:
+                    self.samples.append(v)
+                self._stop.wait(0.05)
+        self._t = threading.Thread(target=run, daemon=True)
+        self._t.start()
+        return self
+
+    def __exit__(self, *a):
+        self._stop.set()
+        self._t.join()
+
+    def summary(self):
+        import numpy as np
+        if not self.samples:
+            return {"sclk_mhz": None, "note": "no readable sclk table", "peak_at_clock_tflops": None}
+        mhz = float(np.median(self.samples))
+        return {"sclk_mhz": mhz, "samples": len(self.samples), "source": "sysfs pp_dpm_sclk (active level)",
+                "peak_at_clock_tflops": PEAK_BF16_TFLOPS * mhz / 2400.0,
+                "note": "dense bf16 peak scaled from 2.4 GHz to the sampled clock"}
+
+
+def measure_workload(name, steps, warmup):
+    """A second workload through the same hot path (encode + layout + overlay): wall-clock
+    throughput over `steps` passes, the event-timed per-pass distribution, and the per-kernel
+    times that give the GEMM + attention fraction of the dense bf16 peak."""
+    import numpy as np
+    import torch
+    import multimodal_vision_encoder_amd as vit
+    import synth
+    wl = synth.workload(name)
+    cfg, grids = wl.cfg, wl.grids
+    N, M = wl.n_patches, wl.n_tokens
+    blob = synth.make_weights(cfg)
+    enc = vit.Encoder(cfg, blob)
+    del blob
+    enc.reserve(N)
+    d_px = torch.from_numpy(synth.make_pixels(cfg, grids)).cuda()
+    out = torch.empty((M, cfg.out_hidden), dtype=torch.float32, device="cuda")
+    types, src = vit.layout(grids)
+    R = wl.embed_rows or (64 + types.size)
+    start = (R - types.size) // 2
+    rows = np.full(M, -1, np.int32)
+    img_pos = np.nonzero(types == vit.TOK_IMAGE)[0]
+    rows[src[img_pos]] = start + img_pos
+    embeds = torch.zeros((R, cfg.out_hidden), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        enc.encode(d_px, grids, out=out)
+        vit.layout(grids)
+        enc.overlay(embeds, rows, out)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    ms = el / steps * 1e3
+    fl = flops_per_pass(cfg, grids)
+    res = {"workload": name, "images": len(grids), "patches": N, "tokens": M, "out_hidden": cfg.out_hidden,
+           "embed_rows": R, "ms_per_pass": ms, "visual_tokens_per_s": M * steps / el,
+           "images_per_s": len(grids) * steps / el, "tflops": sum(fl.values()) / (ms * 1e-3) / 1e12}
+    res["mfma_frac"] = res["tflops"] / PEAK_BF16_TFLOPS
+    res["pass_ms"] = pass_distribution(step, max(20, steps))
+    enc.timing(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    tm = enc.timing_read()
+    enc.timing(False)
+    gemm_attn = ("qkv", "attention", "out_proj", "fc1", "fc2")
+    ga_ms = sum(tm[k][0] for k in gemm_attn) / steps
+    res["gemm_attention_mfma_frac"] = sum(fl[k] for k in gemm_attn) / (ga_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
+    res["attention_ms_per_pass"] = tm["attention"][0] / steps
+    res["kernels_ms_per_pass"] = {k: v[0] / steps for k, v in tm.items() if v[1]}
+    enc.close()
+    log(f"{name}: {ms:.3f} ms/pass, {res['visual_tokens_per_s']:.0f} tokens/s, "
+        f"GEMM+attention {res['gemm_attention_mfma_frac']:.3f} of peak")
+    return res
+
+
+def _oracle_image_child(args):
+    """One packed-batch image through the single-threaded oracle in its own process: T_fixed
+    (patchify, patch projection, final norm, merge, projector) and T_layer (one block), on all
+    of the image's patches.  Weights of a one-layer tower with the same shapes (the values
+    do not change the work)."""
+    cfg, (gh, gw), i = args
+    import dataclasses
+    import oracle
+    import synth
+    c1 = dataclasses.replace(cfg, layers=1)
+    W = oracle.Weights(c1, synth.make_weights(c1))
+    img = synth.make_pixels(c1, [(gh, gw)], seed=synth.SEED_PIXELS + i)
+    t0 = time.perf_counter()
+    oracle.encode_image(c1, W, img, gh, gw, workers=1, layers=0)
+    t_fixed = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.encode_image(c1, W, img, gh, gw, workers=1, layers=1)
+    t_layer = max(time.perf_counter() - t0 - t_fixed, 0.0)
+    return t_fixed, t_layer
+
+
+def cpu_baseline_packed(cfg, grids):
+    """The packed 16-image batch on the host: min(16, cores) independent single-threaded oracle
+    processes, one image each; each image's pass is extrapolated as T_fixed + layers T_layer
+    and the batch takes as long as its slowest image."""
+    import multiprocessing as mp
+    cores = min(16, len(os.sched_getaffinity(0)))
+    todo = [(cfg, g, i) for i, g in enumerate(grids)]
+    t0 = time.perf_counter()
+    with mp.get_context("spawn").Pool(cores) as pool:
+        res = pool.map(_oracle_image_child, todo)
+    wall = time.perf_counter() - t0
+    per_image = [tf + cfg.layers * tl for tf, tl in res]
+    # images are dealt to the processes in order; a process runs its images back to back
+    lanes = [0.0] * cores
+    for t in per_image:
+        k = lanes.index(min(lanes))
+        lanes[k] += t
+    t_batch = max(lanes)
+    tokens = sum(cfg.tokens(gh, gw) for gh, gw in grids)
+    return {"value": tokens / t_batch, "unit": "visual tokens/s", "cores": cores, "kind": "oracle",
+            "images_per_s": len(grids) / t_batch, "seconds_per_batch": t_batch,
+            "sample": (f"{len(grids)} images in {cores} single-threaded oracle processes (fp32): per image "
+                       f"T_fixed and 1 of {cfg.layers} blocks timed on all its patches ({wall:.1f} s "
+                       f"wall), each pass extrapolated as T_fixed + {cfg.layers} T_layer, batch time = "
+                       f"the slowest process")}
+
+
 def attention_traffic():
     """(bytes per launch, note) from the committed counter summary, or (None, reason)."""
     import hashlib
@@ -249,6 +423,8 @@ def main():
     ap.add_argument("--no-variant", action="store_true",
                     help="skip the extra official-layer variant measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the 384-token and packed 16-image workloads measured after the headline")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel timing loop")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
@@ -311,6 +487,11 @@ def main():
     ms = elapsed / args.steps * 1e3
     log(f"{args.steps} steps in {elapsed:.3f} s: {ms:.3f} ms/step")
 
+    with ClockSampler() as clk:
+        dist = pass_distribution(step, max(20, args.steps))
+    log(f"event-timed passes: median {dist['median_ms']:.3f} ms, p10 {dist['p10_ms']:.3f}, "
+        f"p90 {dist['p90_ms']:.3f}")
+
     fl = flops_per_pass(cfg, grids)
     total_flops = sum(fl.values())
     result = {
@@ -326,7 +507,11 @@ def main():
         "images_per_s": len(grids) * args.steps / elapsed,
         "tflops": total_flops / (ms * 1e-3) / 1e12,
         "mfma_frac": total_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "pass_ms": dist,
+        "clock": clk.summary(),
     }
+    pk = result["clock"]["peak_at_clock_tflops"]
+    result["mfma_frac_at_clock"] = (total_flops / (dist["median_ms"] * 1e-3) / 1e12 / pk) if pk else None
 
     if not args.no_profile:
         enc.timing(True)
@@ -363,15 +548,25 @@ def main():
             result["roofline"] = {"kernel": "attention", "bound": "mfma", "achieved": achieved,
                                   "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                   "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
-                                  "traffic_unit": "bytes per launch", "traffic_note": note}
+                                  "traffic_unit": "bytes per launch", "traffic_note": note,
+                                  "peak_at_clock": pk,
+                                  "frac_at_clock": achieved / pk if pk else None}
         result["around_the_path"] = around_the_path(enc, cfg, grids, out, args.steps)
         log(json.dumps(kernels, indent=1))
         if args.workload in ("v4_384", "v41_1024", "packed16") and args.tower == "base" and not args.no_variant:
             result["official_layer_variant"] = official_variant(cfg, grids, args.steps, args.warmup)
+    if args.workload == "v41_1024" and args.tower == "base" and not args.no_other_workloads:
+        enc.close()
+        # the 384-token V4 image and the packed 16-image batch, in the same run
+        result["workloads"] = {w: measure_workload(w, args.steps, args.warmup) for w in ("v4_384", "packed16")}
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
         result["cpu_baseline"] = cpu_baseline(cfg, blob, px, grids)
+        if "workloads" in result:
+            log("timing the CPU oracle on the packed batch ...")
+            pw = synth.workload("packed16")
+            result["workloads"]["packed16"]["cpu_baseline"] = cpu_baseline_packed(pw.cfg, pw.grids)
     print(json.dumps(result), flush=True)
     enc.close()
 

@@ -140,8 +140,11 @@ int64_t vit_num_patches(const vit_ctx *ctx, const vit_grid *h_grids, int32_t n_i
 vit_status vit_encode(vit_ctx *ctx, const uint8_t *d_pixels, const vit_grid *h_grids,
                       int32_t n_images, float *d_out_rows, void *stream);
 
-/* Token types of the image span layout. */
-enum { VIT_TOK_START = 1, VIT_TOK_IMAGE = 2, VIT_TOK_NEWLINE = 3, VIT_TOK_END = 4 };
+/* Token types of the image span layout (PAD only in the V4 Flash layout). */
+enum { VIT_TOK_START = 1, VIT_TOK_IMAGE = 2, VIT_TOK_NEWLINE = 3, VIT_TOK_END = 4, VIT_TOK_PAD = 5 };
+
+/* Span layouts: the V4.1 stream (vit_layout) and the V4 Flash stream (vit_layout_v4). */
+enum { VIT_SPAN_V41 = 0, VIT_SPAN_V4 = 1 };
 
 /* Span layout of a batch ([Z] "Connect the complete image-to-text path"; [G] V4.1: START,
  * then per merged row width x IMAGE and one NEWLINE, then END; identity order).  Writes
@@ -150,6 +153,25 @@ enum { VIT_TOK_START = 1, VIT_TOK_IMAGE = 2, VIT_TOK_NEWLINE = 3, VIT_TOK_END = 
  * numbering, as in vit_encode's output) of an IMAGE position, -1 elsewhere.  Host only. */
 vit_status vit_layout(const vit_grid *h_grids, int32_t n_images, int32_t merge,
                       int32_t *h_types, int32_t *h_src, int64_t *n_positions);
+
+/* V4 Flash span layout, same conventions as vit_layout.  The pages name its parts without a
+ * formula ([G] V4 Flash Vision-Exp column: synthetic sentinel tokens, row-pair interleave,
+ * pos % 4 alignment; V4.1 Flash row: V4.1 drops the row-pair interleave and compress_pad;
+ * [L] DS4V: the projector's tile permutation is applied once when rows are assembled with the
+ * named sentinel embeddings).  Reading implemented here, not checked against the official
+ * model: START; then for each pair of merged rows (2p, 2p+1) -- a last lone row when mh is
+ * odd -- the pair's IMAGE positions column by column, (2p, c) then (2p+1, c), and one
+ * NEWLINE; then END; then VIT_TOK_PAD positions up to a multiple of 4 (compress_pad), so a
+ * span that starts at a multiple of 4 also ends on one.  h_src still numbers visual rows as
+ * vit_encode emits them (row-major in each image): the interleave is a permutation of the
+ * IMAGE positions.  Per image 4 * ceil((2 + ceil(mh/2) + mh*mw) / 4) positions.  Host only. */
+vit_status vit_layout_v4(const vit_grid *h_grids, int32_t n_images, int32_t merge, int32_t *h_types,
+                         int32_t *h_src, int64_t *n_positions);
+
+/* Span layout vit_assemble writes: VIT_SPAN_V41 (default) or VIT_SPAN_V4 (vit_layout_v4's
+ * positions; span starts must then be multiples of 4, else vit_assemble returns VIT_E_ARG, and
+ * PAD positions are left as they are).  VIT_E_ARG for other values. */
+vit_status vit_set_span_layout(vit_ctx *ctx, int32_t layout);
 
 /* Overlay visual rows onto prompt embeddings ([Z] "Multimodal basics": vision vectors
  * replace the image-placeholder rows):  d_embeds[h_rows[t]][:] = bf16_rne(d_rows[t][:]) for

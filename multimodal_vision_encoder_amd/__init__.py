@@ -16,7 +16,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libvit.so")
 
 VIT_OK, VIT_E_ARG, VIT_E_BUDGET, VIT_E_NOMEM, VIT_E_DEVICE = 0, 1, 2, 3, 4
-TOK_START, TOK_IMAGE, TOK_NEWLINE, TOK_END = 1, 2, 3, 4
+TOK_START, TOK_IMAGE, TOK_NEWLINE, TOK_END, TOK_PAD = 1, 2, 3, 4, 5
+SPAN_V41, SPAN_V4 = 0, 1
 DUMP_PATCHES, DUMP_EMBED, DUMP_QKV, DUMP_ATTN, DUMP_LAYER, DUMP_FINAL_NORM, DUMP_MERGED = range(7)
 ACT_NONE, ACT_GELU_TANH, ACT_GELU_ERF, ACT_SWIGLU = 0, 1, 2, 3
 
@@ -27,7 +28,7 @@ EXPORTS = ("vit_blob_elems", "vit_create", "vit_destroy", "vit_reserve", "vit_nu
            "vit_op_attention", "vit_op_merge_project", "vit_timing_enable", "vit_timing_read",
            "vit_set_attention_split", "vit_op_qkv_rope", "vit_set_sentinels",
            "vit_assemble", "vit_plan_image", "vit_preprocess", "vit_op_rmsnorm",
-           "vit_op_linear_noalloc")
+           "vit_op_linear_noalloc", "vit_layout_v4", "vit_set_span_layout")
 STEP_NAMES = ("patch_embed", "layernorm", "qkv", "rope", "attention", "out_proj", "fc1", "fc2",
               "projector", "overlay")
 
@@ -94,6 +95,8 @@ def lib():
             "vit_num_patches": (i64, [vp, P(Grid), i32]),
             "vit_encode": (i32, [vp, vp, P(Grid), i32, vp, vp]),
             "vit_layout": (i32, [P(Grid), i32, i32, vp, vp, P(i64)]),
+            "vit_layout_v4": (i32, [P(Grid), i32, i32, vp, vp, P(i64)]),
+            "vit_set_span_layout": (i32, [vp, i32]),
             "vit_overlay": (i32, [vp, vp, i64, vp, vp, i64, i32, vp]),
             "vit_dump": (i32, [vp, i32, i32, vp, P(Grid), i32, vp, sz, vp]),
             "vit_last_error": (ctypes.c_char_p, [vp]),
@@ -160,17 +163,19 @@ def grid_array(grids):
     return arr
 
 
-def layout(grids, merge: int = 3):
-    """Span layout (types, src) of a batch, as int32 numpy arrays."""
+def layout(grids, merge: int = 3, span=SPAN_V41):
+    """Span layout (types, src) of a batch, as int32 numpy arrays (vit_layout, or vit_layout_v4
+    with span=SPAN_V4)."""
     L = lib()
+    fn = L.vit_layout_v4 if span == SPAN_V4 else L.vit_layout
     g = grid_array(grids)
     n = ctypes.c_int64(0)
-    st = L.vit_layout(g, len(grids), merge, None, None, ctypes.byref(n))
+    st = fn(g, len(grids), merge, None, None, ctypes.byref(n))
     if st != VIT_OK:
         raise VitError(st, L.vit_last_error(None).decode())
     types = np.zeros(n.value, np.int32)
     src = np.zeros(n.value, np.int32)
-    st = L.vit_layout(g, len(grids), merge, types.ctypes.data, src.ctypes.data, ctypes.byref(n))
+    st = fn(g, len(grids), merge, types.ctypes.data, src.ctypes.data, ctypes.byref(n))
     if st != VIT_OK:
         raise VitError(st, L.vit_last_error(None).decode())
     return types, src
@@ -340,6 +345,10 @@ class Encoder:
         self._check(lib().vit_preprocess(self._ctx, _ptr(src), int(height), int(width), ctypes.byref(p),
                                          _ptr(canvas), _stream(stream)))
         return canvas
+
+    def set_span_layout(self, span: int):
+        """Span geometry of assemble(): SPAN_V41 or SPAN_V4 (starts at multiples of 4)."""
+        self._check(lib().vit_set_span_layout(self._ctx, int(span)))
 
     def set_sentinels(self, sentinels: np.ndarray):
         """Learned START, NEWLINE, END rows: bf16 bits [3][out_hidden] (host)."""

@@ -96,6 +96,7 @@ struct vit_ctx {
     char *d_attn_ws = nullptr;    // key-slice partials of the attention
     size_t attn_ws_bytes = 0;
     int attn_split_fixed = 0;     // 0: chosen per batch; 1..4: fixed key slices
+    int span_layout = VIT_SPAN_V41;   // span geometry of vit_assemble
     int64_t cap_patches = 0, cap_vt_cols = 0, reserve_cap = 0;
     bf16_t *x = nullptr, *ln = nullptr, *qkv = nullptr, *vt = nullptr, *o = nullptr,
            *delta = nullptr, *h1 = nullptr, *patches = nullptr;
@@ -173,6 +174,47 @@ size_t blob_elems_of(const vit_config &c)
 int gelu_act(const vit_config &c) { return c.gelu_kind == 1 ? ACT_GELU_ERF : ACT_GELU_TANH; }
 
 int64_t tokens_of(int gh, int gw) { return (int64_t)((gh + 2) / 3) * ((gw + 2) / 3); }
+
+constexpr int kSpanAlign = 4;    // V4 Flash spans: positions in groups of 4 ([G] pos % 4)
+
+// Positions of one image's span: V4.1, START + mh (mw IMAGE + NEWLINE) + END; V4 Flash
+// (reading of [G]: row-pair interleave, pos % 4 alignment, compress_pad), START + per pair of
+// merged rows its 2 mw (or mw for a last lone row) IMAGE and one NEWLINE + END, then PAD up to
+// a multiple of 4.
+int64_t span_length(int layout, int64_t mh, int64_t mw)
+{
+    if (layout != VIT_SPAN_V4) return 2 + mh * (mw + 1);
+    const int64_t core = 2 + (mh + 1) / 2 + mh * mw;
+    return (core + kSpanAlign - 1) / kSpanAlign * kSpanAlign;
+}
+
+// Type of position k of an image's span and, for IMAGE, the merged token (r * mw + c) it takes.
+int span_entry(int layout, int64_t mh, int64_t mw, int64_t k, int64_t *tok)
+{
+    *tok = -1;
+    if (k == 0) return VIT_TOK_START;
+    if (layout != VIT_SPAN_V4) {
+        if (k == 1 + mh * (mw + 1)) return VIT_TOK_END;
+        const int64_t q = k - 1, r = q / (mw + 1), c = q - r * (mw + 1);
+        if (c == mw) return VIT_TOK_NEWLINE;
+        *tok = r * mw + c;
+        return VIT_TOK_IMAGE;
+    }
+    const int64_t core = 2 + (mh + 1) / 2 + mh * mw;
+    if (k == core - 1) return VIT_TOK_END;
+    if (k >= core) return VIT_TOK_PAD;
+    const int64_t q = k - 1, pairs = mh / 2, pair_len = 2 * mw + 1;
+    if (q < pairs * pair_len) {
+        const int64_t p = q / pair_len, j = q - p * pair_len;
+        if (j == 2 * mw) return VIT_TOK_NEWLINE;
+        *tok = (2 * p + (j & 1)) * mw + j / 2;
+        return VIT_TOK_IMAGE;
+    }
+    const int64_t j = q - pairs * pair_len;   // the last, lone merged row
+    if (j == mw) return VIT_TOK_NEWLINE;
+    *tok = (mh - 1) * mw + j;
+    return VIT_TOK_IMAGE;
+}
 
 vit_status make_plan(vit_ctx *ctx, const vit_grid *grids, int n, Plan &p)
 {
@@ -792,8 +834,10 @@ vit_status vit_dump(vit_ctx *ctx, int32_t boundary, int32_t arg, const uint8_t *
                        arg, d_dst, dst_bytes);
 }
 
-vit_status vit_layout(const vit_grid *h_grids, int32_t n_images, int32_t merge, int32_t *h_types,
-                      int32_t *h_src, int64_t *n_positions)
+namespace {
+
+vit_status layout_impl(int layout, const vit_grid *h_grids, int32_t n_images, int32_t merge, int32_t *h_types,
+                       int32_t *h_src, int64_t *n_positions)
 {
     if (!n_positions) return fail(nullptr, VIT_E_ARG, "n_positions is NULL");
     if (n_images < 0 || (n_images > 0 && !h_grids) || merge < 1)
@@ -802,25 +846,44 @@ vit_status vit_layout(const vit_grid *h_grids, int32_t n_images, int32_t merge, 
     for (int i = 0; i < n_images; ++i) {
         if (h_grids[i].gh < 1 || h_grids[i].gw < 1) return fail(nullptr, VIT_E_ARG, "bad grid");
         const int64_t mh = (h_grids[i].gh + merge - 1) / merge, mw = (h_grids[i].gw + merge - 1) / merge;
-        total += 2 + mh * (mw + 1);
+        total += span_length(layout, mh, mw);
     }
     *n_positions = total;
     if (!h_types && !h_src) return VIT_OK;
-    int64_t p = 0, row = 0;
-    auto put = [&](int32_t t, int32_t s) {
-        if (h_types) h_types[p] = t;
-        if (h_src) h_src[p] = s;
-        ++p;
-    };
+    int64_t p = 0, first = 0;
     for (int i = 0; i < n_images; ++i) {
         const int64_t mh = (h_grids[i].gh + merge - 1) / merge, mw = (h_grids[i].gw + merge - 1) / merge;
-        put(VIT_TOK_START, -1);
-        for (int64_t r = 0; r < mh; ++r) {
-            for (int64_t cc = 0; cc < mw; ++cc) put(VIT_TOK_IMAGE, (int32_t)row++);
-            put(VIT_TOK_NEWLINE, -1);
+        const int64_t len = span_length(layout, mh, mw);
+        for (int64_t k = 0; k < len; ++k, ++p) {
+            int64_t tok;
+            const int t = span_entry(layout, mh, mw, k, &tok);
+            if (h_types) h_types[p] = t;
+            if (h_src) h_src[p] = tok >= 0 ? (int32_t)(first + tok) : -1;
         }
-        put(VIT_TOK_END, -1);
+        first += mh * mw;
     }
+    return VIT_OK;
+}
+
+}  // namespace
+
+vit_status vit_layout(const vit_grid *h_grids, int32_t n_images, int32_t merge, int32_t *h_types,
+                      int32_t *h_src, int64_t *n_positions)
+{
+    return layout_impl(VIT_SPAN_V41, h_grids, n_images, merge, h_types, h_src, n_positions);
+}
+
+vit_status vit_layout_v4(const vit_grid *h_grids, int32_t n_images, int32_t merge, int32_t *h_types,
+                         int32_t *h_src, int64_t *n_positions)
+{
+    return layout_impl(VIT_SPAN_V4, h_grids, n_images, merge, h_types, h_src, n_positions);
+}
+
+vit_status vit_set_span_layout(vit_ctx *ctx, int32_t layout)
+{
+    if (!ctx) return fail(nullptr, VIT_E_ARG, "ctx is NULL");
+    if (layout != VIT_SPAN_V41 && layout != VIT_SPAN_V4) return fail(ctx, VIT_E_ARG, "unknown span layout");
+    ctx->span_layout = layout;
     return VIT_OK;
 }
 
@@ -976,11 +1039,14 @@ vit_status vit_assemble(vit_ctx *ctx, uint16_t *d_embeds, int64_t chunk_lo, int6
     if (n_images > 0 && !h_span_start) return fail(ctx, VIT_E_ARG, "NULL pointer");
     if (!ctx->d_sentinels) return fail(ctx, VIT_E_ARG, "no sentinel rows: call vit_set_sentinels first");
     // spans: START, mh x (mw IMAGE, NEWLINE), END; they must not overlap
+    const int lay = ctx->span_layout;
     std::vector<std::pair<int64_t, int64_t>> spans;
     for (int i = 0; i < n_images; ++i) {
         const ImgDesc &d = p.imgs[i];
         if (h_span_start[i] < 0) return fail(ctx, VIT_E_ARG, "negative span start");
-        spans.push_back({h_span_start[i], 2 + (int64_t)d.mh * (d.mw + 1)});
+        if (lay == VIT_SPAN_V4 && h_span_start[i] % kSpanAlign)
+            return fail(ctx, VIT_E_ARG, "V4 Flash spans start at multiples of 4");
+        spans.push_back({h_span_start[i], span_length(lay, d.mh, d.mw)});
     }
     std::vector<std::pair<int64_t, int64_t>> sorted = spans;
     std::sort(sorted.begin(), sorted.end());
@@ -993,16 +1059,11 @@ vit_status vit_assemble(vit_ctx *ctx, uint16_t *d_embeds, int64_t chunk_lo, int6
         const int64_t s0 = spans[i].first, len = spans[i].second;
         const int64_t lo = std::max(s0, chunk_lo), hi = std::min(s0 + len, chunk_hi);
         for (int64_t pos = lo; pos < hi; ++pos) {
-            const int64_t k = pos - s0;
-            int32_t src;
-            if (k == 0) {
-                src = -1;                                   // START
-            } else if (k == len - 1) {
-                src = -3;                                   // END
-            } else {
-                const int64_t q = k - 1, r = q / (d.mw + 1), c = q - r * (d.mw + 1);
-                src = c == d.mw ? -2 : (int32_t)(d.tok_off + r * d.mw + c);   // NEWLINE or IMAGE
-            }
+            int64_t tok;
+            const int t = span_entry(lay, d.mh, d.mw, pos - s0, &tok);
+            if (t == VIT_TOK_PAD) continue;                 // left as the caller wrote it
+            const int32_t src = t == VIT_TOK_IMAGE ? (int32_t)(d.tok_off + tok)
+                                : t == VIT_TOK_START ? -1 : t == VIT_TOK_NEWLINE ? -2 : -3;
             entries.push_back((int32_t)(pos - chunk_lo));
             entries.push_back(src);
         }

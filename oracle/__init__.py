@@ -29,8 +29,9 @@ _LIBS = {"f32": os.path.join(_HERE, "liboracle_f32.so"),
          "f64": os.path.join(_HERE, "liboracle_f64.so")}
 _FLAGS = ["-O3", "-march=x86-64-v3", "-ffp-contract=off", "-fno-fast-math", "-shared", "-fPIC"]
 
-# Span token types (row-major layout: START, (IMAGE x mw, NEWLINE) x mh, END).
-TOK_TEXT, TOK_START, TOK_IMAGE, TOK_NEWLINE, TOK_END = 0, 1, 2, 3, 4
+# Span token types (row-major layout: START, (IMAGE x mw, NEWLINE) x mh, END; the V4 Flash
+# reading adds PAD positions at the end of a span).
+TOK_TEXT, TOK_START, TOK_IMAGE, TOK_NEWLINE, TOK_END, TOK_PAD = 0, 1, 2, 3, 4, 5
 
 
 def build(force: bool = True):
@@ -452,6 +453,41 @@ def layout(grids, merge: int = 3):
     return np.array(types, np.int32), np.array(src, np.int32)
 
 
+def layout_v4(grids, merge: int = 3, align: int = 4):
+    """The V4 Flash span layout, as read from [G] (V4 Flash Vision-Exp column: synthetic
+    sentinel tokens, row-pair interleave, pos % 4 alignment; V4.1 row: V4.1 drops the
+    row-pair interleave and compress_pad) and [L] DS4V (the projector's tile permutation is
+    applied once when rows are assembled with the named sentinel embeddings).  Reading (parity
+    unpinned: the pages give no formula):
+      START; then for each pair of merged rows (2p, 2p+1) -- the last row alone when mh is
+      odd -- the pair's IMAGE positions column by column, (2p, c) then (2p+1, c), followed by
+      one NEWLINE; then END; then PAD positions up to a multiple of `align` (compress_pad),
+      so that a span placed at a multiple of `align` ends on one too.
+    Returns (types, src) like ``layout``: src is the visual row (image-major, row-major inside
+    the image as the encoder emits them) of an IMAGE position and -1 elsewhere."""
+    types, src, first = [], [], 0
+    for gh, gw in grids:
+        mh, mw = -(-gh // merge), -(-gw // merge)
+        span_t, span_s = [TOK_START], [-1]
+        for p in range(0, mh, 2):
+            rows_of_pair = [r for r in (p, p + 1) if r < mh]
+            for c in range(mw):
+                for r in rows_of_pair:
+                    span_t.append(TOK_IMAGE)
+                    span_s.append(first + r * mw + c)
+            span_t.append(TOK_NEWLINE)
+            span_s.append(-1)
+        span_t.append(TOK_END)
+        span_s.append(-1)
+        while len(span_t) % align:
+            span_t.append(TOK_PAD)
+            span_s.append(-1)
+        types += span_t
+        src += span_s
+        first += mh * mw
+    return np.array(types, np.int32), np.array(src, np.int32)
+
+
 def overlay(embeds_bits: np.ndarray, placeholder_rows, rows: np.ndarray) -> np.ndarray:
     """embeds[placeholder_rows[t]] = bf16(rows[t]); rows with a negative index are skipped.
     [Z] "Multimodal basics": vision vectors replace the image-placeholder rows."""
@@ -463,7 +499,7 @@ def overlay(embeds_bits: np.ndarray, placeholder_rows, rows: np.ndarray) -> np.n
 
 
 def assemble(embeds_bits: np.ndarray, chunk_lo: int, chunk_hi: int, grids, span_start,
-             rows: np.ndarray, sentinels_bits: np.ndarray, merge: int = 3) -> np.ndarray:
+             rows: np.ndarray, sentinels_bits: np.ndarray, merge: int = 3, v4: bool = False) -> np.ndarray:
     """Embedding rows of one prefill chunk.  [Z] "Connect the complete image-to-text path":
     each image placeholder becomes the span START, (IMAGE x mw, NEWLINE) x mh, END; the
     aligner output replaces the IMAGE positions and learned vectors fill START, NEWLINE and
@@ -473,15 +509,16 @@ def assemble(embeds_bits: np.ndarray, chunk_lo: int, chunk_hi: int, grids, span_
     ``embeds_bits`` (bf16 bits, one row per prompt position chunk_lo .. chunk_hi-1) is copied;
     image i's span starts at prompt position span_start[i]; IMAGE positions take the image's
     visual rows (image-major, as the encoder emits them) rounded to bf16; the other span
-    positions take sentinels_bits[0 / 1 / 2] for START / NEWLINE / END."""
+    positions take sentinels_bits[0 / 1 / 2] for START / NEWLINE / END.  With ``v4`` the spans
+    follow ``layout_v4`` and its PAD positions are left as they are."""
     out = embeds_bits.copy()
     which = {TOK_START: 0, TOK_NEWLINE: 1, TOK_END: 2}
     first = 0   # first visual row of the current image
     for (gh, gw), s0 in zip(grids, span_start):
-        types, src = layout([(gh, gw)], merge)
+        types, src = (layout_v4 if v4 else layout)([(gh, gw)], merge)
         for k in range(len(types)):
             p = s0 + k
-            if not chunk_lo <= p < chunk_hi:
+            if not chunk_lo <= p < chunk_hi or types[k] == TOK_PAD:
                 continue
             if types[k] == TOK_IMAGE:
                 out[p - chunk_lo] = float_to_bf16_bits(rows[first + src[k]])

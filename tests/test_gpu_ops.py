@@ -699,6 +699,41 @@ def _prompt(grids, gaps, seed):
     return starts, pos + gaps[-1]
 
 
+def test_assemble_v4_span_layout_chunks_exact():
+    """The V4 Flash span reading (row-pair interleave, spans at multiples of 4, PAD positions
+    left as they are) written whole and chunk by chunk: bitwise the oracle's assembly."""
+    torch = require_gpu()
+    cfg = synth.TINY
+    enc = vit.Encoder(cfg, synth.make_weights(cfg))
+    enc.set_span_layout(vit.SPAN_V4)
+    Dl = cfg.out_hidden
+    sent = synth.make_sentinels(Dl)
+    enc.set_sentinels(sent)
+    grids = [(6, 9), (5, 7), (3, 3), (12, 3)]
+    starts, pos = [], 8
+    for g in grids:
+        starts.append(pos)
+        t, _ = oracle.layout_v4([g])
+        pos += len(t) + 4
+    R = pos + 4
+    n_vis = sum(cfg.tokens(*g) for g in grids)
+    rows = synth.normal_f32(115, 0, n_vis * Dl, 0.0, 3.0).reshape(n_vis, Dl)
+    emb = seeded_bf16((R, Dl), 115, 1)
+    d_rows = torch.from_numpy(rows).cuda()
+    want = oracle.assemble(emb, 0, R, grids, starts, rows, sent, v4=True)
+    for cuts in ([0, R], [0, 9, 13, 30, R], list(range(0, R, 7)) + [R]):
+        parts = []
+        for a, b in zip(cuts[:-1], cuts[1:]):
+            d = to_dev_bf16(emb[a:b])
+            enc.assemble(d, a, grids, starts, d_rows)
+            torch.cuda.synchronize()
+            parts.append(d.view(torch.int16).cpu().numpy().view(np.uint16).reshape(b - a, Dl))
+        assert np.array_equal(np.concatenate(parts), want)
+    with pytest.raises(vit.VitError):   # a V4 span must start at a multiple of 4
+        enc.assemble(to_dev_bf16(emb), 0, grids[:1], [2], d_rows[:cfg.tokens(*grids[0])])
+    enc.close()
+
+
 def test_assemble_chunks_exact():
     """Learned START/NEWLINE/END rows and the visual rows of four images, written into a
     prompt whole and chunk by chunk (a chunk inside one span, cuts through spans, an empty

@@ -121,6 +121,12 @@ PY_MUTATIONS = [
      'h = swiglu(u, g, kw.get("prec", "f32"))', _OFFICIAL_CASE),
     ("aligner inner layer left unrounded", 'a1 = linear(A, None, W["proj.b"], act=act, Wt=W.T("proj.w"), **kw)',
      'a1 = linear(A, None, W["proj.b"], act=act, round_out=False, Wt=W.T("proj.w"), **kw)', _ALIGNER_CASE),
+    ("V4 layout without the row-pair interleave",
+     "            for c in range(mw):\n                for r in rows_of_pair:",
+     "            for r in rows_of_pair:\n                for c in range(mw):",
+     lambda: __import__("tests.test_layout_v4", fromlist=["x"]).test_v4_layout_closed_forms([(6, 9), (3, 3)])),
+    ("V4 layout without compress_pad", "        while len(span_t) % align:", "        while False:",
+     lambda: __import__("tests.test_layout_v4", fromlist=["x"]).test_v4_layout_closed_forms([(6, 9), (3, 3)])),
     ("pixel map with mean and std exchanged",
      "m32 = [float(np.float32(m)) for m in mean]\n    s32 = [float(np.float32(sd)) for sd in std]",
      "m32 = [float(np.float32(m)) for m in std]\n    s32 = [float(np.float32(sd)) for sd in mean]",

@@ -257,10 +257,18 @@ vit_status vit_assemble(vit_ctx *ctx, uint16_t *d_embeds, int64_t chunk_lo, int6
  *   VIT_DUMP_FINAL_NORM  bf16 [N][D]           final norm output (LayerNorm or RMSNorm)
  *   VIT_DUMP_MERGED      bf16 [M][9D]          merged projector input, channel-major
  *                                              (same gather as the projector GEMM)
+ *   VIT_DUMP_ROPE        fp32 [N][hd]          2D RoPE cos/sin ([Z] "Step 2" table, the
+ *                                              "2D RoPE cos/sin" boundary): row n holds
+ *                                              cos theta_0 .. theta_{hd/2-1} of patch n, then
+ *                                              sin of the same angles, read through the same
+ *                                              device lookup as the QKV epilogue's rotation;
+ *                                              theta = [h f_0 .. h f_{hd/4-1}, w f_0 ..], f_j =
+ *                                              base^(-4j/hd) ([Z] "Step 3"); d_pixels is not
+ *                                              read (may be NULL); d_dst 16-byte aligned
  * N = patches, M = merged tokens of the batch. */
 enum {
     VIT_DUMP_PATCHES = 0, VIT_DUMP_EMBED = 1, VIT_DUMP_QKV = 2, VIT_DUMP_ATTN = 3,
-    VIT_DUMP_LAYER = 4, VIT_DUMP_FINAL_NORM = 5, VIT_DUMP_MERGED = 6
+    VIT_DUMP_LAYER = 4, VIT_DUMP_FINAL_NORM = 5, VIT_DUMP_MERGED = 6, VIT_DUMP_ROPE = 7
 };
 vit_status vit_dump(vit_ctx *ctx, int32_t boundary, int32_t arg, const uint8_t *d_pixels,
                     const vit_grid *h_grids, int32_t n_images, void *d_dst, size_t dst_bytes,

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libvit.so")
 VIT_OK, VIT_E_ARG, VIT_E_BUDGET, VIT_E_NOMEM, VIT_E_DEVICE = 0, 1, 2, 3, 4
 TOK_START, TOK_IMAGE, TOK_NEWLINE, TOK_END, TOK_PAD = 1, 2, 3, 4, 5
 SPAN_V41, SPAN_V4 = 0, 1
-DUMP_PATCHES, DUMP_EMBED, DUMP_QKV, DUMP_ATTN, DUMP_LAYER, DUMP_FINAL_NORM, DUMP_MERGED = range(7)
+DUMP_PATCHES, DUMP_EMBED, DUMP_QKV, DUMP_ATTN, DUMP_LAYER, DUMP_FINAL_NORM, DUMP_MERGED, DUMP_ROPE = range(8)
 ACT_NONE, ACT_GELU_TANH, ACT_GELU_ERF, ACT_SWIGLU = 0, 1, 2, 3
 
 # every entry point declared in include/vit.h and include/vit_ops.h
@@ -312,6 +312,11 @@ class Encoder:
         D, ps = int(self.cfg.hidden), int(self.cfg.patch)
         N, M, npx = batch_sizes(grids, ps, int(self.cfg.merge))
         check_tensor(pixels, "pixels", torch.uint8, numel=npx)
+        if boundary == DUMP_ROPE:   # fp32 [N][hd]: cos of the hd/2 angles, then their sin
+            dst = torch.empty((N, D // int(self.cfg.heads)), dtype=torch.float32, device=pixels.device)
+            self._check(lib().vit_dump(self._ctx, boundary, arg, _ptr(pixels), grid_array(grids),
+                                       len(grids), _ptr(dst), dst.numel() * 4, _stream(stream)))
+            return dst
         shape = {DUMP_PATCHES: (N, 3 * ps * ps), DUMP_EMBED: (N, D), DUMP_QKV: (N, 3 * D),
                  DUMP_ATTN: (N, D), DUMP_LAYER: (N, D), DUMP_FINAL_NORM: (N, D),
                  DUMP_MERGED: (M, 9 * D)}[boundary]

@@ -66,6 +66,43 @@ __device__ __forceinline__ int image_of_token(const ImgDesc *imgs, int n, int64_
     return find_segment(n, row, [&](int i) { return imgs[i].tok_off; });
 }
 
+// Position (row, column) on its image's patch grid of packed patch `row`: patch p of an image
+// sits at (p / gw, p % gw) ([G] V4 Flash vision row: RoPE uses the raw patch grid).
+__device__ __forceinline__ int2 patch_grid_pos(const ImgDesc *imgs, int n, int64_t row)
+{
+    const ImgDesc &d = imgs[image_of_patch(imgs, n, row)];
+    const int lr = (int)(row - d.patch_off), hp = lr / d.gw;
+    return make_int2(hp, lr - hp * d.gw);
+}
+
+// cos and sin of the rotary angles i0 .. i0+7 (i0 % 8 == 0, i0 + 8 <= hd/2) of the patch at
+// grid position hw ([Z] "Step 3": theta = [h f_0 .. h f_{Q-1}, w f_0 .. w f_{Q-1}], Q = hd/4),
+// read from the host-built tables cos_t / sin_t [position][Q] (entry j of position p holds
+// the angle p f_j).  Every RoPE rotation and the rotary-table dump read their angles here.
+template <int HD>
+__device__ __forceinline__ void rope_cos_sin8(const float *cos_t, const float *sin_t, int2 hw, int i0,
+                                              float *cs, float *sn)
+{
+    constexpr int Q4 = HD / 4;
+    if constexpr (Q4 % 8 == 0) {   // the 8 angles lie on one axis: two 16-byte loads each
+        const int ax = i0 >= Q4, j0 = i0 - ax * Q4;
+        const float4 *c4 = reinterpret_cast<const float4 *>(cos_t + (ax ? hw.y : hw.x) * Q4 + j0);
+        const float4 *s4 = reinterpret_cast<const float4 *>(sin_t + (ax ? hw.y : hw.x) * Q4 + j0);
+        const float4 c_a = c4[0], c_b = c4[1], s_a = s4[0], s_b = s4[1];
+        cs[0] = c_a.x, cs[1] = c_a.y, cs[2] = c_a.z, cs[3] = c_a.w;
+        cs[4] = c_b.x, cs[5] = c_b.y, cs[6] = c_b.z, cs[7] = c_b.w;
+        sn[0] = s_a.x, sn[1] = s_a.y, sn[2] = s_a.z, sn[3] = s_a.w;
+        sn[4] = s_b.x, sn[5] = s_b.y, sn[6] = s_b.z, sn[7] = s_b.w;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int i = i0 + e, j = i < Q4 ? i : i - Q4, p = i < Q4 ? hw.x : hw.y;
+            cs[e] = cos_t[p * Q4 + j];
+            sn[e] = sin_t[p * Q4 + j];
+        }
+    }
+}
+
 // Source patch (local row inside the image) of position `pos` (dy*3 + dx) of merged token
 // (my, mx), or -1 when it falls in the right/bottom zero padding.
 __device__ __forceinline__ int merge_source(const ImgDesc &d, int my, int mx, int pos)

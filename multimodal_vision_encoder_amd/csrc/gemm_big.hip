@@ -328,23 +328,17 @@ struct EpiQKVRope {
     template <int BM, int NT>
     __device__ __forceinline__ void prepare(char *pos, int64_t m0, int rows, int tid) const
     {
-        for (int r = tid; r < rows; r += NT) {
-            const int64_t row = m0 + r;
-            const ImgDesc &d = imgs[image_of_patch(imgs, n_img, row)];
-            const int lr = (int)(row - d.patch_off), hp = lr / d.gw;
-            reinterpret_cast<int2 *>(pos)[r] = make_int2(hp, lr - hp * d.gw);
-        }
+        for (int r = tid; r < rows; r += NT) reinterpret_cast<int2 *>(pos)[r] = patch_grid_pos(imgs, n_img, m0 + r);
     }
     template <int BM, int BN, int NT>
     __device__ __forceinline__ void write(const char *smem, int pitch, int64_t m0, int n0, int rows, int tid) const
     {
-        constexpr int HALF = HD / 2, Q4 = HD / 4, HC = HALF / 8, NHB = BN / HD;
+        constexpr int HALF = HD / 2, HC = HALF / 8, NHB = BN / HD;
         static_assert(HD >= 16 && BN % HD == 0, "head blocks must tile the column tile");
         const int2 *pos = reinterpret_cast<const int2 *>(smem + BM * pitch);
         // q and k (and v rows with store_v): item = (row, head block, chunk of 8 elements of
         // the first half and the 8 they pair with); the items of one row are consecutive
-        // lanes, so each row's stores are contiguous.  With Q4 % 8 == 0 a chunk lies on one
-        // axis and takes 8 consecutive angles of it.
+        // lanes, so each row's stores are contiguous.
         for (int w = tid; w < BM * NHB * HC; w += NT) {
             const int r = w / (NHB * HC), it = w - r * (NHB * HC), hb = it / HC, ch = it - hb * HC;
             const int c0 = n0 + hb * HD;
@@ -364,23 +358,7 @@ struct EpiQKVRope {
             }
             const int2 hw = pos[r];
             float cs[8], sn[8];
-            if constexpr (Q4 % 8 == 0) {
-                const int ax = ch * 8 >= Q4, j0 = ch * 8 - ax * Q4;
-                const float4 *c4 = reinterpret_cast<const float4 *>(cos_t + (ax ? hw.y : hw.x) * Q4 + j0);
-                const float4 *s4 = reinterpret_cast<const float4 *>(sin_t + (ax ? hw.y : hw.x) * Q4 + j0);
-                const float4 c_a = c4[0], c_b = c4[1], s_a = s4[0], s_b = s4[1];
-                cs[0] = c_a.x, cs[1] = c_a.y, cs[2] = c_a.z, cs[3] = c_a.w;
-                cs[4] = c_b.x, cs[5] = c_b.y, cs[6] = c_b.z, cs[7] = c_b.w;
-                sn[0] = s_a.x, sn[1] = s_a.y, sn[2] = s_a.z, sn[3] = s_a.w;
-                sn[4] = s_b.x, sn[5] = s_b.y, sn[6] = s_b.z, sn[7] = s_b.w;
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int i = ch * 8 + e, j = i < Q4 ? i : i - Q4, p = i < Q4 ? hw.x : hw.y;
-                    cs[e] = cos_t[p * Q4 + j];
-                    sn[e] = sin_t[p * Q4 + j];
-                }
-            }
+            rope_cos_sin8<HD>(cos_t, sin_t, hw, ch * 8, cs, sn);
             const uint32_t wa[4] = {ua.x, ua.y, ua.z, ua.w}, wb[4] = {ub.x, ub.y, ub.z, ub.w};
             float na[8], nb[8];
 #pragma unroll

@@ -105,6 +105,10 @@ hipError_t launch_dump_patches(const uint8_t *px, const ImgDesc *imgs, int n_img
                                hipStream_t s);
 hipError_t launch_dump_merged(const bf16_t *y, const ImgDesc *imgs, int n_img, int64_t Mtok,
                               int D, bf16_t *out, const bf16_t *zero, hipStream_t s);
+// Rotary angles of every packed patch as the RoPE rotations read them: out fp32 [M][hd] =
+// [cos theta_0 .. theta_{hd/2-1} | sin of the same].
+hipError_t launch_dump_rope(const ImgDesc *imgs, int n_img, int64_t M, int hd, const float *cos_t,
+                            const float *sin_t, float *out, hipStream_t s);
 
 // Rows of an attention query tile (one block) and of a RoPE tile.
 int attention_q_tile();

@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256) void rope_kernel(bf16_t *__restrict__ qkv, bf1
                                                    const float *__restrict__ cos_t,
                                                    const float *__restrict__ sin_t)
 {
-    constexpr int HALF = HD / 2, Q4 = HD / 4, T = kRopeTile, HC = HALF / 8;   // chunks per half
+    constexpr int HALF = HD / 2, T = kRopeTile, HC = HALF / 8;   // chunks per half
     constexpr int VLD = T + 8;                      // LDS row of the transposed v tile
     __shared__ __attribute__((aligned(16))) uint16_t sv[HD * VLD];   // binary16 bits
 
@@ -92,19 +92,15 @@ __global__ __launch_bounds__(256) void rope_kernel(bf16_t *__restrict__ qkv, bf1
         const int r = w / (2 * HC), rem = w - r * (2 * HC), part = rem / HC, ch = rem - part * HC;
         const int lr = tile.r0 + r;
         if (lr >= d.n) continue;
-        const int hp = lr / d.gw, wp = lr - hp * d.gw;
+        const int hp = lr / d.gw;
         bf16_t *v = base + (int64_t)lr * ld + part * D + ch * 8;
-        float a[8], b[8];
+        float a[8], b[8], cs[8], sn[8];
         unpack8(*reinterpret_cast<const uint4 *>(v), a);
         unpack8(*reinterpret_cast<const uint4 *>(v + HALF), b);
+        rope_cos_sin8<HD>(cos_t, sin_t, make_int2(hp, lr - hp * d.gw), ch * 8, cs, sn);
         float na[8], nb[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int i = ch * 8 + e;
-            const int j = i < Q4 ? i : i - Q4;
-            const int pos = i < Q4 ? hp : wp;
-            rotate(a[e], b[e], cos_t[pos * Q4 + j], sin_t[pos * Q4 + j], na[e], nb[e]);
-        }
+        for (int e = 0; e < 8; ++e) rotate(a[e], b[e], cs[e], sn[e], na[e], nb[e]);
         if (part == 0) {   // q
             *reinterpret_cast<uint4 *>(v) = pack8(na);
             *reinterpret_cast<uint4 *>(v + HALF) = pack8(nb);
@@ -138,6 +134,38 @@ __global__ __launch_bounds__(256) void rope_kernel(bf16_t *__restrict__ qkv, bf1
     }
 }
 
+// Rotary table dump: row n of out (fp32 [M][hd]) = cos theta_0 .. theta_{hd/2-1} of packed
+// patch n, then sin of the same angles; one thread per (patch, 8 angles).
+template <int HD>
+__global__ __launch_bounds__(256) void rope_dump_kernel(const ImgDesc *__restrict__ imgs, int n_img, int64_t M,
+                                                        const float *__restrict__ cos_t,
+                                                        const float *__restrict__ sin_t, float *__restrict__ out)
+{
+    constexpr int HALF = HD / 2, HC = HALF / 8;
+    const int64_t w = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (w >= M * HC) return;
+    const int64_t row = w / HC;
+    const int i0 = (int)(w - row * HC) * 8;
+    float cs[8], sn[8];
+    rope_cos_sin8<HD>(cos_t, sin_t, patch_grid_pos(imgs, n_img, row), i0, cs, sn);
+    float4 *oc = reinterpret_cast<float4 *>(out + row * HD + i0);
+    float4 *os = reinterpret_cast<float4 *>(out + row * HD + HALF + i0);
+    oc[0] = make_float4(cs[0], cs[1], cs[2], cs[3]);
+    oc[1] = make_float4(cs[4], cs[5], cs[6], cs[7]);
+    os[0] = make_float4(sn[0], sn[1], sn[2], sn[3]);
+    os[1] = make_float4(sn[4], sn[5], sn[6], sn[7]);
+}
+
+template <int HD>
+hipError_t run_rope_dump(const ImgDesc *imgs, int n_img, int64_t M, const float *c, const float *s, float *out,
+                         hipStream_t st)
+{
+    const int64_t threads = M * (HD / 16);
+    hipLaunchKernelGGL(rope_dump_kernel<HD>, dim3((unsigned)ceil_div(threads, 256)), dim3(256), 0, st, imgs, n_img,
+                       M, c, s, out);
+    return hipGetLastError();
+}
+
 template <int HD>
 hipError_t run_rope(bf16_t *qkv, bf16_t *vt, int64_t ldv, const RowTile *tiles, int n_tiles,
                     const ImgDesc *imgs, int D, int H, const float *c, const float *s,
@@ -160,6 +188,19 @@ hipError_t launch_rope(bf16_t *qkv, bf16_t *vt, int64_t ldv, const RowTile *tile
     case 32: return run_rope<32>(qkv, vt, ldv, tiles, n_tiles, imgs, D, H, cos_t, sin_t, s);
     case 64: return run_rope<64>(qkv, vt, ldv, tiles, n_tiles, imgs, D, H, cos_t, sin_t, s);
     case 128: return run_rope<128>(qkv, vt, ldv, tiles, n_tiles, imgs, D, H, cos_t, sin_t, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_dump_rope(const ImgDesc *imgs, int n_img, int64_t M, int hd, const float *cos_t,
+                            const float *sin_t, float *out, hipStream_t s)
+{
+    if (M <= 0) return hipSuccess;
+    switch (hd) {
+    case 16: return run_rope_dump<16>(imgs, n_img, M, cos_t, sin_t, out, s);
+    case 32: return run_rope_dump<32>(imgs, n_img, M, cos_t, sin_t, out, s);
+    case 64: return run_rope_dump<64>(imgs, n_img, M, cos_t, sin_t, out, s);
+    case 128: return run_rope_dump<128>(imgs, n_img, M, cos_t, sin_t, out, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -511,13 +511,17 @@ vit_status encode_impl(vit_ctx *c, const uint8_t *px, const vit_grid *grids, int
             want = (size_t)p.N * D * b2; break;
         case VIT_DUMP_QKV: want = (size_t)p.N * 3 * D * b2; break;
         case VIT_DUMP_MERGED: want = (size_t)p.M * 9 * D * b2; break;
+        case VIT_DUMP_ROPE: want = (size_t)p.N * c->hd * sizeof(float); break;
         default: return fail(c, VIT_E_ARG, "unknown dump boundary");
         }
         if ((stop == VIT_DUMP_QKV || stop == VIT_DUMP_ATTN || stop == VIT_DUMP_LAYER) &&
             (arg < 0 || arg >= L))
             return fail(c, VIT_E_ARG, "layer index out of range");
         if (dst_bytes != want) return fail(c, VIT_E_ARG, "dst_bytes does not match the boundary size");
-        if (p.N > 0 && (!px || !dst)) return fail(c, VIT_E_ARG, "d_pixels or d_dst is NULL");
+        if (p.N > 0 && !dst) return fail(c, VIT_E_ARG, "d_dst is NULL");
+        if (p.N > 0 && stop != VIT_DUMP_ROPE && !px) return fail(c, VIT_E_ARG, "d_pixels is NULL");
+        if (stop == VIT_DUMP_ROPE && ((uintptr_t)dst & 15) != 0)
+            return fail(c, VIT_E_ARG, "d_dst of the RoPE dump must be 16-byte aligned");
     }
     if (p.N == 0) return VIT_OK;
     st = ensure_workspace(c, p.N, p.vt_cols);
@@ -533,6 +537,10 @@ vit_status encode_impl(vit_ctx *c, const uint8_t *px, const vit_grid *grids, int
         return VIT_OK;
     };
 
+    if (stop == VIT_DUMP_ROPE) {
+        LAUNCH(c, launch_dump_rope(dp.imgs, ni, p.N, c->hd, c->d_cos, c->d_sin, (float *)dst, s));
+        return VIT_OK;
+    }
     if (stop == VIT_DUMP_PATCHES) {
         LAUNCH(c, launch_dump_patches(px, dp.imgs, ni, p.N, c->s3, c->t3, c->ps, (bf16_t *)dst, s));
         return VIT_OK;

@@ -69,6 +69,65 @@ def test_identity_patch_projection_bit_exact():
     assert not x0[:, 588:].any()
 
 
+@pytest.mark.parametrize("cfg,grids", [(synth.V41, [(5, 7), (96, 96), (1, 1), (3, 11)]),
+                                       (synth.TINY, [(6, 6), (2, 9)]),
+                                       (replace(synth.V41, heads=8, rope_base=500.0), [(9, 4), (13, 2)])],
+                         ids=["hd64_packed", "hd16", "hd128_base500"])
+def test_rope_dump_matches_oracle_angles(cfg, grids):
+    """[Z] "Step 2" table, the "2D RoPE cos/sin" boundary: the cos and sin of every rotary
+    angle of every patch of a packed batch, read through the device lookup the QKV epilogue
+    rotates with, equal the oracle's angle function bit for bit (both evaluate the angle in
+    double and round once).  The 96x96 image is checked on every row of its first and last
+    grid rows and on 64 sampled rows in between."""
+    torch = require_gpu()
+    c0 = replace(cfg, layers=0, out_hidden=16)
+    enc = vit.Encoder(c0, synth.make_weights(c0))
+    px = synth.make_pixels(c0, grids)
+    got = enc.dump(vit.DUMP_ROPE, torch.from_numpy(px).cuda(), grids).cpu().numpy()
+    torch.cuda.synchronize()
+    hd, half = c0.hidden // c0.heads, c0.hidden // c0.heads // 2
+    assert got.shape == (sum(gh * gw for gh, gw in grids), hd) and got.dtype == np.float32
+    rng = np.random.default_rng(7)
+    off = 0
+    for gh, gw in grids:
+        n = gh * gw
+        rows = np.arange(n)
+        if n > 512:
+            rows = np.unique(np.concatenate([np.arange(gw), np.arange(n - gw, n), rng.integers(0, n, 64)]))
+        for p in rows:
+            h, w = divmod(int(p), gw)
+            want = np.array([oracle.rope_angle(h, w, i, hd, c0.rope_base) for i in range(half)], np.float32)
+            assert np.array_equal(got[off + p, :half], want[:, 0]), (gh, gw, p)
+            assert np.array_equal(got[off + p, half:], want[:, 1]), (gh, gw, p)
+        off += n
+
+
+def test_rope_dump_contract():
+    """The RoPE boundary reads no pixels (NULL accepted), and refuses a destination of the
+    wrong size or one not 16-byte aligned, writing nothing."""
+    import ctypes
+    torch = require_gpu()
+    c0 = replace(synth.V41, layers=0, out_hidden=16)
+    enc = vit.Encoder(c0, synth.make_weights(c0))
+    grids = [(4, 5), (2, 3)]
+    buf = torch.full((26 * 64 + 4,), 7.0, dtype=torch.float32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def call(dst, nbytes):
+        return vit.lib().vit_dump(enc._ctx, vit.DUMP_ROPE, 0, None, vit.grid_array(grids), len(grids),
+                                  ctypes.c_void_p(dst), nbytes, stream)
+    assert call(buf.data_ptr(), 26 * 64 * 4) == vit.VIT_OK
+    torch.cuda.synchronize()
+    ref = buf[:26 * 64].clone()
+    assert not torch.equal(ref, torch.full_like(ref, 7.0))
+    buf.fill_(7.0)
+    torch.cuda.synchronize()
+    assert call(buf.data_ptr() + 4, 26 * 64 * 4) == vit.VIT_E_ARG          # misaligned
+    assert call(buf.data_ptr(), 26 * 64 * 4 - 4) == vit.VIT_E_ARG          # wrong size
+    torch.cuda.synchronize()
+    assert torch.equal(buf, torch.full_like(buf, 7.0))
+
+
 @pytest.mark.parametrize("base,grids", [(synth.TINY, [(5, 7), (6, 6), (1, 2)]),
                                         (synth.V41, [(5, 7), (96, 96), (4, 9), (1, 2)])],
                          ids=["d64", "d1024_96x96"])

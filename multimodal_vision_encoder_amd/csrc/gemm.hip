@@ -1,36 +1,30 @@
-// Patchify and the patch projection, plus the debug materialisation of fused-only tensors.
-//
-// The patch projection writes the normalised bf16 patch matrix once ([Z] "Step 1": rows in
-// (grid_y, grid_x) order, columns (channel, y, x); columns past 3*ps*ps zero up to the padded
-// K of the projection weight, [Z] "Step 5") and runs the large-tile GEMM of gemm_big.hip on
-// it.  The matrix is ~12 MB at the 1024-token image; computing it inside the GEMM's A loader
-// would cost the direct global -> LDS copies that the GEMM depends on.
+// Debug materialisation of the tensors that exist only inside fused loaders: the patch
+// matrix (patchify runs inside the patch projection's A loader, SrcPatch) and the merged
+// projector input (the 3x3 gather inside the projector's A loader, SrcMerge).  Both go
+// through the loaders' own device functions, so a dump is exactly what the GEMM consumed.
 #include "kernels.h"
 #include "loaders.h"
 
 namespace {
 
-// One thread per 16-byte chunk (8 values) of the patch matrix [M][pitch].
-__global__ __launch_bounds__(256) void patchify_kernel(LoadPatch al, bf16_t *out, int pitch)
+// One thread per (patch, 8-column chunk of the loader's K order); the valid values are
+// written at their (channel, y, x) column c ps^2 + y ps + x ([Z] "Step 1").
+__global__ __launch_bounds__(256) void dump_patches_kernel(SrcPatch src, int kchunks, bf16_t *out)
 {
-    const int chunks = pitch / 8;
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= al.M * chunks) return;
-    const int64_t row = idx / chunks;
-    const int k = (int)(idx - row * chunks) * 8;
-    *reinterpret_cast<uint4 *>(out + row * pitch + k) = al(row, k);
-}
-
-__global__ __launch_bounds__(256) void dump_patches_kernel(LoadPatch al, bf16_t *out)
-{
-    const int64_t row = blockIdx.x;
-    for (int k = threadIdx.x * 8; k < al.cols; k += 256 * 8) {
-        const uint4 v = al(row, k);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    const int64_t w = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (w >= src.M * kchunks) return;
+    const int64_t row = w / kchunks;
+    const int k = (int)(w - row * kchunks) * 8;
+    const SrcPatch::Row rw = src.row(row);
+    const SrcPatch::KChunk kc = src.chunk(k, src.consts());
+    const uint4 v = src.convert(kc, src.load(rw, kc));
+    const uint32_t h[4] = {v.x, v.y, v.z, v.w};
+    const int ps = src.ps, pp = ps * ps;
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (k + j < al.cols)
-                out[row * al.cols + k + j] = (bf16_t)((w[j >> 1] >> ((j & 1) * 16)) & 0xFFFFu);
+    for (int e = 0; e < 8; ++e) {
+        if (e >= kc.nv) break;
+        const int b = kc.b0 + e, x = b / 3, c = b - 3 * x;
+        out[(src.m_base + row) * 3 * pp + c * pp + kc.yc * ps + x] = (bf16_t)((h[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
     }
 }
 
@@ -50,37 +44,18 @@ __global__ __launch_bounds__(256) void dump_merged_kernel(SrcMerge src, bf16_t *
     }
 }
 
-LoadPatch patch_loader(const uint8_t *px, const ImgDesc *imgs, int n_img, int64_t M,
-                       const float *s3, const float *t3, int ps)
-{
-    return LoadPatch{px, imgs, n_img, M, ps, 3 * ps * ps, s3[0], s3[1], s3[2], t3[0], t3[1], t3[2]};
-}
-
 }  // namespace
 
-hipError_t launch_patch_embed(const uint8_t *px, const ImgDesc *imgs, int n_img, int64_t M,
-                              const float *s3, const float *t3, int ps, const bf16_t *Wpe,
-                              int Kp, const bf16_t *bias, int D, bf16_t *patches, bf16_t *out,
-                              const GemmWorkspace *ws, hipStream_t s)
+hipError_t launch_dump_patches(const uint8_t *lpx, int64_t pix_first, int64_t pix_bytes, const ImgDesc *imgs,
+                               int n_img, int64_t m_first, int64_t M, const float *s3, const float *t3, int ps,
+                               bf16_t *out, hipStream_t s)
 {
     if (M <= 0) return hipSuccess;
-    if (Kp % 8 != 0 || Kp < 3 * ps * ps) return hipErrorInvalidValue;
-    const LoadPatch al = patch_loader(px, imgs, n_img, M, s3, t3, ps);
-    const int64_t threads = M * (Kp / 8);
-    hipLaunchKernelGGL(patchify_kernel, dim3((unsigned)ceil_div(threads, 256)), dim3(256), 0, s, al,
-                       patches, Kp);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return launch_linear(patches, M, Kp, Wpe, bias, D, ACT_NONE, false, out, ws, s);
-}
-
-hipError_t launch_dump_patches(const uint8_t *px, const ImgDesc *imgs, int n_img, int64_t M,
-                               const float *s3, const float *t3, int ps, bf16_t *out,
-                               hipStream_t s)
-{
-    if (M <= 0) return hipSuccess;
-    const LoadPatch al = patch_loader(px, imgs, n_img, M, s3, t3, ps);
-    hipLaunchKernelGGL(dump_patches_kernel, dim3((unsigned)M), dim3(256), 0, s, al, out);
+    if (ps > 64 || pix_bytes <= 0 || pix_bytes >= kPatchLaunchBytes) return hipErrorInvalidValue;
+    const int kchunks = patch_gemm_k(ps) / 8;
+    const int64_t threads = M * kchunks;
+    hipLaunchKernelGGL(dump_patches_kernel, dim3((unsigned)ceil_div(threads, 256)), dim3(256), 0, s,
+                       patch_source(lpx, pix_first, pix_bytes, imgs, n_img, m_first, M, s3, t3, ps), kchunks, out);
     return hipGetLastError();
 }
 

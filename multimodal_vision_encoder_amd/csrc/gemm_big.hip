@@ -31,7 +31,11 @@
 //
 // The A rows come from an address source: plain row-major activations, or the 3x3 merge
 // gather of the projector ([Z] "Step 4"), where positions in the right/bottom zero padding
-// read from a zero page.  Rows past M are clamped to row M-1 and never stored.
+// read from a zero page.  Rows past M are clamped to row M-1 and never stored.  The patch
+// projection's A comes from the pixels themselves (patchify fused into the loader): group 0
+// copies the raw bytes of k-tile t+NS+2 global -> LDS in the step of k-tile t, and two steps
+// later converts them to bf16 and writes them into their stage with ds_write (the bytes need
+// arithmetic on the way, so the stage cannot be filled by the copies themselves).
 #include <type_traits>
 
 #include "kernels.h"
@@ -83,12 +87,33 @@ __device__ __forceinline__ void copy16(const void *g, uint32_t lds)
                      ::"v"(g), "s"(lds) : "memory", "m0");
 }
 
+// 12-byte global -> LDS copy of base + off (base wave-uniform, off per lane, 4-byte aligned);
+// lane l writes LDS bytes lds + 16 l .. lds + 16 l + 11 (the lanes keep a 16-byte pitch, as
+// measured; the 4 bytes after each are left as they were).
+__device__ __forceinline__ void copy12(const void *base, uint32_t off, uint32_t lds)
+{
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    const uint64_t ub = ((uint64_t)hi << 32) | (uint64_t)lo;
+    __asm__ volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx3 %0, %1"
+                     ::"v"(off), "s"(ub), "s"(lds) : "memory", "m0");
+}
+
 // s_waitcnt vmcnt(N) lgkmcnt(0): all but this wave's newest N global loads done, LDS reads done.
 template <int N>
 __device__ __forceinline__ void wait_vmem_n()
 {
     static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
     __builtin_amdgcn_s_waitcnt(0x0070 | (N & 15) | ((N >> 4) << 14));
+}
+
+// s_waitcnt vmcnt(N): all but this wave's newest N global loads done (LDS operations not waited for).
+template <int N>
+__device__ __forceinline__ void wait_vm_only()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
 __device__ __forceinline__ void bare_barrier() { __asm__ volatile("s_barrier" ::: "memory"); }
@@ -487,7 +512,11 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(SRC src, const bf16_t 
     constexpr bool PSTAGED = BM * PPITCH <= 160 * 1024;
     constexpr int SMEM0 = (STAGED && BM * PITCH > NS * STAGE) ? BM * PITCH : NS * STAGE;
     constexpr int SMEM1 = (PSTAGED && BM * PPITCH > SMEM0) ? BM * PPITCH : SMEM0;
-    constexpr int SMEM = EpiExtra<EP>::template bytes<BM, PITCH>() > SMEM1 ? EpiExtra<EP>::template bytes<BM, PITCH>() : SMEM1;
+    constexpr int SMEM2 = EpiExtra<EP>::template bytes<BM, PITCH>() > SMEM1 ? EpiExtra<EP>::template bytes<BM, PITCH>() : SMEM1;
+    // pixel A: two raw k-tiles (a 16-byte slot per chunk, BM * CPR chunks) after the ring, free
+    // again before the epilogue stages its tile
+    constexpr int RAWB = BM * CPR * 16;
+    constexpr int SMEM = SRC::REG && NS * STAGE + 2 * RAWB > SMEM2 ? NS * STAGE + 2 * RAWB : SMEM2;
     __shared__ __attribute__((aligned(1024))) char smem[SMEM];
     auto stage = [&](auto st) -> char * { return smem + decltype(st)::value * STAGE; };
     auto stage_lds = [&](auto st) -> uint32_t {
@@ -525,17 +554,31 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(SRC src, const bf16_t 
 
     // group 0 copies the A tile, group 1 the W tile; chunk c = (i*4 + w4)*64 + lane of a tile
     // holds row c / CPR, logical chunk (c % CPR) ^ swz(row)
+    // Register-staged A (pixel sources): both groups convert, group g the chunks
+    // i = g AH .. g AH + AH - 1 (AH = AL / 2) of the same layout, and group 1 still copies W.
+    constexpr int AH = SRC::REG ? AL / 2 : AL;
+    static_assert(!SRC::REG || AL % 2 == 0, "the pixel chunks split evenly between the groups");
     typename SRC::Row arow[AL];
     int aslot[AL];
     const bf16_t *wptr[BL];
-    if (grp == 0) {
+    if constexpr (SRC::REG) {
 #pragma unroll
-        for (int i = 0; i < AL; ++i) {
-            const int c = (i * 4 + w4) * 64 + lane, r = c / CPR;
-            arow[i] = src.row(m0 + r);
-            aslot[i] = ((c % CPR) ^ swz(r)) * 8;
+        for (int h = 0; h < AH; ++h) {
+            const int i = grp * AH + h, c = (i * 4 + w4) * 64 + lane, r = c / CPR;
+            arow[h] = src.row(m0 + r);
         }
-    } else {
+    }
+    if (grp == 0) {
+        if constexpr (!SRC::REG) {
+#pragma unroll
+            for (int i = 0; i < AL; ++i) {
+                const int c = (i * 4 + w4) * 64 + lane, r = c / CPR;
+                arow[i] = src.row(m0 + r);
+                aslot[i] = ((c % CPR) ^ swz(r)) * 8;
+            }
+        }
+    }
+    if (grp == 1) {
 #pragma unroll
         for (int i = 0; i < BL; ++i) {
             const int c = (i * 4 + w4) * 64 + lane, r = c / CPR;
@@ -543,21 +586,74 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(SRC src, const bf16_t 
             wptr[i] = W + (int64_t)n * K + ((c % CPR) ^ swz(r)) * 8;
         }
     }
-    auto issue = [&](int kt, auto st) {
+    // The 12 raw bytes of each chunk of k-tile j go global -> LDS into raw slot j % 2 (each lane
+    // reads back only what its own copy wrote, so no barrier), are converted two steps later
+    // and written into their stage.  The thread's chunk of every row it fills is logical chunk alj; ash keeps
+    // each chunk's first byte inside its dwords.
+    uint32_t ash[2][SRC::REG ? AH : 1];
+    constexpr int PL = AH;   // raw copies per k-tile of a thread (one 12-byte copy per chunk)
+    const int alj = (lane & 3) ^ ((lane >> 4) & 3);
+    typename SRC::Consts acs{};
+    if constexpr (SRC::REG) acs = src.consts();
+    // raw slot b: chunk i (0 .. AL-1) of wave w4 at (i * 4 + w4) * 1024 + 16 lane
+    auto raw_at = [&](int b, int i) -> char * { return smem + NS * STAGE + b * RAWB + (i * 4 + w4) * 1024; };
+    auto load_a = [&](int kt, auto buf) __attribute__((always_inline)) {
+        if constexpr (SRC::REG) {
+            constexpr int B = decltype(buf)::value;
+            const auto kc = src.chunk((kt0 + kt) * BK + 8 * alj, acs);
+#pragma unroll
+            for (int h = 0; h < AH; ++h) {
+                const auto a = src.addr(arow[h], kc);
+                ash[B][h] = a.sh;
+                copy12(src.px, a.o, (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)raw_at(B, grp * AH + h));
+            }
+        }
+    };
+    auto put_a = [&](int kt, auto st, auto buf) __attribute__((always_inline)) {
+        if constexpr (SRC::REG) {
+            constexpr int B = decltype(buf)::value;
+            const auto kc = src.chunk((kt0 + kt) * BK + 8 * alj, acs);
+#pragma unroll
+            for (int h = 0; h < AH; ++h) {
+                const int i = grp * AH + h;
+                const uint3 r3 = *reinterpret_cast<const uint3 *>(raw_at(B, i) + lane * 16);
+                const RawChunk d{r3.x, r3.y, r3.z, ash[B][h]};
+                *reinterpret_cast<uint4 *>(stage(st) + (i * 4 + w4) * 1024 + lane * 16) = src.convert(kc, d);
+            }
+        }
+    };
+    auto issue = [&](int kt, auto st) __attribute__((always_inline)) {
         const int k0 = (kt0 + kt) * BK;
         if (grp == 0) {
+            if constexpr (!SRC::REG) {
 #pragma unroll
-            for (int i = 0; i < AL; ++i)
-                copy16(src.addr(arow[i], k0 + aslot[i]), stage_lds(st) + (i * 4 + w4) * 1024);
+                for (int i = 0; i < AL; ++i)
+                    copy16(src.addr(arow[i], k0 + aslot[i]), stage_lds(st) + (i * 4 + w4) * 1024);
+            }
         } else {
 #pragma unroll
             for (int i = 0; i < BL; ++i) copy16(wptr[i] + k0, stage_lds(st) + A_BYTES + (i * 4 + w4) * 1024);
         }
     };
-    // this wave's copies of all but the newest NS-2 k-tiles landed, and its LDS reads done
+    // this wave's copies of all but the newest NS-2 k-tiles landed, and its LDS reads and writes
+    // done.  Register-staged A: a step issues the raw copies of k-tile t+NS+2 and then (group 1)
+    // the W copies of k-tile t+NS, so the newest two of each may stay in flight.
+    static_assert(NS % 2 == 0 && NS - 2 == 2, "the raw A slots alternate with the stage parity");
     auto wait_ring = [&]() {
-        if (grp == 0) wait_vmem_n<(NS - 2) * AL>();
-        else wait_vmem_n<(NS - 2) * BL>();
+        if (grp == 0) {
+            if constexpr (SRC::REG) wait_vmem_n<2 * PL>();
+            else wait_vmem_n<(NS - 2) * AL>();
+        } else {
+            if constexpr (SRC::REG) wait_vmem_n<2 * PL + 2 * BL>();
+            else wait_vmem_n<(NS - 2) * BL>();
+        }
+    };
+    // before converting raw k-tile t+NS (copied two steps ago): only the raw copies of k-tile
+    // t+NS+1 and (group 1) the W copies of the two steps since may still be in flight
+    auto wait_raw = [&]() {
+        if (grp == 0) wait_vm_only<PL>();
+        else wait_vm_only<PL + 2 * BL>();
+        __asm__ volatile("" ::: "memory");   // the raw reads stay below the wait
     };
     // instructions stay on their side of a barrier (the MFMAs especially)
     auto sync = [&]() {
@@ -575,7 +671,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(SRC src, const bf16_t 
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     bf16x8_t fa[BK / 16][TM], fb[BK / 16][TN];
-    auto ldfrag = [&](auto st) {
+    auto ldfrag = [&](auto st) __attribute__((always_inline)) {
         const char *sa = stage(st), *sb = sa + A_BYTES;
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
@@ -591,7 +687,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(SRC src, const bf16_t 
             }
         }
     };
-    auto mma = [&]() {
+    auto mma = [&]() __attribute__((always_inline)) {
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks)
@@ -608,28 +704,64 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(SRC src, const bf16_t 
     using I0 = std::integral_constant<int, 0>;
     constexpr auto stages = std::make_integer_sequence<int, NS>{};
     each_stage(stages, [&](auto st) { issue(min((int)decltype(st)::value, nk - 1), st); });
-    if (grp == 0) wait_vmem_n<(NS - 1) * AL>();
-    else wait_vmem_n<(NS - 1) * BL>();
+    if constexpr (SRC::REG) {
+        // stages 0 .. NS-1 converted with two raw k-tiles in flight (each wait also covers the
+        // W copies above); leaves raw k-tiles NS, NS+1 in flight
+        using B0 = std::integral_constant<int, 0>;
+        using B1 = std::integral_constant<int, 1>;
+        load_a(0, B0{});
+        load_a(min(1, nk - 1), B1{});
+        each_stage(stages, [&](auto st) {
+            using B = std::integral_constant<int, decltype(st)::value % 2>;
+            wait_vm_only<PL>();
+            __asm__ volatile("" ::: "memory");   // the raw reads stay below the wait
+            put_a(min((int)decltype(st)::value, nk - 1), st, B{});
+            load_a(min((int)decltype(st)::value + 2, nk - 1), B{});
+        });
+        __asm__ volatile("" ::: "memory");   // the stage writes stay above the wait below
+        wait_vmem_n<2 * PL>();
+    } else {
+        if (grp == 0) wait_vmem_n<(NS - 1) * AL>();
+        else wait_vmem_n<(NS - 1) * BL>();
+    }
     sync();
     ldfrag(I0{});
     if (grp == 1) {   // group 1 runs one phase behind
         wait_ring();
         sync();
     }
-    auto step = [&](int t, auto st) {
+    auto step = [&](int t, auto st) __attribute__((always_inline)) {
         constexpr int S = decltype(st)::value;
         mma();
         wait_ring();
         sync();
         if (t + 1 < nk) ldfrag(std::integral_constant<int, (S + 1) % NS>{});
+        if constexpr (SRC::REG) {   // raw k-tile t+NS (copied two steps ago) into stage S; copy t+NS+2
+            using B = std::integral_constant<int, S % 2>;
+            wait_raw();
+            put_a(min(t + NS, nk - 1), std::integral_constant<int, S>{}, B{});
+            load_a(min(t + NS + 2, nk - 1), B{});
+        }
         issue(min(t + NS, nk - 1), std::integral_constant<int, S>{});
+        if constexpr (SRC::REG) __asm__ volatile("" ::: "memory");   // the stage writes stay above wait_ring
         wait_ring();
         sync();
     };
-    for (int kt = 0; kt < nk; kt += NS)
+    if constexpr (SRC::REG) {
+        // whole groups of NS steps first: with no skipped step inside the loop body, the
+        // compiler's count of the raw loads still in flight stays exact (its waits before the
+        // conversions then leave the newest raw k-tile loading)
+        int kt = 0;
+        for (; kt + NS <= nk; kt += NS) each_stage(stages, [&](auto st) { step(kt + decltype(st)::value, st); });
         each_stage(stages, [&](auto st) {
             if (kt + decltype(st)::value < nk) step(kt + decltype(st)::value, st);
         });
+    } else {
+        for (int kt = 0; kt < nk; kt += NS)
+            each_stage(stages, [&](auto st) {
+                if (kt + decltype(st)::value < nk) step(kt + decltype(st)::value, st);
+            });
+    }
     if (grp == 0) sync();   // same barrier count as group 1
     wait_vmem_n<0>();       // the trailing copies of the last k-tile
     sync();
@@ -864,6 +996,13 @@ template <int ACT>
 EpiBF16<ACT> rows_from(const EpiBF16<ACT> &e, int64_t m0) { return EpiBF16<ACT>{e.out + m0 * e.N, e.bias, e.M - m0, e.N}; }
 EpiF32 rows_from(const EpiF32 &e, int64_t m0) { return EpiF32{e.out + m0 * e.N, e.bias, e.M - m0, e.N}; }
 EpiSwiGLU rows_from(const EpiSwiGLU &e, int64_t m0) { return EpiSwiGLU{e.out + m0 * (e.N / 2), e.bias, e.M - m0, e.N}; }
+SrcPatch rows_from(const SrcPatch &s, int64_t m0)
+{
+    SrcPatch r = s;
+    r.m_base += m0;
+    r.M -= m0;
+    return r;
+}
 
 // Row tail of a multi-round launch (one block per CU): when the tiles of the last, partial
 // round are whole rows of tiles, those rows run afterwards as 128 x 128 tiles, four times as
@@ -883,8 +1022,8 @@ int64_t row_tail_start(int64_t M, int N, int BM, int BN)
 
 // A launch with BM x BN tiles, its partial last round of whole tile rows (if any) moved to a
 // second launch of 128 x 128 tiles.  Launches that use the split-K tail keep it instead.
-template <int BM, int BN, class EP>
-hipError_t run_rows(SrcPlain src, const bf16_t *W, int64_t M, int N, int K, EP ep, const GemmWorkspace *ws,
+template <int BM, int BN, class SRC, class EP>
+hipError_t run_rows(SRC src, const bf16_t *W, int64_t M, int N, int K, EP ep, const GemmWorkspace *ws,
                     hipStream_t s)
 {
     const int64_t m_tail = plan_split(M, N, K, BM, BN, ws != nullptr).splits > 1 ? M : row_tail_start(M, N, BM, BN);
@@ -973,6 +1112,22 @@ hipError_t launch_linear(const bf16_t *A, int64_t M, int K, const bf16_t *W, con
                          int N, int act, bool out_f32, void *out, const GemmWorkspace *ws, hipStream_t s)
 {
     return dispatch(SrcPlain{A, K, M}, W, M, N, K, bias, act, out_f32, out, ws, s);
+}
+
+hipError_t launch_patch_embed(const uint8_t *lpx, int64_t pix_first, int64_t pix_bytes, const ImgDesc *imgs,
+                              int n_img, int64_t m_first, int64_t M, const float *s3, const float *t3, int ps,
+                              const bf16_t *Wpe, int Kp, const bf16_t *bias, int D, bf16_t *out,
+                              const GemmWorkspace *ws, hipStream_t s)
+{
+    if (M <= 0) return hipSuccess;
+    if (Kp != patch_gemm_k(ps) || ps > 64 || pix_bytes <= 0 || pix_bytes >= kPatchLaunchBytes)
+        return hipErrorInvalidValue;
+    const SrcPatch src = patch_source(lpx, pix_first, pix_bytes, imgs, n_img, m_first, M, s3, t3, ps);
+    const EpiBF16<ACT_NONE> ep{out + m_first * D, bias, M, D};
+    // The pixel conversion costs VALU work per A element, the MFMA work per A element grows
+    // with BN: 256 x 256 tiles whenever they give a quarter of a round of blocks.
+    if (ceil_div(M, 256) * ceil_div(D, 256) * 4 >= cu_count()) return run_rows<256, 256>(src, Wpe, M, D, Kp, ep, ws, s);
+    return run_rows<128, 128>(src, Wpe, M, D, Kp, ep, ws, s);
 }
 
 template <int HD>

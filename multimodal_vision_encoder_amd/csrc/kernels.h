@@ -28,11 +28,15 @@ hipError_t launch_linear(const bf16_t *A, int64_t M, int K, const bf16_t *W, con
                          int N, int act, bool out_f32, void *out, const GemmWorkspace *ws,
                          hipStream_t s);
 
-// Patchify + patch projection: x0 = bf16(P W_pe^T + b), W_pe zero-padded to Kp columns
-// (Kp % 32 == 0); `patches` is bf16 scratch [M][Kp] for the patch matrix.
-hipError_t launch_patch_embed(const uint8_t *px, const ImgDesc *imgs, int n_img, int64_t M,
-                              const float *s3, const float *t3, int ps, const bf16_t *Wpe,
-                              int Kp, const bf16_t *bias, int D, bf16_t *patches, bf16_t *out,
+// Patchify fused into the patch projection: x0 = bf16(P W_pe^T + b) for patch rows
+// [m_first, m_first + M) (out is the whole [N][D] output), the patch matrix P computed from
+// the pixels inside the GEMM's A loader.  Those rows' images hold the pix_bytes (< 2^31) bytes
+// at lpx, the first at offset pix_first of the batch's pixels (fewer than 12 bytes plus the
+// misalignment of lpx: lpx must have 16 readable bytes); Wpe holds the projection weight in
+// the loader's K order (SrcPatch in loaders.h), Kp = patch_gemm_k(ps).
+hipError_t launch_patch_embed(const uint8_t *lpx, int64_t pix_first, int64_t pix_bytes, const ImgDesc *imgs,
+                              int n_img, int64_t m_first, int64_t M, const float *s3, const float *t3, int ps,
+                              const bf16_t *Wpe, int Kp, const bf16_t *bias, int D, bf16_t *out,
                               const GemmWorkspace *ws, hipStream_t s);
 
 // 3x3 merge gather + projector: out [Mtok][Dl], fp32 or bf16 after `act`; Wp position-major
@@ -100,9 +104,11 @@ hipError_t launch_overlay(uint16_t *embeds, const float *src, const int32_t *row
                           int hidden, hipStream_t s);
 
 // Debug materialisation of fused-only tensors through the GEMM loaders.
-hipError_t launch_dump_patches(const uint8_t *px, const ImgDesc *imgs, int n_img, int64_t M,
-                               const float *s3, const float *t3, int ps, bf16_t *out,
-                               hipStream_t s);
+// Patch matrix rows [m_first, m_first + M) in the pages' (channel, y, x) column order, through
+// the patch projection's own loader (arguments as launch_patch_embed; out is [N][3 ps^2]).
+hipError_t launch_dump_patches(const uint8_t *lpx, int64_t pix_first, int64_t pix_bytes, const ImgDesc *imgs,
+                               int n_img, int64_t m_first, int64_t M, const float *s3, const float *t3, int ps,
+                               bf16_t *out, hipStream_t s);
 hipError_t launch_dump_merged(const bf16_t *y, const ImgDesc *imgs, int n_img, int64_t Mtok,
                               int D, bf16_t *out, const bf16_t *zero, hipStream_t s);
 // Rotary angles of every packed patch as the RoPE rotations read them: out fp32 [M][hd] =

@@ -10,6 +10,7 @@
 #include <vector>
 
 #include "kernels.h"
+#include "loaders.h"
 #include "vit.h"
 #include "vit_ops.h"
 
@@ -66,6 +67,7 @@ struct Plan {
     std::vector<ImgDesc> imgs;
     std::vector<RowTile> attn, rope;
     int64_t N = 0, M = 0, vt_cols = 0;
+    int64_t npx = 0;   // pixel bytes of the batch
 };
 
 }  // namespace
@@ -83,6 +85,7 @@ struct vit_ctx {
     bf16_t *a1 = nullptr;              // aligner inner activations, bf16 [cap_tokens][Da]
     int64_t cap_tokens = 0;
     bf16_t *d_zero = nullptr;   // 256 zero bytes: the padding source of the merge gather
+    uint8_t *d_tinypx = nullptr; // 64 bytes: padded copy of a batch of fewer than 12 pixel bytes
     uint16_t *d_sentinels = nullptr;   // learned START, NEWLINE, END rows, bf16 [3][Dl]
     float *d_pre_ws = nullptr;         // preprocessing scratch (horizontal resize pass)
     size_t pre_ws_bytes = 0;
@@ -99,7 +102,7 @@ struct vit_ctx {
     int span_layout = VIT_SPAN_V41;   // span geometry of vit_assemble
     int64_t cap_patches = 0, cap_vt_cols = 0, reserve_cap = 0;
     bf16_t *x = nullptr, *ln = nullptr, *qkv = nullptr, *vt = nullptr, *o = nullptr,
-           *delta = nullptr, *h1 = nullptr, *patches = nullptr;
+           *delta = nullptr, *h1 = nullptr;
 
     // per-call metadata: pinned staging -> device
     char *h_stage = nullptr, *d_meta = nullptr;
@@ -250,6 +253,7 @@ vit_status make_plan(vit_ctx *ctx, const vit_grid *grids, int n, Plan &p)
         pix += (int64_t)ctx->ps * gh * ctx->ps * gw * 3;
         if (p.vt_cols > INT32_MAX / 2) return fail(ctx, VIT_E_ARG, "batch too large");
     }
+    p.npx = pix;
     // attention query tiles, largest images first (longest-processing-time order)
     std::vector<int> order(n);
     for (int i = 0; i < n; ++i) order[i] = i;
@@ -265,7 +269,7 @@ vit_status make_plan(vit_ctx *ctx, const vit_grid *grids, int n, Plan &p)
 
 void free_workspace(vit_ctx *c)
 {
-    bf16_t **bufs[] = {&c->x, &c->ln, &c->qkv, &c->vt, &c->o, &c->delta, &c->h1, &c->patches};
+    bf16_t **bufs[] = {&c->x, &c->ln, &c->qkv, &c->vt, &c->o, &c->delta, &c->h1};
     for (auto b : bufs) {
         if (*b) (void)hipFree(*b);
         *b = nullptr;
@@ -338,8 +342,7 @@ vit_status ensure_workspace(vit_ctx *c, int64_t N, int64_t vt_cols)
     const size_t D = c->D;
     struct { bf16_t **p; size_t n; } req[] = {
         {&c->x, Np * D}, {&c->ln, Np * D}, {&c->qkv, Np * 3 * D}, {&c->o, Np * D},
-        {&c->delta, Np * D}, {&c->h1, Np * (size_t)c->F}, {&c->vt, (size_t)c->H * c->hd * Vc},
-        {&c->patches, Np * (size_t)c->Kp}};
+        {&c->delta, Np * D}, {&c->h1, Np * (size_t)c->F}, {&c->vt, (size_t)c->H * c->hd * Vc}};
     for (auto &r : req) {
         if (hipMalloc((void **)r.p, r.n * sizeof(bf16_t)) != hipSuccess) {
             (void)hipGetLastError();
@@ -541,12 +544,43 @@ vit_status encode_impl(vit_ctx *c, const uint8_t *px, const vit_grid *grids, int
         LAUNCH(c, launch_dump_rope(dp.imgs, ni, p.N, c->hd, c->d_cos, c->d_sin, (float *)dst, s));
         return VIT_OK;
     }
-    if (stop == VIT_DUMP_PATCHES) {
-        LAUNCH(c, launch_dump_patches(px, dp.imgs, ni, p.N, c->s3, c->t3, c->ps, (bf16_t *)dst, s));
+    // The fused patch loader addresses under 2^31 pixel bytes per launch: whole images in
+    // groups.  It reads 12 bytes per chunk, so a group of fewer than 12 pixel bytes (plus the
+    // misalignment of its start) is read from a padded 64-byte copy.
+    auto pixel_groups = [&](auto &&fn) -> vit_status {
+        for (int i0 = 0; i0 < ni;) {
+            int i1 = i0 + 1;
+            const int64_t first = p.imgs[i0].pix_off;
+            auto end_of = [&](int i) { return i + 1 < ni ? p.imgs[i + 1].pix_off : p.npx; };
+            while (i1 < ni && end_of(i1) - first < kPatchLaunchBytes) ++i1;
+            const int64_t m0 = p.imgs[i0].patch_off, m1 = i1 < ni ? p.imgs[i1].patch_off : p.N;
+            const int64_t bytes = end_of(i1 - 1) - first;
+            const uint8_t *lpx = px + first;
+            if (bytes + (int64_t)((uintptr_t)lpx & 3) < 12) {
+                HIP_TRY(c, hipMemcpyAsync(c->d_tinypx, lpx, (size_t)bytes, hipMemcpyDeviceToDevice, s));
+                lpx = c->d_tinypx;
+            }
+            const vit_status st2 = fn(lpx, first, bytes, m0, m1 - m0);
+            if (st2 != VIT_OK) return st2;
+            i0 = i1;
+        }
         return VIT_OK;
+    };
+    if (stop == VIT_DUMP_PATCHES)
+        return pixel_groups([&](const uint8_t *lpx, int64_t pf, int64_t pb, int64_t m0, int64_t rows) -> vit_status {
+            LAUNCH(c, launch_dump_patches(lpx, pf, pb, dp.imgs, ni, m0, rows, c->s3, c->t3, c->ps, (bf16_t *)dst, s));
+            return VIT_OK;
+        });
+    {
+        const long t_ = timing_start(c, s);
+        st = pixel_groups([&](const uint8_t *lpx, int64_t pf, int64_t pb, int64_t m0, int64_t rows) -> vit_status {
+            LAUNCH(c, launch_patch_embed(lpx, pf, pb, dp.imgs, ni, m0, rows, c->s3, c->t3, c->ps, c->d_wpe, c->Kp,
+                                         c->pe_b, D, c->x, &gws, s));
+            return VIT_OK;
+        });
+        if (st != VIT_OK) return st;
+        timing_stop(c, s, VIT_STEP_PATCH_EMBED, t_);
     }
-    TLAUNCH(c, VIT_STEP_PATCH_EMBED, s, launch_patch_embed(px, dp.imgs, ni, p.N, c->s3, c->t3, c->ps, c->d_wpe, c->Kp,
-                                 c->pe_b, D, c->patches, c->x, &gws, s));
     if (stop == VIT_DUMP_EMBED) return copy_out(c->x);
 
     // the transposed-V columns past each image's end are read as masked keys: zero them once
@@ -597,7 +631,7 @@ void destroy(vit_ctx *c)
     if (!c) return;
     (void)hipDeviceSynchronize();
     free_workspace(c);
-    void *bufs[] = {c->d_blob, c->d_wpe, c->d_wproj, c->d_cos, c->d_sin, c->d_meta, c->d_zero, c->d_gemm_ws,
+    void *bufs[] = {c->d_blob, c->d_wpe, c->d_wproj, c->d_cos, c->d_sin, c->d_meta, c->d_zero, c->d_tinypx, c->d_gemm_ws,
                     c->d_attn_ws, c->d_sentinels, c->d_pre_ws, c->d_gu, c->a1};
     for (void *b : bufs)
         if (b) (void)hipFree(b);
@@ -642,7 +676,7 @@ vit_status vit_create(const vit_weights *w, vit_ctx **out)
     c->L = w->cfg.layers;
     c->ps = w->cfg.patch;
     const int P = 3 * c->ps * c->ps;
-    c->Kp = (int)ceil_div(P, 64) * 64;
+    c->Kp = patch_gemm_k(c->ps);
     for (int i = 0; i < 3; ++i) {
         const double sd = (double)w->cfg.pix_std[i], mu = (double)w->cfg.pix_mean[i];
         c->s3[i] = (float)(1.0 / (255.0 * sd));
@@ -674,6 +708,8 @@ vit_status vit_create(const vit_weights *w, vit_ctx **out)
     CREATE_HIP(hipEventCreateWithFlags(&c->stage_ev, hipEventDisableTiming));
     CREATE_HIP(hipMalloc((void **)&c->d_zero, 256));
     CREATE_HIP(hipMemset(c->d_zero, 0, 256));
+    CREATE_HIP(hipMalloc((void **)&c->d_tinypx, 64));
+    CREATE_HIP(hipMemset(c->d_tinypx, 0, 64));
     CREATE_HIP(hipMalloc((void **)&c->d_blob, want * sizeof(bf16_t)));
     CREATE_HIP(hipMemcpy(c->d_blob, w->blob, want * sizeof(bf16_t), hipMemcpyHostToDevice));
 
@@ -742,11 +778,18 @@ vit_status vit_create(const vit_weights *w, vit_ctx **out)
         }
     }
 
-    // patch projection weight zero-padded to Kp columns ([Z] "Step 5")
+    // patch projection weight in the fused loader's K order: column (c, y, x) of the pages'
+    // patch vector ([Z] "Step 1") moves to y * RP + 3 x + c (the pixel bytes of patch row y as
+    // the image stores them, each row padded to RP columns); every other column is zero
+    // ([Z] "Step 5": zero padding leaves the product unchanged)
     {
+        const int ps = c->ps, rp = patch_segment_cols(ps);
         std::vector<uint16_t> pad(D * c->Kp, 0);
         for (size_t r = 0; r < D; ++r)
-            std::memcpy(&pad[r * c->Kp], hb + o_wpe + r * P, P * sizeof(uint16_t));
+            for (int ch = 0; ch < 3; ++ch)
+                for (int y = 0; y < ps; ++y)
+                    for (int x = 0; x < ps; ++x)
+                        pad[r * c->Kp + (size_t)y * rp + 3 * x + ch] = hb[o_wpe + r * P + (size_t)ch * ps * ps + y * ps + x];
         CREATE_HIP(hipMalloc((void **)&c->d_wpe, pad.size() * sizeof(bf16_t)));
         CREATE_HIP(hipMemcpy(c->d_wpe, pad.data(), pad.size() * sizeof(bf16_t), hipMemcpyHostToDevice));
     }

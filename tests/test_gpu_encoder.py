@@ -31,14 +31,33 @@ def run(cfg, blob, grids, pixels=None):
                                        (replace(synth.TINY, patch=16), [(5, 7), (1, 1), (3, 6)]),
                                        (replace(synth.TINY, patch=8), [(6, 5), (2, 2)]),
                                        (replace(synth.TINY, patch=1), [(9, 7)]),
-                                       (replace(synth.TINY, patch=32), [(3, 4)])],
-                         ids=["tiny", "ragged", "one_layer", "patch16", "patch8", "patch1", "patch32"])
-def test_patchify_bit_exact(cfg, grids):
+                                       (replace(synth.TINY, patch=32), [(3, 4)]),
+                                       (replace(synth.TINY, patch=7), [(5, 3), (1, 1), (2, 7)]),
+                                       (replace(synth.TINY, patch=3), [(1, 1)]),
+                                       (replace(synth.TINY, patch=1), [(1, 1)]),
+                                       (replace(synth.TINY, patch=64), [(2, 3)]),
+                                       (replace(synth.TINY, patch=1), [(1, 1), (1, 1), (1, 1)]),
+                                       (replace(synth.TINY, patch=2), [(1, 1)])],
+                         ids=["tiny", "ragged", "one_layer", "patch16", "patch8", "patch1", "patch32", "patch7",
+                              "patch3_one_patch", "patch1_three_bytes", "patch64", "patch1_nine_bytes",
+                              "patch2_twelve_bytes"])
+@pytest.mark.parametrize("misalign", [0, 1, 3], ids=["aligned", "px+1", "px+3"])
+def test_patchify_bit_exact(cfg, grids, misalign):
+    """The patch matrix the fused loader feeds the patch projection (dumped through the same
+    device functions), bit-exact against the oracle's patchify: patch sides 1 to 64 (segments
+    of 3 to 192 bytes, odd sides misaligning every other segment), packed ragged batches,
+    batches of 3, 9 and 12 bytes (under 12, the loader reads a padded copy), and pixel buffers
+    that start 1 or 3 bytes past an aligned address (the loader reads 12 aligned bytes around
+    each chunk, lowered at the end of the buffer so that it never passes the last dword)."""
     torch = require_gpu()
     c1 = replace(cfg, layers=0, out_hidden=16)
     enc = vit.Encoder(c1, synth.make_weights(c1))
     px = synth.make_pixels(c1, grids)
-    got = from_dev_bf16(enc.dump(vit.DUMP_PATCHES, torch.from_numpy(px).cuda(), grids))
+    store = torch.zeros(px.size + 8, dtype=torch.uint8, device="cuda")
+    store[misalign:misalign + px.size] = torch.from_numpy(px).cuda()
+    d_px = store[misalign:misalign + px.size]
+    assert d_px.data_ptr() % 4 == misalign
+    got = from_dev_bf16(enc.dump(vit.DUMP_PATCHES, d_px, grids))
     torch.cuda.synchronize()
     off, pix = 0, 0
     for gh, gw in grids:
@@ -48,25 +67,62 @@ def test_patchify_bit_exact(cfg, grids):
         pix += npx
 
 
-def test_identity_patch_projection_bit_exact():
+@pytest.mark.parametrize("grids", [[(7, 5), (3, 3)], [(96, 96), (7, 5), (3, 3)]], ids=["small", "96x96_packed"])
+def test_identity_patch_projection_bit_exact(grids):
     """W_pe = identity (D = 1024 >= 588 columns), b = 0: x0[:, :588] = patches and 0 after;
-    exact because each output has one non-zero product, so the zero K padding (588 -> 640)
-    and the patchify gather are checked together."""
+    exact because each output has one non-zero product, so the patchify inside the projection's
+    A loader, the permutation of W_pe into the loader's K order (588 columns spread over 672)
+    and its zero columns are checked together, on every row (9,260 rows: 256 x 128 tiles and
+    their 128 x 128 row tail)."""
     torch = require_gpu()
     cfg = replace(synth.V41, layers=0, out_hidden=16)
     blob = synth.make_weights(cfg)
     W = synth.split_weights(cfg, blob)
     W["pe.w"][:] = 0
     W["pe.w"][np.arange(588), np.arange(588)] = 0x3F80
-    grids = [(7, 5), (3, 3)]
     enc = vit.Encoder(cfg, blob)
     px = synth.make_pixels(cfg, grids)
     x0 = from_dev_bf16(enc.dump(vit.DUMP_EMBED, torch.from_numpy(px).cuda(), grids))
     torch.cuda.synchronize()
-    P = np.concatenate([oracle.patchify(px[:14 * 7 * 14 * 5 * 3], 7, 5, cfg),
-                        oracle.patchify(px[14 * 7 * 14 * 5 * 3:], 3, 3, cfg)])
-    assert np.array_equal(x0[:, :588], P)
+    parts, off = [], 0
+    for gh, gw in grids:
+        n = 14 * gh * 14 * gw * 3
+        parts.append(oracle.patchify(px[off:off + n], gh, gw, cfg))
+        off += n
+    assert np.array_equal(x0[:, :588], np.concatenate(parts))
     assert not x0[:, 588:].any()
+
+
+def test_patch_projection_over_2gib_of_pixels():
+    """A batch of 400 images of 96 x 96 patches holds 2.17 GB of pixels, more than one launch of
+    the fused patch loader addresses (under 2^31 bytes): the projection runs in groups of whole
+    images (here 396 and 4).  The patch matrix and the projection of the first image, the two
+    images at the group boundary and the last image match the oracle (patches bit-exact).
+    Pixels drawn on the GPU from a seeded generator (2 GB would take minutes on the host)."""
+    torch = require_gpu()
+    cfg = replace(synth.TINY, layers=0, out_hidden=16)
+    blob = synth.make_weights(cfg)
+    W = oracle.Weights(cfg, blob)
+    enc = vit.Encoder(cfg, blob)
+    grids = [(96, 96)] * 400
+    per = 14 * 96 * 14 * 96 * 3
+    assert 396 * per < 2 ** 31 < 397 * per
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20251202)
+    d_px = torch.randint(0, 256, (400 * per,), dtype=torch.uint8, device="cuda", generator=gen)
+    P = enc.dump(vit.DUMP_PATCHES, d_px, grids)
+    X = enc.dump(vit.DUMP_EMBED, d_px, grids)
+    torch.cuda.synchronize()
+    for i in (0, 395, 396, 399):
+        img = d_px[i * per:(i + 1) * per].cpu().numpy()
+        want = oracle.patchify(img, 96, 96, cfg)
+        got = from_dev_bf16(P[i * 9216:(i + 1) * 9216])
+        assert np.array_equal(got, want), i
+        x_want = oracle.linear(want, None, W["pe.b"], Wt=W.T("pe.w"))
+        # slack for an fp32 sum taken in another order: 2^-18 sum_k |p_k w_k| per output
+        slack = 2.0 ** -18 * (np.abs(want).astype(np.float64) @ np.abs(W.T("pe.w")).astype(np.float64))
+        assert_bf16_close(from_dev_bf16(X[i * 9216:(i + 1) * 9216]), x_want, atol=slack,
+                          what=f"embed of image {i}")
 
 
 @pytest.mark.parametrize("cfg,grids", [(synth.V41, [(5, 7), (96, 96), (1, 1), (3, 11)]),

@@ -119,11 +119,12 @@ def test_linear_row_tail(act, out_f32):
 
 @pytest.mark.parametrize("act,out_f32", [(vit.ACT_GELU_TANH, False), (vit.ACT_NONE, True)])
 def test_linear_split_k_tail(act, out_f32):
-    """264 tiles of 256 x 128 on 256 compute units: the 8 leftover tiles (rows 8192..8399,
-    ragged in M and N) are cut into K slices whose fp32 partials a second kernel sums."""
+    """264 tiles of 256 x 128 on 256 compute units (K = 4096: long enough that the 132 tiles of
+    256 x 256 are not chosen): the 8 leftover tiles (rows 8192..8399, ragged in M and N) are cut
+    into K slices whose fp32 partials a second kernel sums."""
     torch = require_gpu()
     enc, _, _ = encoder()
-    M, K, N = 8400, 2048, 1020
+    M, K, N = 8400, 4096, 1020
     A = seeded_bf16((M, K), 107, 0)
     W = seeded_bf16((N, K), 107, 1, std=0.02)
     b = seeded_bf16((N,), 107, 2, std=0.02)

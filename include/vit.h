@@ -281,11 +281,12 @@ vit_status vit_dump(vit_ctx *ctx, int32_t boundary, int32_t arg, const uint8_t *
  * may be NULL) and starts a new accumulation.  Disabled by default.  VIT_STEP_LAYERNORM also
  * counts the RMSNorm of the official layers, VIT_STEP_FC1 their SwiGLU step (gate and up
  * projections in one launch), VIT_STEP_FC2 the down projection, and VIT_STEP_PROJECTOR the
- * whole aligner (both projections when there are two). */
+ * whole aligner (both projections when there are two).  VIT_STEP_ATTENTION is the attention
+ * kernel alone; VIT_STEP_ATTN_MERGE the merge of its key-sliced items, when a batch has any. */
 enum {
     VIT_STEP_PATCH_EMBED = 0, VIT_STEP_LAYERNORM = 1, VIT_STEP_QKV = 2, VIT_STEP_ROPE = 3,
     VIT_STEP_ATTENTION = 4, VIT_STEP_OUT_PROJ = 5, VIT_STEP_FC1 = 6, VIT_STEP_FC2 = 7,
-    VIT_STEP_PROJECTOR = 8, VIT_STEP_OVERLAY = 9, VIT_STEP_COUNT = 10
+    VIT_STEP_PROJECTOR = 8, VIT_STEP_OVERLAY = 9, VIT_STEP_ATTN_MERGE = 10, VIT_STEP_COUNT = 11
 };
 vit_status vit_timing_enable(vit_ctx *ctx, int32_t enable);
 vit_status vit_timing_read(vit_ctx *ctx, float *ms, int64_t *launches);

@@ -30,7 +30,7 @@ EXPORTS = ("vit_blob_elems", "vit_create", "vit_destroy", "vit_reserve", "vit_nu
            "vit_assemble", "vit_plan_image", "vit_preprocess", "vit_op_rmsnorm",
            "vit_op_linear_noalloc", "vit_layout_v4", "vit_set_span_layout")
 STEP_NAMES = ("patch_embed", "layernorm", "qkv", "rope", "attention", "out_proj", "fc1", "fc2",
-              "projector", "overlay")
+              "projector", "overlay", "attn_merge")
 
 
 class VitError(RuntimeError):

@@ -552,11 +552,6 @@ hipError_t run_attention(const bf16_t *qkv, const bf16_t *vt, int64_t ldv, bf16_
     const float c_log2 = (float)(1.4426950408889634 / sqrt((double)HD));
     hipLaunchKernelGGL(attention_kernel<HD>, dim3((unsigned)grid), dim3(256), 0, s, qkv, vt, ldv, o, work,
                        n_work, imgs, D, H, c_log2, sp);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || tail == 0 || sp.slices == 1) return e;
-    const int64_t threads = (int64_t)8 * tail * 128 * (HD / 8);
-    hipLaunchKernelGGL(attention_merge_kernel, dim3((unsigned)ceil_div(threads, 256)), dim3(256), 0, s,
-                       sp, work, n_work, imgs, D, HD, o);
     return hipGetLastError();
 }
 
@@ -622,6 +617,19 @@ AttnSplit attention_plan(const ImgDesc *imgs, int n_img, int n_work, int D, int 
     sp.full = full;
     sp.slices = s;
     return sp;
+}
+
+bool attention_needs_merge(const AttnSplit &sp) { return sp.per_xcd > sp.full && sp.slices > 1; }
+
+hipError_t launch_attention_merge(bf16_t *o, const RowTile *work, int n_work, const ImgDesc *imgs, int D, int H,
+                                  const AttnSplit &sp, hipStream_t s)
+{
+    if (n_work <= 0 || !attention_needs_merge(sp)) return hipSuccess;
+    const int tail = sp.per_xcd - sp.full, hd = D / H;
+    const int64_t threads = (int64_t)8 * tail * attention_q_tile() * (hd / 8);
+    hipLaunchKernelGGL(attention_merge_kernel, dim3((unsigned)ceil_div(threads, 256)), dim3(256), 0, s, sp, work,
+                       n_work, imgs, D, hd, o);
+    return hipGetLastError();
 }
 
 hipError_t launch_attention(const bf16_t *qkv, const bf16_t *vt, int64_t ldv, bf16_t *o,

@@ -82,9 +82,15 @@ struct AttnSplit {
 // 1 = never split, 2..4 = every item cut into that many key ranges.
 AttnSplit attention_plan(const ImgDesc *h_imgs, int n_img, int n_work, int D, int H, int fixed);
 size_t attention_plan_bytes(const AttnSplit &sp, int D, int H);
+// launch_attention runs the attention kernel; when the split has key-sliced items
+// (attention_needs_merge), launch_attention_merge must follow it on the same stream to write
+// their rows of o.
 hipError_t launch_attention(const bf16_t *qkv, const bf16_t *vt, int64_t ldv, bf16_t *o,
                             const RowTile *work, int n_work, const ImgDesc *imgs, int D, int H,
                             const AttnSplit &sp, hipStream_t s);
+bool attention_needs_merge(const AttnSplit &sp);
+hipError_t launch_attention_merge(bf16_t *o, const RowTile *work, int n_work, const ImgDesc *imgs, int D, int H,
+                                  const AttnSplit &sp, hipStream_t s);
 
 // Compute units of the current device.
 int cu_count();

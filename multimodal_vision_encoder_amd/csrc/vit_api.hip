@@ -596,6 +596,9 @@ vit_status encode_impl(vit_ctx *c, const uint8_t *px, const vit_grid *grids, int
         if (stop == VIT_DUMP_QKV && arg == l) return copy_out(c->qkv);
         TLAUNCH(c, VIT_STEP_ATTENTION, s, launch_attention(c->qkv, c->vt, p.vt_cols, c->o, dp.attn, (int)p.attn.size(),
                                    dp.imgs, D, H, asp, s));
+        if (attention_needs_merge(asp))
+            TLAUNCH(c, VIT_STEP_ATTN_MERGE, s,
+                    launch_attention_merge(c->o, dp.attn, (int)p.attn.size(), dp.imgs, D, H, asp, s));
         if (stop == VIT_DUMP_ATTN && arg == l) return copy_out(c->o);
         TLAUNCH(c, VIT_STEP_OUT_PROJ, s, launch_linear(c->o, p.N, D, w.wo, w.bo, D, ACT_NONE, false, c->delta, &gws, s));
         TLAUNCH(c, VIT_STEP_LAYERNORM, s, launch_layernorm(c->x, c->delta, c->x, p.N, D, w.ln2g, w.ln2b, c->cfg.ln_eps,
@@ -1290,6 +1293,8 @@ vit_status vit_op_attention(vit_ctx *ctx, const uint16_t *d_qkv, const uint16_t 
     if ((st = stage_plan(ctx, p, (hipStream_t)stream, dp)) != VIT_OK) return st;
     LAUNCH(ctx, launch_attention(d_qkv, d_vt, p.vt_cols, d_o, dp.attn, (int)p.attn.size(), dp.imgs,
                                  ctx->D, ctx->H, asp, (hipStream_t)stream));
+    LAUNCH(ctx, launch_attention_merge(d_o, dp.attn, (int)p.attn.size(), dp.imgs, ctx->D, ctx->H, asp,
+                                       (hipStream_t)stream));
     return VIT_OK;
 }
 

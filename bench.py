@@ -63,10 +63,9 @@ def bytes_per_pass(cfg, grids, vt_cols):
     D, L, Dl = cfg.hidden, cfg.layers, cfg.out_hidden
     N = sum(gh * gw for gh, gw in grids)
     M = sum(cfg.tokens(gh, gw) for gh, gw in grids)
-    ln_first = 2 * N * D * 2                   # read x, write ln
-    ln_res = 4 * N * D * 2                     # read x and delta, write x and ln
-    n_res = 2 * L                              # ln1 of layers 1.., ln2 of every layer, final
-    ln = (ln_first + n_res * ln_res) if L > 0 else ln_first
+    # every norm reads x and writes its output (the residual adds run in the epilogues of the
+    # out-projection and fc2): two per layer and the final one
+    ln = (2 * L + 1) * 2 * N * D * 2
     rope = L * (8 * N * D + 2 * N * D + 2 * vt_cols * D)   # q,k in+out, v in, v^T out
     overlay = M * Dl * (4 + 2) + 4 * M
     return {"layernorm": ln, "rope": rope, "overlay": overlay}

@@ -53,6 +53,18 @@ vit_status vit_op_linear_noalloc(vit_ctx *ctx, const uint16_t *d_A, int64_t M, i
                                  const uint16_t *d_W, const uint16_t *d_b, int32_t N, int32_t act,
                                  int32_t out_f32, void *d_out, void *stream);
 
+/* Linear layer with the block's residual add, as vit_encode runs the out-projection and fc2
+ * ([Z] "Step 2" boundary table: the block output fixes the residual order; [Z] "Multimodal
+ * basics": pre-norm transformer blocks):
+ *   x[i][j] = bf16(x[i][j] + bf16(sum_k A[i][k] W[j][k] + b[j]))
+ * i.e. vit_op_linear (VIT_ACT_NONE, bf16 output) followed by the residual add of
+ * vit_op_layernorm, bitwise, in one pass: the sum is formed as the product tile is written.
+ * A bf16 [M][K], W bf16 [N][K], b bf16 [N] or NULL, x bf16 [M][N] read and updated in place.
+ * VIT_E_ARG when A and x overlap, or as vit_op_linear for the sizes. */
+vit_status vit_op_linear_residual(vit_ctx *ctx, const uint16_t *d_A, int64_t M, int32_t K,
+                                  const uint16_t *d_W, const uint16_t *d_b, int32_t N, uint16_t *d_x,
+                                  void *stream);
+
 /* Residual add + LayerNorm over rows of width D (D in {64, 128, 256, 512, 1024, 1536, 2048}):
  *   if d_delta != NULL:  x = bf16(x + delta), written to d_xout (may alias d_x);
  *   out = bf16((x - mean) / sqrt(var + eps) * g + b), mean/var over the row (biased).

@@ -28,7 +28,8 @@ EXPORTS = ("vit_blob_elems", "vit_create", "vit_destroy", "vit_reserve", "vit_nu
            "vit_op_attention", "vit_op_merge_project", "vit_timing_enable", "vit_timing_read",
            "vit_set_attention_split", "vit_op_qkv_rope", "vit_set_sentinels",
            "vit_assemble", "vit_plan_image", "vit_preprocess", "vit_op_rmsnorm",
-           "vit_op_linear_noalloc", "vit_layout_v4", "vit_set_span_layout")
+           "vit_op_linear_noalloc", "vit_layout_v4", "vit_set_span_layout",
+           "vit_op_linear_residual")
 STEP_NAMES = ("patch_embed", "layernorm", "qkv", "rope", "attention", "out_proj", "fc1", "fc2",
               "projector", "overlay", "attn_merge")
 
@@ -102,6 +103,7 @@ def lib():
             "vit_last_error": (ctypes.c_char_p, [vp]),
             "vit_op_linear": (i32, [vp, vp, i64, i32, vp, vp, i32, i32, i32, vp, vp]),
             "vit_op_linear_noalloc": (i32, [vp, vp, i64, i32, vp, vp, i32, i32, i32, vp, vp]),
+            "vit_op_linear_residual": (i32, [vp, vp, i64, i32, vp, vp, i32, vp, vp]),
             "vit_op_layernorm": (i32, [vp, vp, vp, vp, i64, i32, vp, vp, ctypes.c_float, vp, vp]),
             "vit_op_rmsnorm": (i32, [vp, vp, vp, vp, i64, i32, vp, ctypes.c_float, vp, vp]),
             "vit_vt_stride": (i64, [P(Grid), i32]),
@@ -397,6 +399,22 @@ class Encoder:
         self._check(lib().vit_op_linear(self._ctx, _ptr(A), M, K, _ptr(W), _ptr(b), N, act,
                                         1 if out_f32 else 0, _ptr(out), _stream(stream)))
         return out
+
+    def op_linear_residual(self, A, W, b, x, stream=None):
+        """x = bf16(x + bf16(A W^T + b)) in place on x; returns x."""
+        import torch
+        if A is None or A.dim() != 2 or W is None or W.dim() != 2:
+            raise ValueError("A and W must be 2-D tensors")
+        M, K = A.shape
+        N = W.shape[0]
+        check_tensor(A, "A", torch.bfloat16, shape=(M, K), gpu=False)
+        check_tensor(W, "W", torch.bfloat16, shape=(N, K), gpu=False)
+        check_tensor(b, "b", torch.bfloat16, shape=(N,), optional=True, gpu=False)
+        check_tensor(x, "x", torch.bfloat16, shape=(M, N), gpu=False)
+        on_gpu(A=A, W=W, b=b, x=x)
+        self._check(lib().vit_op_linear_residual(self._ctx, _ptr(A), M, K, _ptr(W), _ptr(b), N, _ptr(x),
+                                                 _stream(stream)))
+        return x
 
     def op_layernorm(self, x, g, b, eps, delta=None, xout=None, stream=None):
         import torch

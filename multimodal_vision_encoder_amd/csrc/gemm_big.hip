@@ -188,7 +188,7 @@ __device__ __forceinline__ void bias_act(const bf16_t *bias, int N, int n, const
 template <int ACT>
 struct EpiBF16 {
     static constexpr int OUT_BYTES = 2;
-    static constexpr bool CUSTOM = false, PAIRED = false;
+    static constexpr bool CUSTOM = false, PAIRED = false, RESID = false;
     bf16_t *out;
     const bf16_t *bias;
     int64_t M;
@@ -217,9 +217,57 @@ struct EpiBF16 {
     }
 };
 
+// 8 bf16 of x plus the 8 bf16 of d, each sum rounded to bf16 (round to nearest even).  The
+// fp32 sum of two bf16 values is exact unless their exponents are far apart, and then the
+// smaller one is far below half a bf16 unit of the larger: rounding via fp32 equals rounding
+// the exact sum.
+__device__ __forceinline__ uint4 add_bf16x8(uint4 x, uint4 d)
+{
+    const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ds[4] = {d.x, d.y, d.z, d.w};
+    uint32_t r[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        r[i] = pack_bf16x2(__uint_as_float(xs[i] << 16) + __uint_as_float(ds[i] << 16),
+                           __uint_as_float(xs[i] & 0xFFFF0000u) + __uint_as_float(ds[i] & 0xFFFF0000u));
+    return make_uint4(r[0], r[1], r[2], r[3]);
+}
+
+// Residual update of the token stream by a block's projection ([Z] "Step 2" boundary table:
+// the block output fixes the residual order; [Z] "Multimodal basics": pre-norm blocks):
+//   x[m][n] = bf16(x[m][n] + bf16(acc + b[n]))
+// the projection rounded to bf16 first, then the sum rounded again, as a separate residual
+// add of the bf16 projection output would.  out is x itself, read and written in place:
+// put() stages bf16(acc + b) and the row writer adds x on the way out.
+struct EpiResid {
+    static constexpr int OUT_BYTES = 2;
+    static constexpr bool CUSTOM = false, PAIRED = false, RESID = true;
+    bf16_t *out;
+    const bf16_t *bias;
+    int64_t M;
+    int N;
+    __device__ __forceinline__ const bf16_t *bias_ptr() const { return bias; }
+    __device__ __forceinline__ int ncols() const { return N; }
+    __device__ __forceinline__ void put(char *dst, const float *v, uint2 b) const
+    {
+        float r[4];
+        add_act<ACT_NONE>(b, v, r);
+        *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]));
+    }
+    __device__ __forceinline__ void store(int64_t m, int n, const float *v) const
+    {
+        if (m >= M) return;
+        float r[4];
+        bias_act<ACT_NONE>(bias, N, n, v, r);
+        bf16_t *o = out + m * N + n;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (n + j < N) o[j] = f32_to_bf16(bf16_to_f32(o[j]) + bf16_to_f32(f32_to_bf16(r[j])));
+    }
+};
+
 struct EpiF32 {
     static constexpr int OUT_BYTES = 4;
-    static constexpr bool CUSTOM = false, PAIRED = false;
+    static constexpr bool CUSTOM = false, PAIRED = false, RESID = false;
     float *out;
     const bf16_t *bias;
     int64_t M;
@@ -251,7 +299,7 @@ struct EpiF32 {
 // Raw fp32 partial tile of a K slice (no bias, no activation), [BM][BN] contiguous.
 struct EpiPart {
     static constexpr int OUT_BYTES = 4;
-    static constexpr bool CUSTOM = false, PAIRED = false;
+    static constexpr bool CUSTOM = false, PAIRED = false, RESID = false;
     float *out;
     __device__ __forceinline__ const bf16_t *bias_ptr() const { return nullptr; }
     __device__ __forceinline__ int ncols() const { return 4; }
@@ -271,7 +319,7 @@ struct EpiPart {
 // N is the fused width 2F; out is bf16 [M][N/2].
 struct EpiSwiGLU {
     static constexpr int OUT_BYTES = 2;
-    static constexpr bool CUSTOM = false, PAIRED = true;
+    static constexpr bool CUSTOM = false, PAIRED = true, RESID = false;
     bf16_t *out;
     const bf16_t *bias;
     int64_t M;
@@ -325,7 +373,7 @@ __device__ __forceinline__ uint32_t bf16_to_f16_sat(uint32_t b)
 template <int HD>
 struct EpiQKVRope {
     static constexpr int OUT_BYTES = 2;
-    static constexpr bool CUSTOM = true, PAIRED = false;
+    static constexpr bool CUSTOM = true, PAIRED = false, RESID = false;
     bf16_t *out;        // [M][3D]
     const bf16_t *bias;
     int64_t M;
@@ -808,11 +856,21 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(SRC src, const bf16_t 
     // whole rows of a staged tile (tile_bytes per row) to global memory
     // A whole tile (every row, full width) reads all its chunks from LDS before it stores any,
     // so one wait covers the LDS latency of all of them; a partial tile goes chunk by chunk.
-    auto write_rows = [&](auto tbc, int pitch, char *gout, int64_t gpitch, int rows, int row_bytes) {
+    // With a residual epilogue (bf16 tiles) each chunk is added to the bf16 values already at
+    // its destination, whose loads are issued before the LDS reads.
+    auto write_rows = [&](auto tbc, auto rsd, int pitch, char *gout, int64_t gpitch, int rows, int row_bytes) {
         constexpr int TB = decltype(tbc)::value, CH = TB / 16, IT = BM * CH / NT;
+        constexpr bool RS = decltype(rsd)::value;
         static_assert(BM * CH % NT == 0, "tile chunks must divide among the threads");
         if (rows == BM && row_bytes == TB) {
-            uint4 val[IT];
+            uint4 val[IT], xv[IT];
+            if constexpr (RS) {
+#pragma unroll
+                for (int it = 0; it < IT; ++it) {
+                    const int c = tid + it * NT, r = c / CH, b = (c % CH) * 16;
+                    xv[it] = *reinterpret_cast<const uint4 *>(gout + r * gpitch + b);
+                }
+            }
 #pragma unroll
             for (int it = 0; it < IT; ++it) {
                 const int c = tid + it * NT, r = c / CH, b = (c % CH) * 16;
@@ -821,6 +879,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(SRC src, const bf16_t 
 #pragma unroll
             for (int it = 0; it < IT; ++it) {
                 const int c = tid + it * NT, r = c / CH, b = (c % CH) * 16;
+                if constexpr (RS) val[it] = add_bf16x8(xv[it], val[it]);
                 *reinterpret_cast<uint4 *>(gout + r * gpitch + b) = val[it];
             }
             return;
@@ -830,21 +889,29 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(SRC src, const bf16_t 
         for (int c = tid; c < BM * ch; c += NT) {
             const int r = c / ch, b = (c % ch) * 16;
             if (r >= rows) break;
-            const uint4 val = *reinterpret_cast<const uint4 *>(smem + r * pitch + b);
+            uint4 val = *reinterpret_cast<const uint4 *>(smem + r * pitch + b);
             char *dst = gout + r * gpitch + b;
             if (b + 16 <= row_bytes) {
+                if constexpr (RS) val = add_bf16x8(*reinterpret_cast<const uint4 *>(dst), val);
                 *reinterpret_cast<uint4 *>(dst) = val;
             } else if (b < row_bytes) {                    // ragged right edge, 2-byte pieces
                 const uint16_t *s16 = reinterpret_cast<const uint16_t *>(smem + r * pitch + b);
-                for (int e2 = 0; e2 < (row_bytes - b) / 2; ++e2) reinterpret_cast<uint16_t *>(dst)[e2] = s16[e2];
+                uint16_t *d16 = reinterpret_cast<uint16_t *>(dst);
+                for (int e2 = 0; e2 < (row_bytes - b) / 2; ++e2) {
+                    if constexpr (RS)
+                        d16[e2] = f32_to_bf16(bf16_to_f32(d16[e2]) + bf16_to_f32(s16[e2]));
+                    else
+                        d16[e2] = s16[e2];
+                }
             }
         }
     };
     auto staged = [&](const auto &e, int pitch, int ob, char *gout, int64_t gpitch, int rows,
                       int row_bytes) {
+        using E = std::decay_t<decltype(e)>;
         stage_tile(e, pitch, ob);
-        write_rows(std::integral_constant<int, BN * std::decay_t<decltype(e)>::OUT_BYTES>{}, pitch, gout, gpitch,
-                   rows, row_bytes);
+        write_rows(std::integral_constant<int, BN * E::OUT_BYTES>{}, std::integral_constant<bool, E::RESID>{}, pitch,
+                   gout, gpitch, rows, row_bytes);
     };
     if (item >= 0) {   // K slice: raw fp32 partial tile, every row and column (host: BN = 128)
         if constexpr (PSTAGED)
@@ -875,7 +942,8 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(SRC src, const bf16_t 
         __syncthreads();
         const int rows = (int)(ep.M - m0 < BM ? ep.M - m0 : BM);
         const int row_bytes = N - n0 < BN ? N - n0 : BN;     // (fused columns / 2) x 2 bytes
-        write_rows(std::integral_constant<int, BN>{}, OPITCH, reinterpret_cast<char *>(ep.out) + (m0 * (N / 2) + n0 / 2) * 2,
+        write_rows(std::integral_constant<int, BN>{}, std::false_type{}, OPITCH,
+                   reinterpret_cast<char *>(ep.out) + (m0 * (N / 2) + n0 / 2) * 2,
                    (int64_t)N, rows, row_bytes);
     } else if constexpr (EP::CUSTOM) {
         static_assert(STAGED, "custom epilogues need the staged tile");
@@ -1002,6 +1070,7 @@ SrcPlain rows_from(const SrcPlain &s, int64_t m0) { return SrcPlain{s.A + m0 * s
 template <int ACT>
 EpiBF16<ACT> rows_from(const EpiBF16<ACT> &e, int64_t m0) { return EpiBF16<ACT>{e.out + m0 * e.N, e.bias, e.M - m0, e.N}; }
 EpiF32 rows_from(const EpiF32 &e, int64_t m0) { return EpiF32{e.out + m0 * e.N, e.bias, e.M - m0, e.N}; }
+EpiResid rows_from(const EpiResid &e, int64_t m0) { return EpiResid{e.out + m0 * e.N, e.bias, e.M - m0, e.N}; }
 EpiSwiGLU rows_from(const EpiSwiGLU &e, int64_t m0) { return EpiSwiGLU{e.out + m0 * (e.N / 2), e.bias, e.M - m0, e.N}; }
 SrcPatch rows_from(const SrcPatch &s, int64_t m0)
 {
@@ -1119,6 +1188,12 @@ hipError_t launch_linear(const bf16_t *A, int64_t M, int K, const bf16_t *W, con
                          int N, int act, bool out_f32, void *out, const GemmWorkspace *ws, hipStream_t s)
 {
     return dispatch(SrcPlain{A, K, M}, W, M, N, K, bias, act, out_f32, out, ws, s);
+}
+
+hipError_t launch_linear_residual(const bf16_t *A, int64_t M, int K, const bf16_t *W, const bf16_t *bias, int N,
+                                  bf16_t *x, const GemmWorkspace *ws, hipStream_t s)
+{
+    return run_shaped(SrcPlain{A, K, M}, W, M, N, K, EpiResid{x, bias, M, N}, ws, s);
 }
 
 hipError_t launch_patch_embed(const uint8_t *lpx, int64_t pix_first, int64_t pix_bytes, const ImgDesc *imgs,

@@ -28,6 +28,12 @@ hipError_t launch_linear(const bf16_t *A, int64_t M, int K, const bf16_t *W, con
                          int N, int act, bool out_f32, void *out, const GemmWorkspace *ws,
                          hipStream_t s);
 
+// Linear layer with the block's residual add: x = bf16(x + bf16(A W^T + b)), x bf16 [M][N]
+// read and written in place (A must not overlap it); tiles, K split and workspace as
+// launch_linear with ACT_NONE and bf16 output.
+hipError_t launch_linear_residual(const bf16_t *A, int64_t M, int K, const bf16_t *W, const bf16_t *bias, int N,
+                                  bf16_t *x, const GemmWorkspace *ws, hipStream_t s);
+
 // Patchify fused into the patch projection: x0 = bf16(P W_pe^T + b) for patch rows
 // [m_first, m_first + M) (out is the whole [N][D] output), the patch matrix P computed from
 // the pixels inside the GEMM's A loader.  Those rows' images hold the pix_bytes (< 2^31) bytes

@@ -6,7 +6,9 @@
 //   vision towers"; "Step 2" boundary table, RMSNorm semantics at the final norm):
 //   out = bf16(x / sqrt(mean(x^2) + eps) * g)
 //
-// Pre-norm blocks and the final norm ([Z] "Step 2" boundary table).  The row stays in
+// Pre-norm blocks and the final norm ([Z] "Step 2" boundary table); the encoder's residual
+// adds run in the epilogues of the out-projection and fc2, so there it takes no delta (the
+// delta form serves vit_op_layernorm / vit_op_rmsnorm).  The row stays in
 // registers: each lane holds D/64 elements (16 at D = 1024, loaded as two 16-byte chunks
 // so that a wave reads 1 KB contiguous per instruction); statistics are two-pass (mean,
 // then squared deviations) with butterfly reductions across the wave.  HBM-bound: it reads

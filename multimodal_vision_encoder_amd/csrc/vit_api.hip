@@ -101,8 +101,7 @@ struct vit_ctx {
     int attn_split_fixed = 0;     // 0: chosen per batch; 1..4: fixed key slices
     int span_layout = VIT_SPAN_V41;   // span geometry of vit_assemble
     int64_t cap_patches = 0, cap_vt_cols = 0, reserve_cap = 0;
-    bf16_t *x = nullptr, *ln = nullptr, *qkv = nullptr, *vt = nullptr, *o = nullptr,
-           *delta = nullptr, *h1 = nullptr;
+    bf16_t *x = nullptr, *ln = nullptr, *qkv = nullptr, *vt = nullptr, *o = nullptr, *h1 = nullptr;
 
     // per-call metadata: pinned staging -> device
     char *h_stage = nullptr, *d_meta = nullptr;
@@ -269,7 +268,7 @@ vit_status make_plan(vit_ctx *ctx, const vit_grid *grids, int n, Plan &p)
 
 void free_workspace(vit_ctx *c)
 {
-    bf16_t **bufs[] = {&c->x, &c->ln, &c->qkv, &c->vt, &c->o, &c->delta, &c->h1};
+    bf16_t **bufs[] = {&c->x, &c->ln, &c->qkv, &c->vt, &c->o, &c->h1};
     for (auto b : bufs) {
         if (*b) (void)hipFree(*b);
         *b = nullptr;
@@ -342,7 +341,7 @@ vit_status ensure_workspace(vit_ctx *c, int64_t N, int64_t vt_cols)
     const size_t D = c->D;
     struct { bf16_t **p; size_t n; } req[] = {
         {&c->x, Np * D}, {&c->ln, Np * D}, {&c->qkv, Np * 3 * D}, {&c->o, Np * D},
-        {&c->delta, Np * D}, {&c->h1, Np * (size_t)c->F}, {&c->vt, (size_t)c->H * c->hd * Vc}};
+        {&c->h1, Np * (size_t)c->F}, {&c->vt, (size_t)c->H * c->hd * Vc}};
     for (auto &r : req) {
         if (hipMalloc((void **)r.p, r.n * sizeof(bf16_t)) != hipSuccess) {
             (void)hipGetLastError();
@@ -587,7 +586,7 @@ vit_status encode_impl(vit_ctx *c, const uint8_t *px, const vit_grid *grids, int
     if (L > 0) LAUNCH(c, launch_vt_tail_zero(c->vt, p.vt_cols, dp.imgs, ni, D, s));
     for (int l = 0; l < L; ++l) {
         const Layer &w = c->layers[l];
-        TLAUNCH(c, VIT_STEP_LAYERNORM, s, launch_layernorm(c->x, l ? c->delta : nullptr, c->x, p.N, D, w.ln1g, w.ln1b,
+        TLAUNCH(c, VIT_STEP_LAYERNORM, s, launch_layernorm(c->x, nullptr, nullptr, p.N, D, w.ln1g, w.ln1b,
                                    c->cfg.ln_eps, rms, c->ln, s));
         // QKV projection with RoPE on q, k and the V^T relayout in its epilogue
         TLAUNCH(c, VIT_STEP_QKV, s, launch_qkv_rope(c->ln, p.N, D, H, w.wqkv, w.bqkv, c->qkv, c->vt, p.vt_cols,
@@ -600,23 +599,19 @@ vit_status encode_impl(vit_ctx *c, const uint8_t *px, const vit_grid *grids, int
             TLAUNCH(c, VIT_STEP_ATTN_MERGE, s,
                     launch_attention_merge(c->o, dp.attn, (int)p.attn.size(), dp.imgs, D, H, asp, s));
         if (stop == VIT_DUMP_ATTN && arg == l) return copy_out(c->o);
-        TLAUNCH(c, VIT_STEP_OUT_PROJ, s, launch_linear(c->o, p.N, D, w.wo, w.bo, D, ACT_NONE, false, c->delta, &gws, s));
-        TLAUNCH(c, VIT_STEP_LAYERNORM, s, launch_layernorm(c->x, c->delta, c->x, p.N, D, w.ln2g, w.ln2b, c->cfg.ln_eps,
+        // the residual adds run in the epilogues of the out-projection and fc2 (x updated in place)
+        TLAUNCH(c, VIT_STEP_OUT_PROJ, s, launch_linear_residual(c->o, p.N, D, w.wo, w.bo, D, c->x, &gws, s));
+        TLAUNCH(c, VIT_STEP_LAYERNORM, s, launch_layernorm(c->x, nullptr, nullptr, p.N, D, w.ln2g, w.ln2b, c->cfg.ln_eps,
                                    rms, c->ln, s));
         // GELU MLP: fc1 + GELU; SwiGLU: gate and up projections + silu(g) u in one launch
         if (swiglu)
             TLAUNCH(c, VIT_STEP_FC1, s, launch_linear(c->ln, p.N, D, w.w1, w.b1, 2 * c->F, ACT_SWIGLU, false, c->h1, &gws, s));
         else
             TLAUNCH(c, VIT_STEP_FC1, s, launch_linear(c->ln, p.N, D, w.w1, w.b1, c->F, gelu_act(c->cfg), false, c->h1, &gws, s));
-        TLAUNCH(c, VIT_STEP_FC2, s, launch_linear(c->h1, p.N, c->F, w.w2, w.b2, D, ACT_NONE, false, c->delta, &gws, s));
-        if (stop == VIT_DUMP_LAYER && arg == l) {
-            // the residual add is fused into the next LayerNorm; run it to materialise x
-            LAUNCH(c, launch_layernorm(c->x, c->delta, c->x, p.N, D, c->lnf_g, c->lnf_b,
-                                       c->cfg.ln_eps, rms, c->ln, s));
-            return copy_out(c->x);
-        }
+        TLAUNCH(c, VIT_STEP_FC2, s, launch_linear_residual(c->h1, p.N, c->F, w.w2, w.b2, D, c->x, &gws, s));
+        if (stop == VIT_DUMP_LAYER && arg == l) return copy_out(c->x);
     }
-    TLAUNCH(c, VIT_STEP_LAYERNORM, s, launch_layernorm(c->x, L ? c->delta : nullptr, c->x, p.N, D, c->lnf_g, c->lnf_b,
+    TLAUNCH(c, VIT_STEP_LAYERNORM, s, launch_layernorm(c->x, nullptr, nullptr, p.N, D, c->lnf_g, c->lnf_b,
                                c->cfg.ln_eps, rms, c->ln, s));
     if (stop == VIT_DUMP_FINAL_NORM) return copy_out(c->ln);
     if (stop == VIT_DUMP_MERGED) {
@@ -1207,6 +1202,21 @@ vit_status vit_op_linear_noalloc(vit_ctx *ctx, const uint16_t *d_A, int64_t M, i
     if (!part) return fail(ctx, VIT_E_DEVICE, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
     const GemmWorkspace gws{part, kNoAllocScratchBytes};
     LAUNCH(ctx, launch_linear(d_A, M, K, d_W, d_b, N, act, out_f32 != 0, d_out, &gws, (hipStream_t)stream));
+    return VIT_OK;
+}
+
+vit_status vit_op_linear_residual(vit_ctx *ctx, const uint16_t *d_A, int64_t M, int32_t K, const uint16_t *d_W,
+                                  const uint16_t *d_b, int32_t N, uint16_t *d_x, void *stream)
+{
+    if (!ctx) return fail(nullptr, VIT_E_ARG, "ctx is NULL");
+    if (M < 0 || N < 1 || K < 64 || K % 64) return fail(ctx, VIT_E_ARG, "bad M, N or K");
+    if (M == 0) return VIT_OK;
+    if (!d_A || !d_W || !d_x) return fail(ctx, VIT_E_ARG, "NULL pointer");
+    const uintptr_t a0 = (uintptr_t)d_A, a1 = a0 + (uintptr_t)M * K * 2, x0 = (uintptr_t)d_x,
+                    x1 = x0 + (uintptr_t)M * N * 2;
+    if (a0 < x1 && x0 < a1) return fail(ctx, VIT_E_ARG, "A overlaps x");
+    const GemmWorkspace gws = gemm_ws(ctx);
+    LAUNCH(ctx, launch_linear_residual(d_A, M, K, d_W, d_b, N, d_x, &gws, (hipStream_t)stream));
     return VIT_OK;
 }
 

@@ -164,6 +164,50 @@ def test_linear_split_k_under_one_round(M, K, N, out_f32):
 # ------------------------------------------------------------------------------------------
 # LayerNorm (+ residual)
 # ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("M,K,N", [
+    (300, 128, 200),     # ragged M, several tiles, rows of 400 bytes (staged writer)
+    (257, 192, 130),     # rows of 260 bytes: per-element stores
+    (1, 64, 5),          # degenerate single row, tiny N
+    (9216, 1024, 1024),  # out-projection of the 1024-token image (256 x 256 tiles)
+    (9216, 4096, 1024),  # fc2 of that image (256 x 128 tiles, K-split tail)
+    (8492, 1024, 2000),  # 128 x 128 row tail
+    (3402, 4096, 1024),  # fc2 of the 384-token image (under one round, K split)
+], ids=["small", "unstaged", "one_row", "out_proj_1024", "fc2_1024", "row_tail", "fc2_384"])
+def test_linear_residual(M, K, N):
+    """x = bf16(x + bf16(A W^T + b)) in place: bitwise the residual add ([Z] "Step 2" table,
+    residual order of the block output; the oracle's add_round) of vit_op_linear's own output,
+    which the linear tests pin to the oracle; sampled rows also against the oracle directly."""
+    torch = require_gpu()
+    enc, _, _ = encoder()
+    A = seeded_bf16((M, K), 109, 0)
+    W = seeded_bf16((N, K), 109, 1, std=0.03)
+    b = seeded_bf16((N,), 109, 2, std=0.1)
+    x = seeded_bf16((M, N), 109, 3, std=2.0)
+    dA, dW, db = to_dev_bf16(A), to_dev_bf16(W), to_dev_bf16(b)
+    dx = to_dev_bf16(x)
+    d = enc.op_linear(dA, dW, db, vit.ACT_NONE, False)
+    got = enc.op_linear_residual(dA, dW, db, dx)
+    torch.cuda.synchronize()
+    assert got.data_ptr() == dx.data_ptr()
+    g = from_dev_bf16(got)
+    want = oracle.add_round(f32(x), from_dev_bf16(d))
+    assert np.array_equal(bf16_bits_of(g), bf16_bits_of(want)), "fused residual differs from linear + add"
+    rows = np.unique(np.r_[0, M // 2, M - 1, max(0, M - 300):M:37])
+    d_o = oracle.linear(f32(A[rows]), f32(W), f32(b), act=vit.ACT_NONE, round_out=True, workers=8)
+    w_o = oracle.add_round(f32(x[rows]), d_o)
+    tol = 2.0 ** -7 * (np.abs(w_o) + np.abs(d_o)) + sum_bound(A[rows], W)
+    assert np.all(np.abs(g[rows] - w_o) <= tol), "fused residual off the oracle"
+
+
+def test_linear_residual_rejects_overlap():
+    torch = require_gpu()
+    enc, _, _ = encoder()
+    buf = torch.zeros((64, 128), dtype=torch.bfloat16, device="cuda")
+    W = torch.zeros((64, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(vit.VitError):
+        enc.op_linear_residual(buf, W, None, buf.view(-1)[:64 * 64].view(64, 64))
+
+
 @pytest.mark.parametrize("M,D,residual", [(37, 64, False), (1000, 1024, True), (9216, 1024, True),
                                           (5, 256, True)])
 def test_layernorm(M, D, residual):

@@ -697,10 +697,16 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(SRC src, const bf16_t 
         }
     };
     // before converting raw k-tile t+NS (copied two steps ago): only the raw copies of k-tile
-    // t+NS+1 and (group 1) the W copies of the two steps since may still be in flight
-    auto wait_raw = [&]() {
+    // t+NS+1 and (group 1) the W copies issued since may still be in flight.  Group 1 issues W
+    // copies from step 0 on, after the raw copies of that step: before step 2 fewer of them
+    // follow the raw k-tile being converted (none in step 0, one k-tile in step 1; the raw
+    // copies of k-tiles NS and NS+1 came from the prologue), so the count is exact per step --
+    // a larger one would let the conversion read a raw slot before its bytes land.
+    auto wait_raw = [&](int t) {
         if (grp == 0) wait_vm_only<PL>();
-        else wait_vm_only<PL + 2 * BL>();
+        else if (t >= 2) wait_vm_only<PL + 2 * BL>();
+        else if (t == 1) wait_vm_only<PL + BL>();
+        else wait_vm_only<PL>();
         __asm__ volatile("" ::: "memory");   // the raw reads stay below the wait
     };
     // instructions stay on their side of a barrier (the MFMAs especially)
@@ -786,7 +792,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(SRC src, const bf16_t 
         if (t + 1 < nk) ldfrag(std::integral_constant<int, (S + 1) % NS>{});
         if constexpr (SRC::REG) {   // raw k-tile t+NS (copied two steps ago) into stage S; copy t+NS+2
             using B = std::integral_constant<int, S % 2>;
-            wait_raw();
+            wait_raw(t);
             put_a(min(t + NS, nk - 1), std::integral_constant<int, S>{}, B{});
             load_a(min(t + NS + 2, nk - 1), B{});
         }

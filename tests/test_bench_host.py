@@ -40,9 +40,10 @@ def test_flops_of_the_official_layer_variant():
 
 
 def test_memory_bound_bytes():
-    """LayerNorm: 4 passes over [N][D] bf16 per residual launch, 2 for the first; overlay:
-    fp32 rows in, bf16 rows out, one int32 index per row."""
+    """LayerNorm: every one of the 2 L + 1 norms reads [N][D] bf16 and writes its output (the
+    residual adds run in the out-projection and fc2 epilogues); overlay: fp32 rows in, bf16 rows
+    out, one int32 index per row."""
     n, D, L, m, Dl = 9216, 1024, 32, 1024, 5120
     by = bench.bytes_per_pass(synth.V41, [(96, 96)], 9216)
-    assert by["layernorm"] == 2 * n * D * 2 + 2 * L * 4 * n * D * 2
+    assert by["layernorm"] == (2 * L + 1) * 2 * n * D * 2
     assert by["overlay"] == m * Dl * 6 + 4 * m

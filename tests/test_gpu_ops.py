@@ -95,6 +95,34 @@ def test_linear_full_size_sampled(N, K, act):
     assert_bf16_close(got[rows], want, atol=sum_bound(A[rows], W), what="linear full size")
 
 
+@pytest.mark.parametrize("K", [64, 192, 320], ids=["one_ktile", "three_ktiles", "five_ktiles"])
+@pytest.mark.parametrize("act", [vit.ACT_NONE, vit.ACT_GELU_TANH], ids=["plain", "gelu"])
+def test_linear_big_tiles_every_row(K, act):
+    """One round of 256 x 256 tiles of plain activations (the 4-wave kernel with 64-wide k-tiles
+    and two LDS stages): M = 3900 leaves a ragged last tile row (60 rows), N = 4056 a ragged last
+    tile column (216 columns), and K = 64, 192, 320 give 1, 3 and 5 k-tiles (fewer than the two
+    stages, and an odd count that ends on the peeled step).  Every output is compared with the
+    oracle; the residual form of the same launch is checked bitwise against linear + add."""
+    torch = require_gpu()
+    enc, _, _ = encoder()
+    M, N = 3900, 4056
+    A = seeded_bf16((M, K), 131, 0)
+    W = seeded_bf16((N, K), 131, 1, std=0.05)
+    b = seeded_bf16((N,), 131, 2, std=0.1)
+    dA, dW, db = to_dev_bf16(A), to_dev_bf16(W), to_dev_bf16(b)
+    got = from_dev_bf16(enc.op_linear(dA, dW, db, act))
+    torch.cuda.synchronize()
+    want = oracle.linear(f32(A), f32(W), f32(b), act=act, workers=8)
+    assert_bf16_close(got, want, atol=sum_bound(A, W), what="256 x 256 tiles, every row")
+    if act == vit.ACT_NONE:
+        x = seeded_bf16((M, N), 131, 3, std=2.0)
+        dx = to_dev_bf16(x)
+        enc.op_linear_residual(dA, dW, db, dx)
+        torch.cuda.synchronize()
+        want_x = oracle.add_round(f32(x), got)
+        assert np.array_equal(bf16_bits_of(from_dev_bf16(dx)), bf16_bits_of(want_x)), "residual form differs"
+
+
 @pytest.mark.parametrize("act,out_f32", [(vit.ACT_GELU_TANH, False), (vit.ACT_NONE, True)])
 def test_linear_row_tail(act, out_f32):
     """272 tiles of 256 x 256 on 256 compute units: the last round's tiles are whole tile

@@ -564,8 +564,9 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_big_kernel(SRC src, const bf1
                                                               int N, int K, EP ep, int tiles_m,
                                                               int tiles_n, SplitK sk)
 {
-    static_assert(NW == 8 || (NW == 4 && std::is_same<SRC, SrcPlain>::value && BM == 256 && BN == 256),
-                  "8 waves, or 4 for 256 x 256 tiles of plain activations");
+    static_assert(NW == 8 || (NW == 4 && std::is_same<SRC, SrcPlain>::value && BN == 256 && (BM == 256 || BM == 192)),
+                  "8 waves, or 4 for 256 x 256 and 192 x 256 tiles of plain activations");
+    static_assert(NW == 4 || BM != 192, "192-row tiles run on 4 waves");
     constexpr int NT = NW * 64, NWN = 2;
     constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2, STAGE = A_BYTES + B_BYTES;
     constexpr int CPR = BK / 8;                             // 16-byte chunks per LDS row
@@ -635,8 +636,8 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_big_kernel(SRC src, const bf1
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     if constexpr (NW == 4) {
-        // One wave per SIMD with a 128 x 128 output tile (half the LDS fragment reads per MFMA
-        // of the 8-wave form), whole tiles only (no K slices).  K-tiles are 64 wide, so each
+        // One wave per SIMD with a (BM/2) x 128 output tile (128 x 128: half the LDS fragment
+        // reads per MFMA of the 8-wave form), whole tiles only (no K slices).  K-tiles are 64 wide, so each
         // LDS row is one 128-byte line of A or W and every copy fetches whole lines; two LDS
         // stages of 64 KB.  Chunk c = (i * 4 + wave) * 64 + lane of a tile holds row c / 8,
         // logical chunk (c % 8) ^ ((row / 2) % 8): 16 consecutive rows of one ds_read_b128 pass
@@ -1170,6 +1171,13 @@ template <int BM, int BN, class SRC, class EP>
 hipError_t launch_big(dim3 grid, SRC src, const bf16_t *W, int N, int K, EP ep, int tiles_m, int tiles_n,
                       SplitK sk, hipStream_t s)
 {
+    if constexpr (BM == 192) {   // chosen only for plain activations under 2^31 bytes, whole tiles
+        static_assert(BN == 256 && std::is_same<SRC, SrcPlain>::value, "192-row tiles: plain sources");
+        if (sk.splits > 1 || !plain_small(src, N, K)) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((gemm_big_kernel<BM, BN, SRC, EP, 4>), grid, dim3(256), 0, s, src, W, N, K, ep, tiles_m,
+                           tiles_n, sk);
+        return hipGetLastError();
+    } else {
     if constexpr (BM == 256 && BN == 256 && std::is_same<SRC, SrcPlain>::value) {
         if (sk.splits <= 1 && plain_small(src, N, K)) {
             hipLaunchKernelGGL((gemm_big_kernel<BM, BN, SRC, EP, 4>), grid, dim3(256), 0, s, src, W, N, K, ep,
@@ -1180,6 +1188,7 @@ hipError_t launch_big(dim3 grid, SRC src, const bf16_t *W, int N, int K, EP ep, 
     hipLaunchKernelGGL((gemm_big_kernel<BM, BN, SRC, EP, 8>), grid, dim3(512), 0, s, src, W, N, K, ep, tiles_m,
                        tiles_n, sk);
     return hipGetLastError();
+    }
 }
 
 template <int BM, int BN, class SRC, class EP>
@@ -1273,11 +1282,30 @@ hipError_t run_rows(SrcMerge src, const bf16_t *W, int64_t M, int N, int K, EP e
 // 128 x 128 when 256 x 128 tiles would occupy at most half of the compute units and K is
 // short (twice the blocks for the same work; with a long K the K split of 256 x 128 tiles
 // does better); 256 x 128 otherwise.
-enum TileKind { TILES_256x256, TILES_128x128, TILES_256x128 };
+enum TileKind { TILES_256x256, TILES_128x128, TILES_256x128, TILES_192x256 };
 
-TileKind tile_kind(int64_t M, int N, int K)
+// 192 x 256 tiles (4 waves, 96 x 128 per wave) for plain activations, when they leave less
+// output area per compute unit over the launch's rounds than 256 x 256 tiles (rounds x tile
+// rows, the 256 columns being common; the smaller tiles counted 1.1 times, their measured
+// cost per output area), and they occupy at least half the compute units.  On the 9216-patch
+// layer this takes the out-projection and fc2 (144 -> 192 tiles, 56 -> 75% of the compute
+// units in their one round: 35.3 -> 32.3 and 104.6 -> 85.5 us), fc1 (576 tiles in 2.25
+// rounds -> 768 in exactly 3: 92.5 -> 87.9 us) and the SwiGLU step (4.5 -> 6 rounds of
+// smaller tiles); QKV keeps 256 x 256 (432 tiles: 2 rounds against 3), and so does fc1 of the
+// 74,088-patch batch (19 rounds against 25 of 192 rows, 23.1 ms against 21.6 ms per pass).
+bool use_192_tiles(int64_t M, int N, bool plain)
 {
-    if (use_big_tiles(M, N, K)) return TILES_256x256;
+    if (!plain) return false;
+    const int64_t P = cu_count();
+    const int64_t t256 = ceil_div(M, 256) * ceil_div(N, 256), t192 = ceil_div(M, 192) * ceil_div(N, 256);
+    if (t192 * 2 < P) return false;
+    return ceil_div(t192, P) * 192 * 11 <= ceil_div(t256, P) * 256 * 10;
+}
+
+TileKind tile_kind(int64_t M, int N, int K, bool plain = false)
+{
+    if (use_big_tiles(M, N, K)) return use_192_tiles(M, N, plain) ? TILES_192x256 : TILES_256x256;
+    if (use_192_tiles(M, N, plain)) return TILES_192x256;
     if (K <= 2048 && ceil_div(M, 256) * ceil_div(N, 128) * 2 <= cu_count()) return TILES_128x128;
     return TILES_256x128;
 }
@@ -1286,7 +1314,11 @@ template <class SRC, class EP>
 hipError_t run_shaped(SRC src, const bf16_t *W, int64_t M, int N, int K, EP ep, const GemmWorkspace *ws,
                       hipStream_t s)
 {
-    switch (tile_kind(M, N, K)) {
+    const bool plain = plain_small(src, N, K);
+    switch (tile_kind(M, N, K, plain)) {
+    case TILES_192x256:
+        if constexpr (std::is_same<SRC, SrcPlain>::value) return run_rows<192, 256>(src, W, M, N, K, ep, ws, s);
+        return hipErrorInvalidValue;
     case TILES_256x256: return run_rows<256, 256>(src, W, M, N, K, ep, ws, s);
     case TILES_128x128: return run_rows<128, 128>(src, W, M, N, K, ep, ws, s);
     default: return run_rows<256, 128>(src, W, M, N, K, ep, ws, s);
@@ -1327,7 +1359,8 @@ size_t linear_workspace_bytes(int64_t M, int K, int N, int act, bool out_f32)
 {
     if (M <= 0 || (act == ACT_SWIGLU && !out_f32)) return 0;   // the paired epilogue never splits
     int BM = 256, BN = 128;
-    switch (tile_kind(M, N, K)) {
+    switch (tile_kind(M, N, K, (int64_t)M * K * 2 < ((int64_t)1 << 31) && (int64_t)N * K * 2 < ((int64_t)1 << 31))) {
+    case TILES_192x256:
     case TILES_256x256: return 0;                              // only BN = 128 tiles split
     case TILES_128x128: BM = 128; break;
     default: break;
@@ -1373,8 +1406,9 @@ hipError_t run_qkv_rope(const bf16_t *A, int64_t M, int D, const bf16_t *W, cons
     const int N = 3 * D;
     EpiQKVRope<HD> ep{qkv, bias, M, N, D, vt, ldv, imgs, n_img, cos_t, sin_t, store_v ? 1 : 0};
     const SrcPlain src{A, D, M};
+    if (use_192_tiles(M, N, plain_small(src, N, D))) return run_big<192, 256>(src, W, M, N, D, ep, nullptr, s);
     return use_big_tiles(M, N, D) ? run_big<256, 256>(src, W, M, N, D, ep, nullptr, s)
-                               : run_big<256, 128>(src, W, M, N, D, ep, nullptr, s);
+                                  : run_big<256, 128>(src, W, M, N, D, ep, nullptr, s);
 }
 
 hipError_t launch_qkv_rope(const bf16_t *A, int64_t M, int D, int H, const bf16_t *W, const bf16_t *bias,

@@ -97,15 +97,16 @@ def test_linear_full_size_sampled(N, K, act):
 
 @pytest.mark.parametrize("K", [64, 192, 320], ids=["one_ktile", "three_ktiles", "five_ktiles"])
 @pytest.mark.parametrize("act", [vit.ACT_NONE, vit.ACT_GELU_TANH], ids=["plain", "gelu"])
-def test_linear_big_tiles_every_row(K, act):
-    """One round of 256 x 256 tiles of plain activations (the 4-wave kernel with 64-wide k-tiles
-    and two LDS stages): M = 3900 leaves a ragged last tile row (60 rows), N = 4056 a ragged last
-    tile column (216 columns), and K = 64, 192, 320 give 1, 3 and 5 k-tiles (fewer than the two
-    stages, and an odd count that ends on the peeled step).  Every output is compared with the
-    oracle; the residual form of the same launch is checked bitwise against linear + add."""
+@pytest.mark.parametrize("M,N", [(3900, 4056), (4000, 2000)], ids=["tiles256", "tiles192"])
+def test_linear_big_tiles_every_row(M, N, K, act):
+    """One round of 4-wave tiles of plain activations (64-wide k-tiles, two LDS stages):
+    3900 x 4056 runs as 256 x 256 tiles (a ragged last tile row of 60 rows and column of 216),
+    4000 x 2000 as 192 x 256 tiles (168 of them; last tile row 160 rows, last column 208).
+    K = 64, 192, 320 give 1, 3 and 5 k-tiles (fewer than the two stages, and an odd count that
+    ends on the peeled step).  Every output is compared with the oracle; the residual form of
+    the same launch is checked bitwise against linear + add."""
     torch = require_gpu()
     enc, _, _ = encoder()
-    M, N = 3900, 4056
     A = seeded_bf16((M, K), 131, 0)
     W = seeded_bf16((N, K), 131, 1, std=0.05)
     b = seeded_bf16((N,), 131, 2, std=0.1)

@@ -426,49 +426,53 @@ struct EpiQKVRope {
         constexpr int HALF = HD / 2, HC = HALF / 8, NHB = BN / HD;
         static_assert(HD >= 16 && BN % HD == 0, "head blocks must tile the column tile");
         const int2 *pos = reinterpret_cast<const int2 *>(smem + BM * pitch);
-        // q and k (and v rows with store_v): item = (row, head block, chunk of 8 elements of
-        // the first half and the 8 they pair with); the items of one row are consecutive
-        // lanes, so each row's stores are contiguous.
-        for (int w = tid; w < BM * NHB * HC; w += NT) {
-            const int r = w / (NHB * HC), it = w - r * (NHB * HC), hb = it / HC, ch = it - hb * HC;
-            const int c0 = n0 + hb * HD;
-            if (r >= rows || c0 >= N) continue;
-            const int part = c0 / D;
+        // q and k (and v rows with store_v): item = (row, chunk of 8 elements of the first half
+        // and the 8 they pair with); the chunk's 8 angles depend on the row alone, so they are
+        // read once per item and serve every head block of the tile.  The items of one row are
+        // consecutive lanes.
+        for (int w = tid; w < BM * HC; w += NT) {
+            const int r = w / HC, ch = w - r * HC;
+            if (r >= rows) continue;
             const int64_t row = m0 + r;
-            const char *src = smem + r * pitch + (hb * HD + ch * 8) * 2;
-            bf16_t *dst = out + row * N + c0 + ch * 8;
-            const uint4 ua = *reinterpret_cast<const uint4 *>(src);
-            const uint4 ub = *reinterpret_cast<const uint4 *>(src + HALF * 2);
-            if (part == 2) {
-                if (store_v) {
-                    *reinterpret_cast<uint4 *>(dst) = ua;
-                    *reinterpret_cast<uint4 *>(dst + HALF) = ub;
-                }
-                continue;
-            }
-            const int2 hw = pos[r];
             float cs[8], sn[8];
-            rope_cos_sin8<HD>(cos_t, sin_t, hw, ch * 8, cs, sn);
-            const uint32_t wa[4] = {ua.x, ua.y, ua.z, ua.w}, wb[4] = {ub.x, ub.y, ub.z, ub.w};
-            float na[8], nb[8];
+            if (n0 < 2 * D) rope_cos_sin8<HD>(cos_t, sin_t, pos[r], ch * 8, cs, sn);   // q or k columns
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float x = __uint_as_float(e & 1 ? wa[e >> 1] & 0xFFFF0000u : wa[e >> 1] << 16);
-                const float y = __uint_as_float(e & 1 ? wb[e >> 1] & 0xFFFF0000u : wb[e >> 1] << 16);
-                rope_rotate(x, y, cs[e], sn[e], na[e], nb[e]);
-            }
-            uint32_t pa[4], pb[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                pa[j] = pack_bf16x2(na[2 * j], na[2 * j + 1]);
-                pb[j] = pack_bf16x2(nb[2 * j], nb[2 * j + 1]);
-                if (part == 1) {
-                    pa[j] = bf16_to_f16_sat(pa[j] & 0xFFFFu) | (bf16_to_f16_sat(pa[j] >> 16) << 16);
-                    pb[j] = bf16_to_f16_sat(pb[j] & 0xFFFFu) | (bf16_to_f16_sat(pb[j] >> 16) << 16);
+            for (int hb = 0; hb < NHB; ++hb) {
+                const int c0 = n0 + hb * HD;
+                if (c0 >= N) break;
+                const int part = c0 / D;
+                const char *src = smem + r * pitch + (hb * HD + ch * 8) * 2;
+                bf16_t *dst = out + row * N + c0 + ch * 8;
+                const uint4 ua = *reinterpret_cast<const uint4 *>(src);
+                const uint4 ub = *reinterpret_cast<const uint4 *>(src + HALF * 2);
+                if (part == 2) {
+                    if (store_v) {
+                        *reinterpret_cast<uint4 *>(dst) = ua;
+                        *reinterpret_cast<uint4 *>(dst + HALF) = ub;
+                    }
+                    continue;
                 }
+                const uint32_t wa[4] = {ua.x, ua.y, ua.z, ua.w}, wb[4] = {ub.x, ub.y, ub.z, ub.w};
+                float na[8], nb[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float x = __uint_as_float(e & 1 ? wa[e >> 1] & 0xFFFF0000u : wa[e >> 1] << 16);
+                    const float y = __uint_as_float(e & 1 ? wb[e >> 1] & 0xFFFF0000u : wb[e >> 1] << 16);
+                    rope_rotate(x, y, cs[e], sn[e], na[e], nb[e]);
+                }
+                uint32_t pa[4], pb[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    pa[j] = pack_bf16x2(na[2 * j], na[2 * j + 1]);
+                    pb[j] = pack_bf16x2(nb[2 * j], nb[2 * j + 1]);
+                    if (part == 1) {
+                        pa[j] = bf16_to_f16_sat(pa[j] & 0xFFFFu) | (bf16_to_f16_sat(pa[j] >> 16) << 16);
+                        pb[j] = bf16_to_f16_sat(pb[j] & 0xFFFFu) | (bf16_to_f16_sat(pb[j] >> 16) << 16);
+                    }
+                }
+                *reinterpret_cast<uint4 *>(dst) = make_uint4(pa[0], pa[1], pa[2], pa[3]);
+                *reinterpret_cast<uint4 *>(dst + HALF) = make_uint4(pb[0], pb[1], pb[2], pb[3]);
             }
-            *reinterpret_cast<uint4 *>(dst) = make_uint4(pa[0], pa[1], pa[2], pa[3]);
-            *reinterpret_cast<uint4 *>(dst + HALF) = make_uint4(pb[0], pb[1], pb[2], pb[3]);
         }
         // V^T: per image in the tile, item = (run of 4 keys 4c..4c+3 of the image, 8 head dims).
         // The bit swap keeps each 4-aligned run on 4 consecutive columns, so a whole run is one

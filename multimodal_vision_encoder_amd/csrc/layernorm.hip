@@ -1,27 +1,41 @@
-// Residual add + LayerNorm or RMSNorm, one wave (64 lanes) per row of width D.
+// Residual add + LayerNorm or RMSNorm, one wave (64 lanes) per row of width D, two rows per
+// wave.
 //
 //   x   = bf16(x + delta)          (when delta is given; written back to xout)
-//   out = bf16((x - mean) / sqrt(var + eps) * g + b),  mean and biased variance over the row
+//   out = bf16((x - mean) * r * g + b),  r = 1 / sqrt(var + eps) rounded once per row,
+//         mean and biased variance over the row
 //   or, RMSNorm (the official tower: [Z] "Comparing the DeepSeek V4.1 Flash and Qwen3-VL
 //   vision towers"; "Step 2" boundary table, RMSNorm semantics at the final norm):
-//   out = bf16(x / sqrt(mean(x^2) + eps) * g)
+//   out = bf16(x * r * g),  r = 1 / sqrt(mean(x^2) + eps)
 //
 // Pre-norm blocks and the final norm ([Z] "Step 2" boundary table); the encoder's residual
 // adds run in the epilogues of the out-projection and fc2, so there it takes no delta (the
-// delta form serves vit_op_layernorm / vit_op_rmsnorm).  The row stays in
-// registers: each lane holds D/64 elements (16 at D = 1024, loaded as two 16-byte chunks
-// so that a wave reads 1 KB contiguous per instruction); statistics are two-pass (mean,
-// then squared deviations) with butterfly reductions across the wave.  HBM-bound: it reads
+// delta form serves vit_op_layernorm / vit_op_rmsnorm).  The rows stay in registers: each
+// lane holds D/64 elements of each row (16 at D = 1024, loaded as two 16-byte chunks so that
+// a wave reads 1 KB contiguous per instruction); statistics are two-pass (mean, then squared
+// deviations) with DPP reductions inside each 16-lane row and the four row sums read as
+// scalars.  Scaling by the per-row reciprocal instead of dividing every element moves a
+// normalised value by at most one fp32 ulp before the bf16 rounding.  HBM-bound: it reads
 // x (+ delta) and writes out (+ x) once.
 #include "kernels.h"
 
 namespace {
 
+// Sum over the wave, the same value in every lane: within each row of 16 lanes by DPP moves
+// (lane ^ 1, lane ^ 2, then rotations by 4 and 8 add the other quads), then the four row
+// sums read as scalars.  No LDS round trips.
 __device__ __forceinline__ float wave_sum(float v)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
+    const int iv = __builtin_bit_cast(int, v);
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 48));
+    return (r0 + r1) + (r2 + r3);
 }
 
 template <int EPL>
@@ -61,7 +75,10 @@ __device__ __forceinline__ void store_row(bf16_t *p, int lane, const float *v)
     }
 }
 
-template <int EPL, bool RMS>
+// Each wave normalises RPW rows: it issues the loads of all its rows first, unpacks gamma and
+// beta once for them, and scales each row by one reciprocal of its deviation (a single
+// division per row instead of one per element).
+template <int EPL, bool RMS, int RPW>
 __global__ __launch_bounds__(256) void layernorm_kernel(const bf16_t *__restrict__ x,
                                                         const bf16_t *__restrict__ delta,
                                                         bf16_t *xout, int64_t M,
@@ -70,62 +87,70 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const bf16_t *__restrict
                                                         bf16_t *__restrict__ out)
 {
     constexpr int D = EPL * 64;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t row0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW;
     const int lane = threadIdx.x & 63;
-    if (row >= M) return;
+    if (row0 >= M) return;
 
-    float v[EPL];
-    load_row<EPL>(x + row * D, lane, v);
+    float v[RPW][EPL];
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr)
+        if (row0 + rr < M) load_row<EPL>(x + (row0 + rr) * D, lane, v[rr]);
     if (delta) {
-        float d[EPL];
-        load_row<EPL>(delta + row * D, lane, d);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) v[e] = bf16_to_f32(f32_to_bf16(__fadd_rn(v[e], d[e])));
-        store_row<EPL>(xout + row * D, lane, v);
-    }
-    float mu = 0.f;
-    if constexpr (!RMS) {
-        float s = 0.f;
+        for (int rr = 0; rr < RPW; ++rr) {
+            if (row0 + rr >= M) continue;
+            float d[EPL];
+            load_row<EPL>(delta + (row0 + rr) * D, lane, d);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) s += v[e];
-        mu = wave_sum(s) / (float)D;
+            for (int e = 0; e < EPL; ++e) v[rr][e] = bf16_to_f32(f32_to_bf16(__fadd_rn(v[rr][e], d[e])));
+            store_row<EPL>(xout + (row0 + rr) * D, lane, v[rr]);
+        }
     }
-    float ss = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-        const float dv = v[e] - mu;
-        ss = __builtin_fmaf(dv, dv, ss);
-    }
-    const float var = wave_sum(ss) / (float)D;
-    const float den = sqrtf(var + eps);
-    // gamma and beta in the same lane layout as the row (16-byte loads)
-    float gv[EPL], y[EPL];
+    // gamma and beta in the same lane layout as the rows (16-byte loads), once for all rows
+    float gv[EPL], bv[EPL];
     load_row<EPL>(g, lane, gv);
-    if constexpr (RMS) {
+    if constexpr (!RMS) load_row<EPL>(b, lane, bv);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) y[e] = __fmul_rn(__fdiv_rn(v[e], den), gv[e]);
-    } else {
-        float bv[EPL];
-        load_row<EPL>(b, lane, bv);
+    for (int rr = 0; rr < RPW; ++rr) {
+        if (row0 + rr >= M) continue;
+        float mu = 0.f;
+        if constexpr (!RMS) {
+            float s = 0.f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) s += v[rr][e];
+            mu = wave_sum(s) / (float)D;
+        }
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            const float dv = v[rr][e] - mu;
+            ss = __builtin_fmaf(dv, dv, ss);
+        }
+        const float var = wave_sum(ss) / (float)D;
+        const float inv = __fdiv_rn(1.f, sqrtf(var + eps));
+        float y[EPL];
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
 #pragma clang fp contract(off)
-            y[e] = __fadd_rn(__fmul_rn(__fdiv_rn(v[e] - mu, den), gv[e]), bv[e]);
+            if constexpr (RMS) y[e] = __fmul_rn(__fmul_rn(v[rr][e], inv), gv[e]);
+            else y[e] = __fadd_rn(__fmul_rn(__fmul_rn(v[rr][e] - mu, inv), gv[e]), bv[e]);
         }
+        store_row<EPL>(out + (row0 + rr) * D, lane, y);
     }
-    store_row<EPL>(out + row * D, lane, y);
 }
 
 template <int EPL>
 hipError_t run_ln(const bf16_t *x, const bf16_t *delta, bf16_t *xout, int64_t M, const bf16_t *g,
                   const bf16_t *b, float eps, bool rms, bf16_t *out, hipStream_t s)
 {
+    constexpr int RPW = 2;
+    const dim3 grid((unsigned)ceil_div(M, 4 * RPW));
     if (rms)
-        hipLaunchKernelGGL((layernorm_kernel<EPL, true>), dim3((unsigned)ceil_div(M, 4)), dim3(256), 0, s, x,
-                           delta, xout, M, g, b, eps, out);
+        hipLaunchKernelGGL((layernorm_kernel<EPL, true, RPW>), grid, dim3(256), 0, s, x, delta, xout, M, g, b,
+                           eps, out);
     else
-        hipLaunchKernelGGL((layernorm_kernel<EPL, false>), dim3((unsigned)ceil_div(M, 4)), dim3(256), 0, s, x,
-                           delta, xout, M, g, b, eps, out);
+        hipLaunchKernelGGL((layernorm_kernel<EPL, false, RPW>), grid, dim3(256), 0, s, x, delta, xout, M, g, b,
+                           eps, out);
     return hipGetLastError();
 }
 

@@ -67,7 +67,9 @@ vit_status vit_op_linear_residual(vit_ctx *ctx, const uint16_t *d_A, int64_t M, 
 
 /* Residual add + LayerNorm over rows of width D (D in {64, 128, 256, 512, 1024, 1536, 2048}):
  *   if d_delta != NULL:  x = bf16(x + delta), written to d_xout (may alias d_x);
- *   out = bf16((x - mean) / sqrt(var + eps) * g + b), mean/var over the row (biased).
+ *   out = bf16((x - mean) * r * g + b), mean/var over the row (biased), r = 1/sqrt(var + eps)
+ *   rounded once per row (within one fp32 ulp of dividing by the root; compared with the
+ *   division form within one bf16 ulp).
  * x, delta, xout, out are bf16 [M][D]; g, b bf16 [D]. */
 vit_status vit_op_layernorm(vit_ctx *ctx, const uint16_t *d_x, const uint16_t *d_delta,
                             uint16_t *d_xout, int64_t M, int32_t D, const uint16_t *d_g,
@@ -76,7 +78,8 @@ vit_status vit_op_layernorm(vit_ctx *ctx, const uint16_t *d_x, const uint16_t *d
 /* Residual add + RMSNorm, the official tower's norm ([Z] "Comparing the DeepSeek V4.1 Flash
  * and Qwen3-VL vision towers"; "Step 2" boundary table: RMSNorm semantics at the final norm),
  * same kernel and conventions as vit_op_layernorm with:
- *   out = bf16(x / sqrt(mean(x^2) + eps) * g)   (no mean subtracted, no beta). */
+ *   out = bf16(x * r * g), r = 1/sqrt(mean(x^2) + eps) rounded once per row   (no mean
+ *   subtracted, no beta). */
 vit_status vit_op_rmsnorm(vit_ctx *ctx, const uint16_t *d_x, const uint16_t *d_delta,
                           uint16_t *d_xout, int64_t M, int32_t D, const uint16_t *d_g,
                           float eps, uint16_t *d_out, void *stream);

@@ -416,13 +416,15 @@ class Encoder:
                                                  _stream(stream)))
         return x
 
-    def op_layernorm(self, x, g, b, eps, delta=None, xout=None, stream=None):
+    def op_layernorm(self, x, g, b, eps, delta=None, xout=None, out=None, stream=None):
         import torch
         M, D = self._check_rows(x, delta, xout)
         check_tensor(g, "g", torch.bfloat16, shape=(D,), gpu=False)
         check_tensor(b, "b", torch.bfloat16, shape=(D,), gpu=False)
-        on_gpu(x=x, delta=delta, xout=xout, g=g, b=b)
-        out = torch.empty_like(x)
+        check_tensor(out, "out", torch.bfloat16, shape=x.shape, optional=True, gpu=False)
+        on_gpu(x=x, delta=delta, xout=xout, g=g, b=b, out=out)
+        if out is None:
+            out = torch.empty_like(x)
         self._check(lib().vit_op_layernorm(self._ctx, _ptr(x), _ptr(delta), _ptr(xout), M, D,
                                            _ptr(g), _ptr(b), float(eps), _ptr(out),
                                            _stream(stream)))

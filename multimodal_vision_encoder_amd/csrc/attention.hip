@@ -512,6 +512,20 @@ __global__ __launch_bounds__(256) void attention_merge_kernel(
     if (idx >= (int64_t)8 * tail * QT * chunks) return;
     const int tix = (int)(idx / (QT * chunks)), rem = (int)(idx - (int64_t)tix * QT * chunks);
     const int r = rem / chunks, col = (rem - r * chunks) * 8;
+    // The partial rows of every thread of the grid lie inside the buffers (8 x tail x slices x
+    // QT rows), so this thread's (max, sum) pairs and output chunks are loaded first, beside
+    // the work-item and image lookups they do not depend on; rows past an image end are
+    // dropped below without being stored.
+    const float2 *ml = reinterpret_cast<const float2 *>(pl.part_ml);
+    const int64_t pr0 = (int64_t)tix * ns * QT + r;   // slice sp at pr0 + sp * QT
+    float2 m[4];
+    uint4 u[4];
+#pragma unroll
+    for (int sp = 0; sp < 4; ++sp)
+        if (sp < ns) {
+            m[sp] = ml[pr0 + (int64_t)sp * QT];
+            u[sp] = *reinterpret_cast<const uint4 *>(pl.part_o + (pr0 + (int64_t)sp * QT) * hd + col);
+        }
     const int L = (tix / tail) * pl.per_xcd + pl.full + tix % tail;
     if (L >= pl.items) return;
     const int head = L / n_work, wi = L - head * n_work;
@@ -519,16 +533,16 @@ __global__ __launch_bounds__(256) void attention_merge_kernel(
     const ImgDesc d = imgs[wt.img];
     const int q = wt.r0 + r;
     if (q >= d.n) return;
-    const float2 *ml = reinterpret_cast<const float2 *>(pl.part_ml);
-    const int64_t pr0 = (int64_t)tix * ns * QT + r;   // slice sp at pr0 + sp * QT
     float mmax = -INFINITY;
-    for (int sp = 0; sp < ns; ++sp) mmax = fmaxf(mmax, ml[pr0 + (int64_t)sp * QT].x);
+#pragma unroll
+    for (int sp = 0; sp < 4; ++sp)
+        if (sp < ns) mmax = fmaxf(mmax, m[sp].x);
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, wsum = 0.f;
-    for (int sp = 0; sp < ns; ++sp) {
-        const float2 m = ml[pr0 + (int64_t)sp * QT];
-        const float w = m.y == 0.f ? 0.f : m.y * fast_exp2(m.x - mmax);
-        const uint4 u = *reinterpret_cast<const uint4 *>(pl.part_o + (pr0 + (int64_t)sp * QT) * hd + col);
-        const uint32_t ww[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int sp = 0; sp < 4; ++sp) {
+        if (sp >= ns) break;
+        const float w = m[sp].y == 0.f ? 0.f : m[sp].y * fast_exp2(m[sp].x - mmax);
+        const uint32_t ww[4] = {u[sp].x, u[sp].y, u[sp].z, u[sp].w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const uint16_t hb = (uint16_t)((ww[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);

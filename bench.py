@@ -597,7 +597,11 @@ def main():
                 e["hbm_frac"] = e["gbs"] / PEAK_HBM_GBS
             kernels[k] = e
         if "layernorm" in kernels and args.tower == "base":
-            kernels["layernorm"]["isolated"] = norm_isolated(enc, cfg, N)
+            try:
+                kernels["layernorm"]["isolated"] = norm_isolated(enc, cfg, N)
+            except Exception as exc:   # an extra figure: never lose the bench line for it
+                torch.cuda.synchronize()
+                kernels["layernorm"]["isolated"] = {"error": f"{type(exc).__name__}: {exc}"}
         result["kernels"] = kernels
         gemm_attn = ("qkv", "attention", "out_proj", "fc1", "fc2")
         # time of the GEMM and attention steps, the merge of the attention's key slices included;

@@ -26,7 +26,7 @@ __device__ __forceinline__ float keys_cubic(float x)
 // Taps [lo, hi) and the centre / kernel stretch of output sample i of an axis n_in -> n_out.
 struct Taps {
     int lo, hi;
-    float c, fs;
+    float c, inv_fs;   // centre, 1 / kernel stretch
 };
 __device__ __forceinline__ Taps taps_of(int i, int n_in, int n_out)
 {
@@ -36,7 +36,7 @@ __device__ __forceinline__ Taps taps_of(int i, int n_in, int n_out)
     t.lo = max(0, (int)floorf(c - support));
     t.hi = min(n_in, (int)ceilf(c + support) + 1);
     t.c = c;
-    t.fs = fs;
+    t.inv_fs = 1.f / fs;
     return t;
 }
 
@@ -51,16 +51,17 @@ __global__ __launch_bounds__(256) void resize_h_kernel(const uint8_t *__restrict
     const uint8_t *row = src + (int64_t)y * w * 3;
     float a0 = 0.f, a1 = 0.f, a2 = 0.f, ks = 0.f;
     for (int j = t.lo; j < t.hi; ++j) {
-        const float k = keys_cubic(((float)j + 0.5f - t.c) / t.fs);
+        const float k = keys_cubic(((float)j + 0.5f - t.c) * t.inv_fs);
         a0 += k * (float)row[3 * j];
         a1 += k * (float)row[3 * j + 1];
         a2 += k * (float)row[3 * j + 2];
         ks += k;
     }
     float *o = tmp + idx * 3;
-    o[0] = a0 / ks;
-    o[1] = a1 / ks;
-    o[2] = a2 / ks;
+    const float inv = 1.f / ks;
+    o[0] = a0 * inv;
+    o[1] = a1 * inv;
+    o[2] = a2 * inv;
 }
 
 // One thread per canvas pixel: three channels, 127 outside the resized image.
@@ -79,14 +80,15 @@ __global__ __launch_bounds__(256) void resize_v_kernel(const float *__restrict__
     const Taps t = taps_of(i, h, oh);
     float a0 = 0.f, a1 = 0.f, a2 = 0.f, ks = 0.f;
     for (int j = t.lo; j < t.hi; ++j) {
-        const float k = keys_cubic(((float)j + 0.5f - t.c) / t.fs);
+        const float k = keys_cubic(((float)j + 0.5f - t.c) * t.inv_fs);
         const float *v = tmp + ((int64_t)j * ow + x) * 3;
         a0 += k * v[0];
         a1 += k * v[1];
         a2 += k * v[2];
         ks += k;
     }
-    const float r[3] = {a0 / ks, a1 / ks, a2 / ks};
+    const float inv = 1.f / ks;
+    const float r[3] = {a0 * inv, a1 * inv, a2 * inv};
 #pragma unroll
     for (int c = 0; c < 3; ++c) o[c] = (uint8_t)fminf(fmaxf(rintf(r[c]), 0.f), 255.f);
 }

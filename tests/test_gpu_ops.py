@@ -148,9 +148,9 @@ def test_linear_row_tail(act, out_f32):
 
 @pytest.mark.parametrize("act,out_f32", [(vit.ACT_GELU_TANH, False), (vit.ACT_NONE, True)])
 def test_linear_split_k_tail(act, out_f32):
-    """264 tiles of 256 x 128 on 256 compute units (K = 4096: long enough that the 132 tiles of
-    256 x 256 are not chosen): the 8 leftover tiles (rows 8192..8399, ragged in M and N) are cut
-    into K slices whose fp32 partials a second kernel sums."""
+    """K = 4096 with ragged M and N (rows 8192..8399 and columns 1016..1019 in partial tiles).
+    Plain activations of this size run as one round of 192 x 256 tiles; the K split of a
+    leftover round is reached by the gathered projector source (test_merge_project_split_k_tail)."""
     torch = require_gpu()
     enc, _, _ = encoder()
     M, K, N = 8400, 4096, 1020
@@ -171,9 +171,10 @@ def test_linear_split_k_tail(act, out_f32):
 @pytest.mark.parametrize("M,K,N,out_f32", [(378, 9216, 4096, True), (3402, 4096, 1024, False)],
                          ids=["projector_v4", "fc2_v4"])
 def test_linear_split_k_under_one_round(M, K, N, out_f32):
-    """Launches with fewer tiles than compute units (the 384-token image's projector, 64 tiles
-    of 256 x 128, and its fc2, 112 tiles): every tile is cut into K slices whose fp32 partials a
-    second kernel sums in slice order.  Rows in every tile row are checked."""
+    """Launches with fewer tiles than compute units.  The 384-token image's projector (64
+    tiles of 256 x 128): every tile is cut into K slices whose fp32 partials a second kernel
+    sums in slice order.  Its fc2 (K = 4096) runs as 216 unsplit tiles of 128 x 128, which fill
+    84% of the compute units.  Rows in every tile row are checked."""
     torch = require_gpu()
     enc, _, _ = encoder()
     A = seeded_bf16((M, K), 128, 0)
@@ -744,6 +745,30 @@ def test_merge_project(grids):
         off += gh * gw
     want = np.concatenate(want)
     np.testing.assert_allclose(got, want, rtol=1e-4, atol=1e-4)
+
+
+def test_merge_project_split_k_tail():
+    """The merge gather into the projector at full width for two 1024-token images: 320 tiles
+    of 256 x 128 (2048 rows x 40 column tiles, K = 9216) leave a round of 64 tiles, which are
+    cut into K slices whose fp32 partials a second kernel sums.  Rows in every tile row, the
+    leftover ones included, against the oracle's merge and linear."""
+    torch = require_gpu()
+    enc, cfg, blob = encoder("v41_1layer")
+    grids = [(96, 96), (96, 96)]
+    N = sum(a * b for a, b in grids)
+    y = seeded_bf16((N, cfg.hidden), 131)
+    got = enc.op_merge_project(to_dev_bf16(y), grids).cpu().numpy()
+    torch.cuda.synchronize()
+    W = oracle.Weights(cfg, blob)
+    rows = np.unique(np.r_[0:2, 255:258, np.arange(0, 2048, 233), 1790:1794, 2044:2048])
+    A = np.concatenate([oracle.merge(f32(y[:9216]), 96, 96), oracle.merge(f32(y[9216:]), 96, 96)])[rows]
+    Wp = W["proj.w"]
+    want = oracle.linear(A, Wp, W["proj.b"], round_out=False, workers=8)
+    g = got[rows]
+    assert g.shape == want.shape
+    # sum_bound's slack, from fp32 operands: 2^-18 * sum_k |a_k w_k| per output
+    slack = 2.0 ** -18 * (np.abs(A).astype(np.float64) @ np.abs(Wp).astype(np.float64).T)
+    assert np.all(np.abs(g - want) <= slack + 1e-6 * np.abs(want))
 
 
 def test_overlay_exact():

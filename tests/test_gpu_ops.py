@@ -89,7 +89,7 @@ def test_linear_full_size_sampled(N, K, act):
     b = seeded_bf16((N,), 103, 2, std=0.02)
     got = from_dev_bf16(enc.op_linear(to_dev_bf16(A), to_dev_bf16(W), to_dev_bf16(b), act))
     torch.cuda.synchronize()
-    # the last tile rows (8192..9215) are the leftover round that fc2 splits along K
+    # rows in the first tile row, the middle and the last tile rows (8192..9215)
     rows = np.r_[0:3, 127:130, 4000:4003, 8192:8196, 8700:8703, M - 5:M]
     want = oracle.linear(f32(A[rows]), f32(W), f32(b), act=act)
     assert_bf16_close(got[rows], want, atol=sum_bound(A[rows], W), what="linear full size")
@@ -199,9 +199,9 @@ def test_linear_split_k_under_one_round(M, K, N, out_f32):
     (257, 192, 130),     # rows of 260 bytes: per-element stores
     (1, 64, 5),          # degenerate single row, tiny N
     (9216, 1024, 1024),  # out-projection of the 1024-token image (256 x 256 tiles)
-    (9216, 4096, 1024),  # fc2 of that image (256 x 128 tiles, K-split tail)
+    (9216, 4096, 1024),  # fc2 of that image (192 x 256 tiles, one round)
     (8492, 1024, 2000),  # 128 x 128 row tail
-    (3402, 4096, 1024),  # fc2 of the 384-token image (under one round, K split)
+    (3402, 4096, 1024),  # fc2 of the 384-token image (216 tiles of 128 x 128, one round)
 ], ids=["small", "unstaged", "one_row", "out_proj_1024", "fc2_1024", "row_tail", "fc2_384"])
 def test_linear_residual(M, K, N):
     """x = bf16(x + bf16(A W^T + b)) in place: bitwise the residual add ([Z] "Step 2" table,

@@ -30,17 +30,17 @@ def call_noalloc(enc, A, W, b, act, out_f32):
 
 
 # (M, K, N, act, fp32 out): every shape below takes the split-K path, whose partial tiles the
-# scratch holds: fc2 of the 1024-token image (4 slices of its last 32 tiles, 16 MiB) then of
-# the 384-token image (2 slices of all 112 tiles, 28 MiB); a 9216-deep fp32 projection (2
-# slices of 96 tiles, 24 MiB) then the 384-token image's projector (4 slices of 64 tiles, the
-# whole 32 MiB); 128 x 128 tiles with GELU (4 slices, 8 MiB then 4 MiB).
-@pytest.mark.parametrize("shapes", [[(9216, 4096, 1024, vit.ACT_NONE, False),
-                                     (3402, 4096, 1024, vit.ACT_NONE, False)],
+# scratch holds: long-K launches under one round of 256 x 128 tiles (4 slices of 48 tiles,
+# 24 MiB, then 8 slices of 16 tiles, 16 MiB); a 9216-deep fp32 projection (2 slices of 96
+# tiles, 24 MiB) then the 384-token image's projector (4 slices of 64 tiles, the whole
+# 32 MiB); 128 x 128 tiles with GELU (4 slices, 8 MiB then 4 MiB).
+@pytest.mark.parametrize("shapes", [[(768, 4096, 2048, vit.ACT_NONE, False),
+                                     (512, 4096, 1024, vit.ACT_NONE, False)],
                                     [(640, 9216, 4096, vit.ACT_NONE, True),
                                      (378, 9216, 4096, vit.ACT_NONE, True)],
                                     [(256, 2048, 2048, vit.ACT_GELU_TANH, False),
                                      (200, 2048, 1024, vit.ACT_GELU_TANH, False)]],
-                         ids=["fc2_shapes", "projector_shapes_fp32", "small_tiles_gelu"])
+                         ids=["long_k_shapes", "projector_shapes_fp32", "small_tiles_gelu"])
 def test_noalloc_linear_equals_linear(shapes):
     torch = require_gpu()
     cfg = synth.TINY

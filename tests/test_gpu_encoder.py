@@ -72,8 +72,8 @@ def test_identity_patch_projection_bit_exact(grids):
     """W_pe = identity (D = 1024 >= 588 columns), b = 0: x0[:, :588] = patches and 0 after;
     exact because each output has one non-zero product, so the patchify inside the projection's
     A loader, the permutation of W_pe into the loader's K order (588 columns spread over 672)
-    and its zero columns are checked together, on every row (9,260 rows: 256 x 128 tiles and
-    their 128 x 128 row tail)."""
+    and its zero columns are checked together, on every row (9,260 rows: 148 tiles of 256 x 256,
+    a ragged last tile row)."""
     torch = require_gpu()
     cfg = replace(synth.V41, layers=0, out_hidden=16)
     blob = synth.make_weights(cfg)

@@ -199,7 +199,7 @@ def test_linear_split_k_under_one_round(M, K, N, out_f32):
     (300, 128, 200),     # ragged M, several tiles, rows of 400 bytes (staged writer)
     (257, 192, 130),     # rows of 260 bytes: per-element stores
     (1, 64, 5),          # degenerate single row, tiny N
-    (9216, 1024, 1024),  # out-projection of the 1024-token image (256 x 256 tiles)
+    (9216, 1024, 1024),  # out-projection of the 1024-token image (192 x 256 tiles)
     (9216, 4096, 1024),  # fc2 of that image (192 x 256 tiles, one round)
     (24700, 1024, 2000),  # 256 x 256 tiles, rows 24576.. as the 128 x 128 row tail
     (3402, 4096, 1024),  # fc2 of the 384-token image (216 tiles of 128 x 128, one round)
